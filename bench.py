@@ -1,0 +1,239 @@
+"""Throughput of the fused attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal8k]
+
+One step = one forward (attn_fwd: online softmax, tau = 8 conditional
+rescale, LSE) plus one backward (attn_bwd phases: D = rowsum(dO o O) and
+clears, the dK/dV/dQ main kernel, dQ conversion) over one batch of seeded
+synthetic bf16 inputs already resident in HBM. Throughput counts algorithmic
+flops: forward 4*B*H*Sq*Sk*d, backward 2.5x, both halved for causal.
+
+Prints one JSON line. The "roofline" object covers the dominant kernel (the
+backward main kernel for fwd+bwd workloads, the forward kernel for forward-only
+ones), timed with HIP events on the stream it runs on. "cpu_baseline" times
+the float64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def _describe(w) -> str:
+    if w.varlen:
+        return (f"{w.name}: {w.num_seqs} packed seqs len U[{w.len_lo},{w.len_hi}], Hq{w.heads_q} "
+                f"Hkv{w.heads_kv} d{w.head_dim} {'causal' if w.causal else 'non-causal'} {w.passes}")
+    return (f"{w.name}: B{w.batch} Hq{w.heads_q} Hkv{w.heads_kv} S{w.seqlen} d{w.head_dim} "
+            f"{'causal' if w.causal else 'non-causal'} {w.passes}"
+            + (" det" if w.deterministic else "") + (" QKx3 half heads" if w.scaled_heads else ""))
+
+
+def cpu_baseline(w, budget_s: float = 20.0) -> dict:
+    """Float64 oracle on a bounded sample: whole (sequence, head) slabs of the
+    workload, fwd (+bwd), until about budget_s seconds have been spent."""
+    import numpy as np
+    import oracle
+    from oracle.attention import head_backward, head_forward
+    from workloads import draw_lengths, make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    if w.varlen:
+        lengths = draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number)
+        sl = max(lengths)
+    else:
+        sl = w.seqlen
+    # one batch row of the workload (all heads drawn, a few used), same distribution
+    inp = make_inputs(1, sl, sl, w.heads_q, w.heads_kv, w.head_dim, seed=71000 + w.number,
+                      scaled_heads=w.scaled_heads, with_grad=True)
+    q, k, v, do = (oracle.attention._f64(inp[n])[0] for n in ("q", "k", "v", "do"))
+    grp = w.heads_q // w.heads_kv
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    for h in range(w.heads_q):
+        hk = h // grp
+        head_forward(q[:, h], k[:, hk], v[:, hk], w.scale, w.causal)
+        f = 4.0 * sl * sl * w.head_dim * (0.5 if w.causal else 1.0)
+        flops += f
+        if w.passes == "fwd+bwd":
+            head_backward(q[:, h], k[:, hk], v[:, hk], do[:, h], w.scale, w.causal)
+            flops += 2.5 * f
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.heads_q * (w.num_seqs if w.varlen else w.batch)} "
+                      f"(sequence, head) slabs at length {sl}, {w.passes}, float64 numpy, "
+                      f"{dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention path "
+              "here has no multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_attention_71_amd as ea
+    from workloads import WORKLOADS, draw_lengths, workload_flops, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {_describe(w)}", file=sys.stderr, flush=True)
+    inp = workload_inputs(w, device=dev)
+    lengths = draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number) if w.varlen else None
+    fl = workload_flops(w, lengths)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    with_bwd = w.passes == "fwd+bwd"
+
+    if w.varlen:
+        cu_q = inp["cu_seqlens_q"].to(dev)
+        cu_k = inp["cu_seqlens_k"].to(dev)
+        mx = max(lengths)
+        tq, hq, d = q.shape
+        p = ea.make_params(w.num_seqs, mx, mx, w.heads_q, w.heads_kv, d, w.scale, w.causal,
+                           w.deterministic, total_q=tq, total_k=k.shape[0])
+        o = torch.empty_like(q)
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=dev)
+    else:
+        cu_q = cu_k = None
+        b, s, hq, d = q.shape
+        p = ea.make_params(b, s, s, w.heads_q, w.heads_kv, d, w.scale, w.causal, w.deterministic)
+        o = torch.empty_like(q)
+        lse = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
+    varlen = w.varlen
+    lib = ea.load()
+    import ctypes
+    fws = torch.empty(max(1, ea.fwd_workspace_size(p, varlen)), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(1, ea.bwd_workspace_size(p, varlen)), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def run_fwd():
+        st = stream()
+        if varlen:
+            r = lib.attn_fwd_varlen(ctypes.byref(p), cu_q.data_ptr(), cu_k.data_ptr(), q.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    fws.data_ptr(), fws.numel(), st)
+        else:
+            r = lib.attn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), fws.data_ptr(), fws.numel(), st)
+        assert r == 0, r
+
+    def run_bwd_phase(mask):
+        r = lib.attn_bwd_phases(ctypes.byref(p), None if cu_q is None else cu_q.data_ptr(),
+                                None if cu_k is None else cu_k.data_ptr(), mask, q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                bws.data_ptr(), bws.numel(), stream())
+        assert r == 0, r
+
+    def stream():
+        return torch.cuda.current_stream().cuda_stream
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    dom_start, dom_end = [], []
+
+    def step(timed: bool):
+        if not with_bwd:
+            if timed:
+                dom_start.append(ev()); dom_start[-1].record()
+            run_fwd()
+            if timed:
+                dom_end.append(ev()); dom_end[-1].record()
+            return
+        run_fwd()
+        run_bwd_phase(ea.BWD_PREPROCESS)
+        if timed:
+            dom_start.append(ev()); dom_start[-1].record()
+        run_bwd_phase(ea.BWD_MAIN)
+        if timed:
+            dom_end.append(ev()); dom_end[-1].record()
+        run_bwd_phase(ea.BWD_POSTPROCESS)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(True)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in zip(dom_start, dom_end)) / len(dom_start)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step, dominant kernel {dom_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+    if with_bwd and w.deterministic:
+        assert ea.bwd_status(p, bws, varlen) == 0
+
+    # separate forward-only timing for the breakdown (not part of `value`)
+    f0, f1 = ev(), ev()
+    f0.record()
+    for _ in range(args.steps):
+        run_fwd()
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+
+    total_flops = fl["fwd+bwd"] if with_bwd else fl["fwd"]
+    value = total_flops / (ms * 1e-3) / 1e12
+    dom_flops = fl["bwd"] if with_bwd else fl["fwd"]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd/bwd TFLOPs/s at hdim128 bf16; % of MI355X BF16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
+        "config": {"workload": _describe(w), "pass": w.passes,
+                   "fwd_tflops": round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12, 2),
+                   "fwd_ms": round(fwd_ms, 4),
+                   "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "bwd_main_kernel" if with_bwd else "fwd_kernel",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(dom_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,255 @@
+"""Python binding of libattn71 (fused exact attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn71.so``. PyTorch provides device memory and the current
+stream. If the library is missing the import fails loudly; there is no
+fallback implementation.
+
+Entry points mirror the C ABI in ``include/attn71.h``:
+
+    fwd(q, k, v, causal=False, softmax_scale=None, return_lse=True)
+    fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
+    bwd(q, k, v, o, do, lse, causal=False, softmax_scale=None, deterministic=False)
+    bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
+    bwd_phases(...)          the backward split into preprocess / main / postprocess
+    tile_order(...)          the fixed-length tile schedule, evaluated on the host
+    set_tuning(key, value)   process-wide knobs ("tile_order", "exp_emulation", "spin_limit")
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn71.so")
+
+ATTN_OK = 0
+BWD_PREPROCESS, BWD_MAIN, BWD_POSTPROCESS = 1, 2, 4
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib().attn_status_string(status).decode()} (status {status})")
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
+                ("seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int32),
+                ("total_k", ctypes.c_int32), ("num_heads_q", ctypes.c_int32),
+                ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32)]
+
+
+_LIB = None
+_P = ctypes.POINTER(AttnParams)
+_vp = ctypes.c_void_p
+
+EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
+           "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
+           "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
+           "attn_set_tuning"]
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_attention_71_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_version.restype = ctypes.c_int
+    for n in ("attn_fwd_workspace_size", "attn_bwd_workspace_size"):
+        getattr(lib, n).restype = ctypes.c_size_t
+        getattr(lib, n).argtypes = [_P, ctypes.c_int32]
+    lib.attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.attn_fwd_varlen.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.attn_bwd.argtypes = [_P] + [_vp] * 10 + [ctypes.c_size_t, _vp]
+    lib.attn_bwd_varlen.argtypes = [_P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    lib.attn_bwd_phases.argtypes = [_P, _vp, _vp, ctypes.c_int32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
+    lib.attn_bwd_status.argtypes = [_P, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_int32), _vp]
+    lib.attn_tile_order.argtypes = [_P, ctypes.c_int32, _vp, ctypes.c_int64,
+                                    ctypes.POINTER(ctypes.c_int64)]
+    lib.attn_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_int32]
+    for n in EXPORTS:
+        if n not in ("attn_status_string", "attn_version", "attn_fwd_workspace_size",
+                     "attn_bwd_workspace_size"):
+            getattr(lib, n).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (raises ImportError if it is not built)."""
+    return _lib()
+
+
+def _check(status: int, where: str) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _expect(t: torch.Tensor, name: str, dtype=torch.bfloat16) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_params(batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, scale, causal,
+                deterministic=False, total_q=0, total_k=0) -> AttnParams:
+    return AttnParams(int(batch), int(seqlen_q), int(seqlen_k), int(total_q), int(total_k),
+                      int(heads_q), int(heads_kv), int(head_dim), float(scale), int(bool(causal)),
+                      int(bool(deterministic)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise AttnError(1, "workspace size")
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def fwd_workspace_size(p: AttnParams, varlen: bool = False) -> int:
+    return _lib().attn_fwd_workspace_size(ctypes.byref(p), int(varlen))
+
+
+def bwd_workspace_size(p: AttnParams, varlen: bool = False) -> int:
+    return _lib().attn_bwd_workspace_size(ctypes.byref(p), int(varlen))
+
+
+# --------------------------------------------------------------------- forward
+def fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
+        return_lse: bool = True, out: Optional[torch.Tensor] = None,
+        lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] bf16 -> (o [B, Sq, Hq, d], lse [B, Hq, Sq] fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, n)
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    p = make_params(b, sq, sk, hq, hkv, d, scale, causal)
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    ws = _workspace(fwd_workspace_size(p), q.device)
+    _check(_lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                           _ptr(ws), ws.numel(), _stream()), "attn_fwd")
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+               causal: bool = False, softmax_scale: Optional[float] = None,
+               return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_seqlens int32 [n+1] -> (o, lse [Hq, Tq])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, n)
+    _expect(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _expect(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    nseq = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    p = make_params(nseq, max_seqlen_q, max_seqlen_k, hq, hkv, d, scale, causal, total_q=tq,
+                    total_k=tk)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device) if return_lse else None
+    ws = _workspace(fwd_workspace_size(p, True), q.device)
+    _check(_lib().attn_fwd_varlen(ctypes.byref(p), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws),
+                                  ws.numel(), _stream()), "attn_fwd_varlen")
+    return o, lse
+
+
+# -------------------------------------------------------------------- backward
+def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float] = None,
+        deterministic: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(do * o) for fixed-length BSHD inputs."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _expect(t, n)
+    _expect(lse, "lse", torch.float32)
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    p = make_params(b, sq, sk, hq, hkv, d, scale, causal, deterministic)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = workspace if workspace is not None else _workspace(bwd_workspace_size(p), q.device)
+    _check(_lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                           _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                           _stream()), "attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+               max_seqlen_k: int, causal: bool = False, softmax_scale: Optional[float] = None,
+               deterministic: bool = False):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _expect(t, n)
+    _expect(lse, "lse", torch.float32)
+    _expect(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _expect(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    nseq = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    p = make_params(nseq, max_seqlen_q, max_seqlen_k, hq, hkv, d, scale, causal, deterministic,
+                    total_q=tq, total_k=tk)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(bwd_workspace_size(p, True), q.device)
+    _check(_lib().attn_bwd_varlen(ctypes.byref(p), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()),
+           "attn_bwd_varlen")
+    return dq, dk, dv
+
+
+def bwd_phases(p: AttnParams, phases: int, q, k, v, o, do, lse, dq, dk, dv,
+               workspace: torch.Tensor, cu_seqlens_q=None, cu_seqlens_k=None) -> None:
+    """Run selected backward phases (mask of BWD_*) on the current stream."""
+    _check(_lib().attn_bwd_phases(ctypes.byref(p), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                  int(phases), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                  _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                  workspace.numel(), _stream()), "attn_bwd_phases")
+
+
+def bwd_status(p: AttnParams, workspace: torch.Tensor, varlen: bool = False) -> int:
+    val = ctypes.c_int32(0)
+    _check(_lib().attn_bwd_status(ctypes.byref(p), int(varlen), _ptr(workspace),
+                                  ctypes.byref(val), _stream()), "attn_bwd_status")
+    return val.value
+
+
+def tile_order(p: AttnParams, which: int):
+    """[(batch, head, block)] per workgroup for which = 0 fwd, 1 bwd, 2 deterministic bwd."""
+    lib = _lib()
+    count = ctypes.c_int64(0)
+    _check(lib.attn_tile_order(ctypes.byref(p), which, None, 0, ctypes.byref(count)), "attn_tile_order")
+    buf = (ctypes.c_int32 * (3 * count.value))()
+    _check(lib.attn_tile_order(ctypes.byref(p), which, buf, count.value, ctypes.byref(count)),
+           "attn_tile_order")
+    return [tuple(buf[3 * i:3 * i + 3]) for i in range(count.value)]
+
+
+def set_tuning(key: str, value: int) -> None:
+    _check(_lib().attn_set_tuning(key.encode(), int(value)), "attn_set_tuning")
+
+
+def version() -> int:
+    return _lib().attn_version()

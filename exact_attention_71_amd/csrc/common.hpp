@@ -1,0 +1,141 @@
+// Device helpers shared by the gfx950 attention kernels: MFMA fragment types,
+// bf16 packing, LDS swizzles, wavefront reductions and the two exp2 paths.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn71 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32x16 bf16 -> fp32.
+// Operand layout (lane l, g = l / 32, c = l % 32):
+//   A[m][k]: lane holds m = c, k = 8g .. 8g+7
+//   B[k][n]: lane holds n = c, k = 8g .. 8g+7
+//   C[m][n]: lane holds n = c, register i holds m = 8*(i/4) + 4*g + (i%4)
+// Only the C layout is relied on across instructions; A and B use the same
+// k slots, so any consistent k-to-slot assignment contracts correctly.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int c_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// Eight fp32 -> eight bf16 (round to nearest even) as one MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                        float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+  return r;
+}
+
+// C registers 8t .. 8t+7 of a 32x32 accumulator as a bf16 operand.
+__device__ __forceinline__ bf16x8 pack_half(const f32x16& x, int t) {
+  return pack8(x[8 * t + 0], x[8 * t + 1], x[8 * t + 2], x[8 * t + 3], x[8 * t + 4],
+               x[8 * t + 5], x[8 * t + 6], x[8 * t + 7]);
+}
+
+__device__ __forceinline__ bf16x4 pack4(float a0, float a1, float a2, float a3) {
+  bf16x4 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// LDS layouts.
+// Row-major tiles [rows][D] of bf16 are stored in 16-byte slots. Slot ch of
+// row r goes to slot ch ^ swz(r), chosen so that 16 consecutive rows read at
+// the same logical slot land in 16 distinct 16-byte bank groups of a 256-byte
+// bank line (and 8 consecutive rows in 8 distinct groups of a 128-byte line).
+// ---------------------------------------------------------------------------
+template <int ROW_ELEMS>
+__device__ __forceinline__ int swz_slot(int row, int ch) {
+  if constexpr (ROW_ELEMS * 2 >= 256) {
+    return ch ^ (row & 15);
+  } else if constexpr (ROW_ELEMS * 2 == 128) {
+    return ch ^ ((row >> 1) & 7);
+  } else {  // 64-byte rows
+    return ch ^ ((row >> 2) & 3);
+  }
+}
+
+// element offset of (row, 8-element chunk ch) in a swizzled [rows][ROW_ELEMS] tile
+template <int ROW_ELEMS>
+__device__ __forceinline__ int swz_off(int row, int ch) {
+  return row * ROW_ELEMS + swz_slot<ROW_ELEMS>(row, ch) * 8;
+}
+
+// Transposed operand tiles hold a key (or query) axis along the row. Within
+// every 16 consecutive positions, bits 2 and 3 of the index are swapped so
+// that the 8 values one lane needs for an MFMA operand built from a C
+// accumulator (indices 16t + 8h + 4g + r, h, r varying) are contiguous.
+__device__ __forceinline__ int perm16(int idx) {
+  return (idx & ~12) | ((idx & 4) << 1) | ((idx & 8) >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor32(float x) {
+  // exchange with lane l ^ 32
+  return __shfl_xor(x, 32, kWave);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Software 2^x on the FMA path: Cody-Waite split x = n + f, n = floor(x),
+// degree-3 Horner polynomial for 2^f on [0, 1) with p0 = 1 and p1..p3 the
+// minimax relative-error fit (max relative error 8.56e-5; the printed
+// 4-digit values are 0.6951, 0.2276, 0.0771), then n added into the exponent
+// field. Inputs below -126 (including -inf) return 0.
+__device__ __forceinline__ float emu_exp2(float x) {
+  const float xs = fmaxf(x, -127.0f);
+  const float n = __builtin_floorf(xs);
+  const float f = xs - n;
+  float p = __builtin_fmaf(0.07706713f, f, 0.22764487f);
+  p = __builtin_fmaf(p, f, 0.69511682f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  const int bits = __float_as_int(p) + (static_cast<int>(n) << 23);
+  return xs < -126.0f ? 0.0f : __int_as_float(bits);
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// ---------------------------------------------------------------------------
+// Buffer resources: raw buffer loads return zero past `bytes`, which handles
+// ragged sequence tails without branches. Offsets are 32-bit byte offsets.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, int voff, int soff) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+}  // namespace attn71

@@ -1,0 +1,330 @@
+// Forward attention kernel for gfx950: O = softmax(alpha Q K^T) V with a
+// tiled online softmax, conditional rescaling and a stored LSE.
+//
+// Method (FlashAttention-4 pages): two GEMMs with a softmax between them
+// (blog page, introduction); running row max, rescale of the accumulator only
+// when the max jumps by more than tau = log2(256) = 8 (digest page, item 3;
+// blog page, forward section equation), decided once per group of rows that
+// execute together; final division by the true row sum and optional LSE
+// (blog page, correction-warpgroup list).
+//
+// gfx950 design (our own, not the pages' Blackwell pipeline):
+//  * workgroup = 4 wavefronts; each wave owns 32*QB query rows and runs both
+//    GEMMs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+//  * S is computed transposed, S^T = K Q^T, so every lane owns one query row
+//    (lane % 32) and half of the keys of each 32-key block: the row max needs
+//    one exchange with lane ^ 32, the rescale factor is a per-lane scalar, and
+//    the accumulator of S^T is already the B operand of O^T = V^T P^T;
+//  * K tiles sit in LDS row-major with a 16-byte-slot XOR swizzle; V tiles are
+//    written transposed (V^T, key order permuted inside each 16 keys) so the
+//    A operand of the PV product is one 16-byte LDS read per lane;
+//  * K/V for tile n+1 are fetched into registers while tile n computes and
+//    written to the other LDS buffer: one barrier per tile;
+//  * the rescale decision is one ballot per wavefront (any row over tau);
+//  * exp2 runs on v_exp_f32; EMU > 0 moves EMU of every 8 elements to the
+//    Cody-Waite + Horner polynomial on the FMA path.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "schedule.hpp"
+
+namespace attn71 {
+
+namespace {
+
+// Padded LDS rows: one extra 16-byte slot per row shifts consecutive rows by
+// one bank group, so 16 lanes reading 16 consecutive rows at the same column
+// hit 16 distinct bank groups, and every per-lane address is a lane base plus
+// a compile-time offset.
+template <int D, int BN>
+struct FwdSmem {
+  static constexpr int KR = D + 8;    // K row stride (elements)
+  static constexpr int VR = BN + 8;   // V^T row stride (elements)
+  bf16 k[2][BN * KR];
+  bf16 vt[2][D * VR];
+};
+
+__device__ __forceinline__ void seq_bounds(const SeqView& sv, int seq, int64_t* q0, int* lq,
+                                           int64_t* k0, int* lk) {
+  if (sv.cu_q) {
+    const int a = sv.cu_q[seq], b = sv.cu_q[seq + 1];
+    const int c = sv.cu_k[seq], d = sv.cu_k[seq + 1];
+    *q0 = a; *lq = b - a; *k0 = c; *lk = d - c;
+  } else {
+    *q0 = (int64_t)seq * sv.seqlen_q; *lq = sv.seqlen_q;
+    *k0 = (int64_t)seq * sv.seqlen_k; *lk = sv.seqlen_k;
+  }
+}
+
+template <int D, int QB, int BN, int EMU>
+__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
+  constexpr int BM = 4 * 32 * QB;
+  constexpr int KS = D / 16;            // MFMA k-steps over the head dim
+  constexpr int NKB = BN / 32;          // 32-key blocks per tile
+  constexpr int NDB = D / 32;           // 32-row blocks of O^T
+  constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+  constexpr int KCH = BN * CPR / 256;   // K chunks staged per thread
+  constexpr int VU = (BN / 4) * CPR / 256;  // 4-key x 8-dim V units per thread
+  static_assert(KCH * 256 == BN * CPR, "K staging must divide evenly");
+  static_assert(VU * 256 == (BN / 4) * CPR, "V staging must divide evenly");
+  using SM = FwdSmem<D, BN>;
+  __shared__ SM sm;
+
+  // ---- which tile
+  Tile t;
+  if (p.sv.cu_q) {
+    t = varlen_tile(blockIdx.x, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
+    if (t.seq < 0) return;
+  } else {
+    t = fwd_tile_fixed(blockIdx.x, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
+  }
+  int64_t qs, ks0;
+  int lq, lk;
+  seq_bounds(p.sv, t.seq, &qs, &lq, &ks0, &lk);
+  const int m0 = t.block * BM;
+  if (m0 >= lq) return;
+  const int h = t.head;
+  const int kvh = h / p.group;
+  const bool causal = p.causal != 0;
+  const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int qw0 = m0 + w * 32 * QB;     // first query row of this wave
+  const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
+  const bf16* __restrict__ qp = static_cast<const bf16*>(p.q);
+  const bf16* __restrict__ kp = static_cast<const bf16*>(p.k);
+  const bf16* __restrict__ vp = static_cast<const bf16*>(p.v);
+
+  // ---- Q^T operands: lane holds query row (qb*32 + c), dims 16ks + 8g .. +7
+  const rsrc_t qr = make_rsrc(qp + qs * qstride + (int64_t)h * D,
+                              ((int64_t)(lq - 1) * qstride + D) * 2);
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + c;
+    const int voff = (row * (int)qstride + 8 * g) * 2;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = buf_load16(qr, voff + 32 * kk, 0);
+  }
+
+  // ---- K/V staging: buffers cover exactly this sequence's rows of this KV head
+  const int64_t kv_bytes = ((int64_t)(lk - 1) * kstride + D) * 2;
+  const bf16* kbase = kp + ks0 * kstride + (int64_t)kvh * D;
+  const bf16* vbase = vp + ks0 * kstride + (int64_t)kvh * D;
+  int koff[KCH], voffs[VU];
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int u = tid + 256 * j;
+    koff[j] = ((u / CPR) * (int)kstride + (u % CPR) * 8) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < VU; ++j) {
+    const int u = tid + 256 * j;
+    voffs[j] = ((4 * (u / CPR)) * (int)kstride + (u % CPR) * 8) * 2;
+  }
+  bf16x8 kreg[KCH];
+  bf16x8 vreg[VU][4];
+  auto load_tile = [&](int n) {
+    // one resource per tile (scalar math): the range check covers the tail
+    const int64_t t0 = (int64_t)n * BN * kstride;
+    const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
+    const rsrc_t vr = make_rsrc(vbase + t0, kv_bytes - 2 * t0);
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) kreg[j] = buf_load16(kr, koff[j], 0);
+#pragma unroll
+    for (int j = 0; j < VU; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vreg[j][r] = buf_load16(vr, voffs[j] + r * (int)kstride * 2, 0);
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int u = tid + 256 * j;
+      const int row = u / CPR, ch = u % CPR;
+      *reinterpret_cast<bf16x8*>(&sm.k[buf][row * SM::KR + ch * 8]) = kreg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = tid + 256 * j;
+      const int kg = u / CPR, dc = u % CPR;
+      const int pos = perm16(4 * kg);          // 4 keys stay contiguous
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = dc * 8 + e;
+        bf16x4 x;
+        x[0] = vreg[j][0][e]; x[1] = vreg[j][1][e]; x[2] = vreg[j][2][e]; x[3] = vreg[j][3][e];
+        const int off = d * SM::VR + pos;
+        *reinterpret_cast<bf16x4*>(&sm.vt[buf][off]) = x;
+      }
+    }
+  };
+
+  f32x16 oacc[QB][NDB];
+  float mref[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mref[qb] = neg_inf();
+    lsum[qb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
+  }
+  const float sl2 = p.scale_log2;
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int n = 0; n < n_tiles; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < n_tiles) load_tile(n + 1);
+    const int k0 = n * BN;
+    const bool active = !(causal && k0 > qw0 + 32 * QB - 1);
+    if (active) {
+      // S^T = K Q^T for this tile
+      f32x16 s[NKB][QB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &sm.k[buf][(kb * 32 + c) * SM::KR + (2 * kk + g) * 8]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(a, qf[qb][kk], s[kb][qb]);
+        }
+      }
+      // mask the ragged key tail and the causal diagonal
+      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int qrow = qw0 + qb * 32 + c;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + kb * 32 + c_row(i, g);
+              const bool hide = key >= lk || (causal && key > qrow);
+              s[kb][qb][i] = hide ? neg_inf() : s[kb][qb][i];
+            }
+          }
+      }
+      // running max and the per-wavefront rescale decision
+      float mnew[QB];
+      bool big = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = neg_inf();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][qb][i], s[kb][qb][i + 1]));
+        mx = fmaxf(mx, xor32(mx));
+        mnew[qb] = fmaxf(mref[qb], mx);
+        big = big || ((mnew[qb] - mref[qb]) * sl2 > kTau);
+      }
+      if (wave_any(big)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float fac = (mref[qb] == neg_inf()) ? 0.0f : fast_exp2((mref[qb] - mnew[qb]) * sl2);
+          lsum[qb] *= fac;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[qb][db] *= fac;
+          mref[qb] = mnew[qb];
+        }
+      }
+      // P = 2^(s*alpha*log2e - m_ref*alpha*log2e), row sums from fp32 p
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nb = (mref[qb] == neg_inf()) ? 0.0f : -mref[qb] * sl2;
+        float acc = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = __builtin_fmaf(s[kb][qb][i], sl2, nb);
+            const float e = ((i & 7) < EMU) ? emu_exp2(x) : fast_exp2(x);
+            s[kb][qb][i] = e;
+            acc += e;
+          }
+        lsum[qb] += acc;
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          bf16x8 pb[QB];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_half(s[kb][qb], tt);
+          const int slot = kb * 4 + tt * 2 + g;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int d = db * 32 + c;
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(&sm.vt[buf][d * SM::VR + slot * 8]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(a, pb[qb], oacc[qb][db]);
+          }
+        }
+    }
+    if (n + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O_acc / l (true statistics), LSE = alpha*m + ln(l)
+  bf16* __restrict__ op = static_cast<bf16*>(p.o);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = lsum[qb] + xor32(lsum[qb]);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const int row = qw0 + qb * 32 + c;
+    if (row < lq) {
+      bf16* dst = op + (qs + row) * qstride + (int64_t)h * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& x = oacc[qb][db];
+          *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * j) =
+              pack4(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv, x[4 * j + 3] * inv);
+        }
+      if (g == 0 && p.lse) {
+        const float val = lt > 0.0f ? mref[qb] * p.alpha + fast_log2(lt) * 0.69314718055994531f
+                                    : neg_inf();
+        const int64_t off = p.sv.cu_q ? (int64_t)h * p.sv.total_q + qs + row
+                                      : ((int64_t)t.seq * p.hq + h) * p.sv.seqlen_q + row;
+        p.lse[off] = val;
+      }
+    }
+  }
+}
+
+template <int D, int EMU>
+hipError_t launch_d(const FwdParams& p, int grid, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  hipLaunchKernelGGL((fwd_kernel<D, C::QB, C::BN, EMU>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// exp_emulation: 0 = all exp2 on v_exp_f32; 2 = 2 of every 8 on the FMA path
+hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation,
+                      hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const bool emu = exp_emulation == 2;
+  switch (d) {
+    case 64: return emu ? launch_d<64, 2>(p, grid, stream) : launch_d<64, 0>(p, grid, stream);
+    case 128: return emu ? launch_d<128, 2>(p, grid, stream) : launch_d<128, 0>(p, grid, stream);
+    case 256: return emu ? launch_d<256, 2>(p, grid, stream) : launch_d<256, 0>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn71

@@ -1,0 +1,100 @@
+// Kernel argument blocks and launchers shared by the host API and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn71 {
+
+// Softmax rescale threshold in base-2 units: tau = log2(256) = 8.0
+// (FlashAttention-4 digest page, item 3; blog page, forward rescaling equation).
+constexpr float kTau = 8.0f;
+
+struct SeqView {
+  const int* cu_q;        // packed varlen offsets (device), null for fixed length
+  const int* cu_k;
+  int batch;              // fixed: B; varlen: number of sequences
+  int seqlen_q, seqlen_k; // fixed length only
+  int total_q;            // rows of the packed q (varlen LSE stride)
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;             // may be null
+  SeqView sv;
+  const int* order;       // varlen: virtual -> actual sequence
+  const int* tile_prefix; // varlen: first tile of each virtual sequence
+  int hq, hkv, group;
+  int nm;                 // fixed: query blocks per sequence
+  int sec, nxcd;
+  int natural;            // 1: plain tile order (tuning / ablation)
+  int causal;
+  float alpha;            // softmax scale
+  float scale_log2;       // alpha * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;            // D = rowsum(dO o O), same layout as LSE
+  float* dq_acc;          // fp32 [rows][Hq][d]
+  int* sem;               // deterministic: one counter per (query block, query head)
+  int* ticket;            // deterministic: workgroup ticket counter
+  int* status;            // error word (non-zero: a bounded wait expired)
+  SeqView sv;
+  const int* order;       // varlen: virtual -> actual sequence (by key length)
+  const int* tile_prefix; // varlen: first tile of each virtual sequence
+  const int* mb_prefix;   // varlen: query-block prefix per actual sequence
+  int hq, hkv, group;
+  int nn;                 // fixed: key blocks per sequence
+  int nm;                 // fixed: query blocks per sequence
+  int sec, nxcd;
+  int natural;            // 1: plain tile order (non-deterministic only)
+  int causal, deterministic;
+  float alpha;
+  float scale_log2;
+  int64_t rows_q;         // total query rows (B*Sq or total_q)
+  int64_t n_sem;          // semaphore words to clear (deterministic)
+  int spin_limit;         // bounded wait for the deterministic chain
+};
+
+// Tile sizes (rows of the query block and keys of the key block) per head dim.
+template <int D> struct FwdCfg {
+  static constexpr int QB = (D <= 128) ? 2 : 1;   // 32-row query blocks per wave
+  static constexpr int BM = 4 * 32 * QB;
+  static constexpr int BN = (D == 64) ? 128 : 64;  // keys per tile
+};
+template <int D> struct BwdCfg {
+  static constexpr int BN = 128;                  // keys per workgroup (32 per wave)
+  static constexpr int BM = (D <= 128) ? 64 : 32; // queries per inner step
+};
+
+inline int fwd_block_m(int d) {
+  return d == 64 ? FwdCfg<64>::BM : d == 128 ? FwdCfg<128>::BM : FwdCfg<256>::BM;
+}
+inline int bwd_block_n(int) { return 128; }
+inline int bwd_block_m(int d) { return d <= 128 ? 64 : 32; }
+
+hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stream);
+hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
+// Varlen pre-pass: order[] = sequences by decreasing length of key_cu (ties
+// by index), tile_prefix[vs] = first tile of virtual sequence vs with
+// cdiv(len of count_cu, blk) * heads tiles each, and (optional) mb_prefix[s]
+// = first query block of actual sequence s with cdiv(len of q_cu, mb_blk).
+hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
+                                  int nseq, int heads, int blk, int* order, int* tile_prefix,
+                                  int* mb_prefix, int mb_blk, hipStream_t stream);
+
+}  // namespace attn71

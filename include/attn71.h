@@ -1,0 +1,172 @@
+/*
+ * attn71 — fused exact attention for AMD MI355X (gfx950), C ABI.
+ *
+ * The operation (FlashAttention-4 pages: digest page, notation table and
+ * roofline paragraph; blog page, introduction, forward section and backward
+ * section):
+ *
+ *   forward   S = alpha * Q K^T, P = softmax(S) over the visible keys,
+ *             O = P V, and optionally LSE = log sum_j exp(S_j) (natural log),
+ *             computed tile by tile with an online softmax whose rescale is
+ *             skipped while the row max grows by at most tau = log2(256) = 8
+ *             (base-2 units) and a final division by the true row sums;
+ *   backward  from Q, K, V, O, dO and the stored LSE: D = rowsum(dO o O),
+ *             P = exp(S - LSE), dP = dO V^T, dS = P o (dP - D),
+ *             dQ = alpha dS K, dK = alpha dS^T Q, dV = P^T dO.
+ *
+ * Conventions shared by every call
+ *   - q, k, v, o, dout, dq, dk, dv are bfloat16, contiguous, head dim
+ *     innermost, 16-byte aligned device pointers.
+ *     Fixed length: BSHD, q/o/dout/dq [batch, seqlen_q, num_heads_q, head_dim],
+ *     k/v/dk/dv [batch, seqlen_k, num_heads_kv, head_dim].
+ *     Packed variable length (the *_varlen calls): THD, q [total_q, Hq, d],
+ *     k [total_k, Hkv, d]; sequence s owns rows cu_seqlens[s] ..
+ *     cu_seqlens[s+1]-1.
+ *   - lse is float32, natural log. Fixed length [batch, Hq, seqlen_q];
+ *     varlen [Hq, total_q]. A row that sees no key gets O = 0, LSE = -inf.
+ *   - Grouped heads: num_heads_q % num_heads_kv == 0 and query head h reads
+ *     KV head h / (num_heads_q / num_heads_kv) (MQA: Hkv = 1, MHA: Hkv = Hq).
+ *     dK, dV are summed over the query heads of each group.
+ *   - causal: key j is visible to query i iff j <= i (lower triangular). It
+ *     requires equal query and key lengths (per sequence for varlen: the
+ *     caller passes cu_seqlens_k equal in content to cu_seqlens_q).
+ *   - softmax_scale (alpha) is finite and > 0, typically 1/sqrt(head_dim).
+ *   - head_dim is 64, 128 or 256; the device must be gfx950.
+ *
+ * Ownership and errors
+ *   - The caller owns all device memory, including the workspace (size from
+ *     the *_workspace_size calls). The library allocates and frees nothing
+ *     and keeps no pointer after a call returns. Host structs are read during
+ *     the call only.
+ *   - Every argument is validated before anything is enqueued: a status other
+ *     than ATTN_OK means no kernel was launched. ATTN_ERR_HIP reports a launch
+ *     error from the HIP runtime. Calls are asynchronous on `stream` (NULL =
+ *     the default stream); faults surface at the caller's next
+ *     synchronisation. Nothing is thrown across the ABI.
+ *   - Reentrant; the only global state is a per-device attribute cache and
+ *     the process-wide tuning knobs of attn_set_tuning.
+ */
+#ifndef ATTN71_H
+#define ATTN71_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN71_VERSION 100 /* 0.1.0 */
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad shape/scale/flag, misalignment */
+  ATTN_ERR_UNSUPPORTED = 2,         /* head_dim not in {64,128,256}, not gfx950, too large */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the *_workspace_size value */
+  ATTN_ERR_HIP = 4                  /* the HIP runtime refused a query or a launch */
+} attn_status;
+
+typedef struct attn_params {
+  int32_t batch;         /* fixed: B. varlen: number of packed sequences */
+  int32_t seqlen_q;      /* fixed: Sq. varlen: max query length (upper bound) */
+  int32_t seqlen_k;      /* fixed: Sk. varlen: max key length (upper bound) */
+  int32_t total_q;       /* varlen only: rows of q/o/dout/dq (ignored for fixed) */
+  int32_t total_k;       /* varlen only: rows of k/v/dk/dv (ignored for fixed) */
+  int32_t num_heads_q;   /* Hq >= 1 */
+  int32_t num_heads_kv;  /* Hkv >= 1, divides Hq */
+  int32_t head_dim;      /* 64, 128 or 256 */
+  float softmax_scale;   /* alpha */
+  int32_t causal;        /* 0 or 1 */
+  int32_t deterministic; /* backward only: 0 = fp32 atomics for dQ; 1 = fixed
+                            accumulation order, bit-identical dQ/dK/dV across runs
+                            (blog page, deterministic-mode section) */
+} attn_params;
+
+/* "OK", "invalid argument", ... ; never NULL. */
+const char* attn_status_string(attn_status status);
+/* ATTN71_VERSION of the built library. */
+int attn_version(void);
+
+/* Workspace bytes for a forward / backward call with these parameters
+ * (varlen = 1 for the *_varlen calls). 0 means no workspace is needed.
+ * Returns (size_t)-1 for parameters that the calls would reject. */
+size_t attn_fwd_workspace_size(const attn_params* p, int32_t varlen);
+size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen);
+
+/* Forward, fixed length. lse may be NULL (the LSE is optional on the pages:
+ * blog page, correction-warpgroup list, "optionally compute and store LSE"). */
+attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward, packed variable length. cu_seqlens_q / cu_seqlens_k: device int32
+ * [batch + 1], non-decreasing, starting at 0, ending at total_q / total_k.
+ * A pre-pass orders the sequences longest first (blog page, scheduling
+ * section, varlen sort and virtual-to-actual batch map). */
+attn_status attn_fwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const void* q, const void* k,
+                            const void* v, void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Backward, fixed length: dq, dk, dv from q, k, v, the forward's o and lse
+ * (required) and dout. Three launches on `stream`: preprocess (D, clears),
+ * main (dK, dV, dQ accumulation), postprocess (dQ to bf16). */
+attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward, packed variable length (same conventions as attn_fwd_varlen). */
+attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const void* q, const void* k,
+                            const void* v, const void* o, const void* dout, const float* lse,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* The backward split into its phases, for callers that schedule or time them
+ * separately. `phases` is a mask of ATTN_BWD_*; running the three masks in
+ * order on one stream with the same workspace equals attn_bwd(_varlen).
+ * cu_seqlens_q/k NULL = fixed length. Arguments a phase does not read may
+ * be NULL only if no selected phase reads them. */
+#define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); clear dQ accumulator, semaphores */
+#define ATTN_BWD_MAIN 2        /* dK, dV; dQ accumulation (reads D, LSE) */
+#define ATTN_BWD_POSTPROCESS 4 /* dQ = bf16(alpha * accumulator) */
+attn_status attn_bwd_phases(const attn_params* p, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t phases, const void* q,
+                            const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Diagnostics of the deterministic backward: the error word of the last
+ * backward that used this workspace (0 = fine; 1 = a bounded wait of the
+ * ordered dQ chain expired and the ordering was abandoned). Synchronous:
+ * waits for `stream`. */
+attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* workspace,
+                            int32_t* status_out, hipStream_t stream);
+
+/* Tile order of the fixed-length kernels, evaluated on the host with the
+ * same arithmetic the kernels use (scheduling section of the blog page:
+ * longest first, L2-sized batch-head sections; here also one contiguous range
+ * per XCD). which = 0: forward, out[3*i..3*i+2] = (batch, query head,
+ * query block) of workgroup i; which = 1: non-deterministic backward,
+ * which = 2: deterministic backward in ticket order, (batch, KV head, key
+ * block). *count receives the grid size; at most `capacity` triples are
+ * written. No GPU is needed. */
+attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,
+                            int64_t* count);
+
+/* Process-wide tuning knobs (not synchronised with launches in flight):
+ *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
+ *                   (batch-head major, blocks ascending, no remap);
+ *   "exp_emulation" 0 = every exp2 on v_exp_f32 (default), 2 = 2 of every 8
+ *                   on the Cody-Waite + Horner FMA path (blog page, faster
+ *                   exponential section);
+ *   "spin_limit"    bound on each wait of the deterministic chain (default
+ *                   2^26 polls).
+ * Returns ATTN_ERR_INVALID_ARGUMENT for unknown keys or values. */
+attn_status attn_set_tuning(const char* key, int32_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN71_H */

@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/attn71.h declares, validates arguments before touching
+the device, sizes workspaces, and produces the documented tile orders."""
+import collections
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_71_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn71.h")
+
+INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 3
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ea.load()
+    names = _declared()
+    assert "attn_fwd" in names and "attn_bwd_varlen" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(ea.EXPORTS)
+
+
+def test_version_and_status_strings():
+    lib = ea.load()
+    assert ea.version() == 100
+    assert lib.attn_status_string(0) == b"OK"
+    assert lib.attn_status_string(3) == b"workspace too small"
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def _p(**kw):
+    base = dict(batch=2, seqlen_q=300, seqlen_k=300, heads_q=4, heads_kv=2, head_dim=128,
+                scale=0.088, causal=False, deterministic=False)
+    base.update(kw)
+    return ea.make_params(base["batch"], base["seqlen_q"], base["seqlen_k"], base["heads_q"],
+                          base["heads_kv"], base["head_dim"], base["scale"], base["causal"],
+                          base["deterministic"], base.get("total_q", 0), base.get("total_k", 0))
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=32), UNSUPPORTED),
+    (dict(heads_q=3, heads_kv=2), INVALID), (dict(heads_kv=0), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(causal=True, seqlen_k=299), INVALID), (dict(batch=-1), INVALID),
+    (dict(seqlen_q=1 << 24, heads_q=64, heads_kv=64), UNSUPPORTED),
+])
+def test_forward_rejects_bad_parameters(kw, status):
+    lib = ea.load()
+    p = _p(**kw)
+    st = lib.attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == status
+    st = lib.attn_bwd(ctypes.byref(p), *([FAKE] * 9), FAKE, 1 << 30, None)
+    assert st == status
+
+
+def test_forward_rejects_null_and_misaligned_pointers():
+    lib = ea.load()
+    p = _p()
+    assert lib.attn_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+    assert lib.attn_fwd(ctypes.byref(p), FAKE + 2, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+    assert lib.attn_fwd(None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+    assert lib.attn_fwd_varlen(ctypes.byref(p), None, None, FAKE, FAKE, FAKE, FAKE, None, None,
+                               0, None) == INVALID
+
+
+def test_backward_requires_lse_and_workspace():
+    lib = ea.load()
+    p = _p()
+    need = ea.bwd_workspace_size(p)
+    args = [FAKE] * 9   # q k v o dout lse dq dk dv
+    args[5] = None      # lse
+    assert lib.attn_bwd(ctypes.byref(p), *args, FAKE, need, None) == INVALID
+    assert lib.attn_bwd(ctypes.byref(p), *([FAKE] * 9), FAKE, need - 1, None) == WS_SMALL
+    assert lib.attn_bwd(ctypes.byref(p), *([FAKE] * 9), None, need, None) == INVALID
+    assert lib.attn_bwd_phases(ctypes.byref(p), None, None, 0, *([FAKE] * 9), FAKE, need,
+                               None) == INVALID
+    assert lib.attn_bwd_phases(ctypes.byref(p), FAKE, None, 7, *([FAKE] * 9), FAKE, need,
+                               None) == INVALID
+
+
+def test_empty_batch_is_a_no_op():
+    lib = ea.load()
+    p = _p(batch=0)
+    assert lib.attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 0
+
+
+def test_workspace_sizes():
+    p = _p()
+    assert ea.fwd_workspace_size(p) == 0
+    rows, hq, d = 2 * 300, 4, 128
+    need = ea.bwd_workspace_size(p)
+    assert need >= rows * hq * 4 + rows * hq * d * 4          # D and the dQ accumulator
+    pd = _p(deterministic=True)
+    assert ea.bwd_workspace_size(pd) > need                     # + semaphores
+    pv = _p(total_q=1000, total_k=1000, batch=5)
+    assert ea.fwd_workspace_size(pv, True) > 0
+    assert ea.fwd_workspace_size(_p(head_dim=80)) == SIZE_MAX
+    assert ea.bwd_workspace_size(_p(heads_q=5)) == SIZE_MAX
+
+
+def test_tuning_knobs():
+    ea.set_tuning("tile_order", 1)
+    ea.set_tuning("tile_order", 0)
+    ea.set_tuning("exp_emulation", 2)
+    ea.set_tuning("exp_emulation", 0)
+    with pytest.raises(ea.AttnError):
+        ea.set_tuning("no_such_knob", 1)
+    with pytest.raises(ea.AttnError):
+        ea.set_tuning("exp_emulation", 3)
+
+
+# ------------------------------------------------------------------ tile order
+def _bm(d):
+    return 256 if d <= 128 else 128
+
+
+@pytest.mark.parametrize("b,s,hq,hkv,d,causal", [
+    (2, 8192, 16, 16, 128, True), (4, 4096, 16, 16, 128, False), (1, 16384, 8, 8, 64, True),
+    (1, 1000, 3, 1, 256, True), (3, 777, 2, 2, 128, False)])
+def test_forward_tile_order_is_a_permutation_longest_first(b, s, hq, hkv, d, causal):
+    p = _p(batch=b, seqlen_q=s, seqlen_k=s, heads_q=hq, heads_kv=hkv, head_dim=d, causal=causal)
+    order = ea.tile_order(p, 0)
+    nm = -(-s // _bm(d))
+    assert len(order) == b * hq * nm
+    assert sorted(order) == sorted((bb, h, m) for bb in range(b) for h in range(hq) for m in range(nm))
+    # per XCD (workgroup i runs on XCD i % 8) and per batch-head, blocks are longest first
+    seen = collections.defaultdict(list)
+    for i, (bb, h, m) in enumerate(order):
+        seen[(i % 8, bb, h)].append(m)
+    for ms in seen.values():
+        assert ms == sorted(ms, reverse=True)
+    if (b * hq) % 8 == 0:
+        # each XCD gets whole batch-heads
+        owner = {}
+        for i, (bb, h, m) in enumerate(order):
+            assert owner.setdefault((bb, h), i % 8) == i % 8
+
+
+@pytest.mark.parametrize("b,s,hq,hkv,d", [(2, 8192, 16, 16, 128), (1, 16384, 8, 8, 256),
+                                         (1, 3000, 8, 2, 64)])
+def test_backward_tile_orders(b, s, hq, hkv, d):
+    p = _p(batch=b, seqlen_q=s, seqlen_k=s, heads_q=hq, heads_kv=hkv, head_dim=d, causal=True)
+    nn = -(-s // 128)
+    full = sorted((bb, h, n) for bb in range(b) for h in range(hkv) for n in range(nn))
+    lpt = ea.tile_order(p, 1)
+    assert sorted(lpt) == full
+    det = ea.tile_order(p, 2)
+    assert sorted(det) == full
+    # deterministic order: for each (batch, KV head) key blocks strictly descending, so every
+    # workgroup only ever waits on workgroups that took earlier tickets
+    pos = {}
+    for i, t in enumerate(det):
+        pos[t] = i
+    for bb in range(b):
+        for h in range(hkv):
+            idx = [pos[(bb, h, n)] for n in range(nn)]
+            assert all(idx[n] > idx[n + 1] for n in range(nn - 1))
+
+
+def test_natural_tile_order_knob():
+    p = _p(batch=1, seqlen_q=1024, seqlen_k=1024, heads_q=2, heads_kv=2, causal=True)
+    ea.set_tuning("tile_order", 1)
+    try:
+        nat = ea.tile_order(p, 0)
+    finally:
+        ea.set_tuning("tile_order", 0)
+    assert nat == [(0, h, m) for h in range(2) for m in range(4)]

@@ -1,0 +1,210 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Sizes here are small enough for the oracle to finish in seconds while still
+spanning several tiles and a ragged tail; the full-size workloads are sampled
+in test_gpu_fullsize.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_71_amd as ea
+import oracle
+from parity import check_grads, check_lse, check_o, to64
+from workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _dev(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def _run_fixed(b, s, hq, hkv, d, causal, seed, scaled=False, det=False, sk=None, bwd=True):
+    sk = s if sk is None else sk
+    inp = make_inputs(b, s, sk, hq, hkv, d, seed=seed, scaled_heads=scaled)
+    g = _dev(inp)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal)
+    what = f"b{b} s{s}/{sk} hq{hq} hkv{hkv} d{d} causal{causal}"
+    check_o(o, o_ref, what)
+    check_lse(lse, lse_ref, what)
+    if not bwd:
+        return
+    dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=causal,
+                        softmax_scale=scale, deterministic=det)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal)
+    check_grads((dq, dk, dv), ref, what)
+
+
+def test_small_workload_fwd_bwd():
+    w = WORKLOADS["small"]
+    inp = workload_inputs(w)
+    g = _dev(inp)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=False, softmax_scale=w.scale)
+    dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=False,
+                        softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], w.scale, False)
+    e = check_o(o, o_ref, "small")
+    assert e["max_abs"] <= 1e-2          # plain criterion holds at this size
+    check_lse(lse, lse_ref, "small")
+    check_grads((dq, dk, dv), oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"],
+                                                        w.scale, False), "small")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(d, causal):
+    _run_fixed(1, 300, 2, 2, d, causal, seed=100 + d)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (4, 1), (6, 3)])
+def test_grouped_heads(hq, hkv):
+    _run_fixed(2, 200, hq, hkv, 128, True, seed=7 + hq + hkv)
+
+
+def test_non_causal_unequal_lengths():
+    _run_fixed(2, 130, 2, 1, 64, False, seed=3, sk=333)
+
+
+def test_scaled_heads_exercise_rescale():
+    """Q, K x3 on half the heads: logit std ~9, max jumps above tau occur."""
+    _run_fixed(1, 1024, 4, 4, 128, True, seed=31, scaled=True)
+    _run_fixed(1, 700, 2, 2, 64, False, seed=32, scaled=True)
+
+
+def test_lse_is_optional_and_output_unchanged():
+    inp = make_inputs(1, 256, 256, 2, 2, 128, seed=5, with_grad=False)
+    g = _dev(inp)
+    o1, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    o2, none = ea.fwd(g["q"], g["k"], g["v"], causal=True, return_lse=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_matches_oracle(causal):
+    lengths = [1, 17, 300, 0, 513, 64, 129]
+    hq, hkv, d = 4, 2, 128
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=41, lengths=lengths)
+    g = _dev(inp)
+    scale = 1.0 / math.sqrt(d)
+    mx = max(lengths)
+    o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], mx, mx,
+                           causal=causal, softmax_scale=scale)
+    dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
+                               g["cu_seqlens_k"], mx, mx, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal,
+                                              inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    check_o(o, o_ref, "varlen")
+    check_lse(lse, lse_ref, "varlen")
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal,
+                                    inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    check_grads((dq, dk, dv), ref, "varlen")
+
+
+def test_varlen_non_causal_different_key_lengths():
+    lq, lk = [40, 300, 7], [260, 0, 90]
+    hq, hkv, d = 2, 1, 64
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=43, lengths=lq, lengths_k=lk)
+    g = _dev(inp)
+    scale = 0.125
+    o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], max(lq),
+                           max(lk), causal=False, softmax_scale=scale)
+    dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
+                               g["cu_seqlens_k"], max(lq), max(lk), softmax_scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, False,
+                                              inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    check_o(o, o_ref, "varlen-k")
+    check_lse(lse, lse_ref, "varlen-k")      # the empty key sequence gives -inf rows
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, False,
+                                    inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    assert torch.all(dq[40:340] == 0)        # rows that see no key have zero gradient
+    check_grads((dq, dk, dv), ref, "varlen-k")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_deterministic_backward_is_bit_identical(d):
+    s, hq, hkv = 640, 4, 2
+    inp = make_inputs(1, s, s, hq, hkv, d, seed=51 + d)
+    g = _dev(inp)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=scale)
+    p = ea.make_params(1, s, s, hq, hkv, d, scale, True, True)
+    ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
+    runs = []
+    for _ in range(3):
+        runs.append(ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True,
+                           softmax_scale=scale, deterministic=True, workspace=ws))
+        torch.cuda.synchronize()
+        assert ea.bwd_status(p, ws) == 0
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True)
+    check_grads(runs[0], ref, f"det d{d}")
+
+
+def test_backward_phases_equal_full_backward():
+    s, hq, hkv, d = 384, 2, 2, 128
+    inp = make_inputs(1, s, s, hq, hkv, d, seed=61)
+    g = _dev(inp)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True)
+    ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
+    full = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True)
+    dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
+    for ph in (ea.BWD_PREPROCESS, ea.BWD_MAIN, ea.BWD_POSTPROCESS):
+        ea.bwd_phases(p, ph, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(full, (dq, dk, dv)):
+        assert torch.equal(a, b)
+
+
+def test_forward_independent_of_tile_order():
+    """No cross-tile reduction in the forward: any tile order gives the same bits."""
+    inp = make_inputs(2, 1024, 1024, 8, 8, 128, seed=71, with_grad=False)
+    g = _dev(inp)
+    o1, l1 = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    ea.set_tuning("tile_order", 1)
+    try:
+        o2, l2 = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    finally:
+        ea.set_tuning("tile_order", 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_exp_emulation_variant_matches_oracle():
+    inp = make_inputs(1, 512, 512, 2, 2, 128, seed=81, scaled_heads=True, with_grad=False)
+    g = _dev(inp)
+    ea.set_tuning("exp_emulation", 2)
+    try:
+        o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    finally:
+        ea.set_tuning("exp_emulation", 0)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], 1 / math.sqrt(128), True)
+    check_o(o, o_ref, "emu")
+    check_lse(lse, lse_ref, "emu")
+
+
+def test_gqa_equals_repeated_kv_on_gpu():
+    inp = make_inputs(1, 256, 256, 8, 2, 64, seed=91)
+    g = _dev(inp)
+    o1, l1 = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    kr = g["k"].repeat_interleave(4, dim=2).contiguous()
+    vr = g["v"].repeat_interleave(4, dim=2).contiguous()
+    o2, l2 = ea.fwd(g["q"], kr, vr, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
