@@ -9,7 +9,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/attn71.h"
+#include "attn71.h"
 #include "kernels.hpp"
 #include "schedule.hpp"
 

@@ -116,19 +116,19 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const float* __restrict__
 // bwd_main
 // ---------------------------------------------------------------------------
 template <int D, int BM, int BN>
-struct BwdSmem {
+struct alignas(16) BwdSmem {
   static constexpr int QR = D + 8;    // row-major Q / dO (rows = queries)
   static constexpr int TR = BM + 8;   // transposed Q^T / dO^T (rows = dims)
   static constexpr int SR = BN + 8;   // dS (rows = queries)
   static constexpr int KR = BN + 8;   // K^T (rows = dims)
-  bf16 q[BM * QR];
-  bf16 dout[BM * QR];
-  bf16 qt[D * TR];
-  bf16 dot[D * TR];
-  bf16 ds[BM * SR];
-  bf16 kt[D * KR];
-  float lse2[BM];
-  float dsum[BM];
+  alignas(16) bf16 q[BM * QR];
+  alignas(16) bf16 dout[BM * QR];
+  alignas(16) bf16 qt[D * TR];
+  alignas(16) bf16 dot[D * TR];
+  alignas(16) bf16 ds[BM * SR];
+  alignas(16) bf16 kt[D * KR];
+  alignas(16) float lse2[BM];
+  alignas(16) float dsum[BM];
   int ticket;
 };
 
@@ -155,7 +155,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   // ---- which key block (deterministic: ticket order = shortest first)
   int v = blockIdx.x;
   if (det) {
-    if (tid == 0) sm.ticket = atomicAdd(p.ticket, 1);
+    // Every workgroup of a launch takes one ticket, so a launch consumes
+    // exactly gridDim.x tickets; the modulo keeps v inside this launch's grid
+    // even if the counter was not cleared since the previous launch.
+    if (tid == 0) sm.ticket = (int)((unsigned)atomicAdd(p.ticket, 1) % gridDim.x);
     __syncthreads();
     v = sm.ticket;
   }
@@ -164,6 +167,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     t = varlen_tile(v, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/det);
     if (t.seq < 0) return;
   } else {
+    if (v >= p.sv.batch * p.hkv * p.nn) return;
     t = bwd_tile_fixed(v, p.sv.batch, p.hkv, p.nn, p.sec, det, p.nxcd, p.natural != 0);
   }
   int64_t qs, ks0;
@@ -226,8 +230,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     const rsrc_t ors = make_rsrc(static_cast<const bf16*>(p.dout) + qb0, bytes);
 #pragma unroll
     for (int j = 0; j < QUT; ++j) {
-      const int u = tid + 256 * j;
-      const int qg = u / CPR, dc = u % CPR;
+      const int u = imin(tid + 256 * j, QU - 1);
+      int qg, dc;
+      unit_coords<CPR, BM / 4>(u, &qg, &dc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int off = ((4 * qg + r) * (int)qstride + dc * 8) * 2;
@@ -252,7 +257,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     for (int j = 0; j < QUT; ++j) {
       const int u = tid + 256 * j;
       if (QU % 256 == 0 || u < QU) {
-        const int qg = u / CPR, dc = u % CPR;
+        int qg, dc;
+        unit_coords<CPR, BM / 4>(u, &qg, &dc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           *reinterpret_cast<bf16x8*>(&sm.q[(4 * qg + r) * SM::QR + dc * 8]) = qreg[j][r];

@@ -96,6 +96,33 @@ __device__ __forceinline__ float xor32(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+// max of three floats in one instruction. Written as inline asm because the
+// compiler otherwise quiets every MFMA result (an extra v_max per element)
+// before fmaxf; MFMA never produces signalling NaNs, so that step is moot here.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Staging-unit mapping for tiles written to LDS both row-major and transposed.
+// A unit is 4 rows x 8 columns (four 16-byte global loads). Within a
+// wavefront, CL consecutive lanes take CL consecutive column chunks of one row
+// group (coalesced loads) and the remaining lane bits take distinct row
+// groups, so a transposed 8-byte store spreads over all LDS banks (each bank
+// hit twice for 512 bytes, the minimum) instead of hitting a few banks eight
+// times.
+template <int CPR, int RG>   // CPR column chunks per row, RG row groups per tile
+__device__ __forceinline__ void unit_coords(int u, int* rg, int* ch) {
+  constexpr int CL = (RG >= 16) ? 4 : 64 / RG;   // consecutive chunks per row group
+  static_assert(CPR % CL == 0 && (CL & (CL - 1)) == 0, "unit mapping needs CL | CPR");
+  const int lo = u % CL;
+  const int g = (u / CL) % RG;
+  const int hi = (u / CL) / RG;
+  *rg = g;
+  *ch = hi * CL + lo;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }

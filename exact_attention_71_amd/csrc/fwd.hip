@@ -36,11 +36,11 @@ namespace {
 // hit 16 distinct bank groups, and every per-lane address is a lane base plus
 // a compile-time offset.
 template <int D, int BN>
-struct FwdSmem {
+struct alignas(16) FwdSmem {
   static constexpr int KR = D + 8;    // K row stride (elements)
   static constexpr int VR = BN + 8;   // V^T row stride (elements)
-  bf16 k[2][BN * KR];
-  bf16 vt[2][D * VR];
+  alignas(16) bf16 k[2][BN * KR];
+  alignas(16) bf16 vt[2][D * VR];
 };
 
 __device__ __forceinline__ void seq_bounds(const SeqView& sv, int seq, int64_t* q0, int* lq,
@@ -55,17 +55,19 @@ __device__ __forceinline__ void seq_bounds(const SeqView& sv, int seq, int64_t* 
   }
 }
 
-template <int D, int QB, int BN, int EMU>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr int BM = 4 * 32 * QB;
+template <int D, int NW, int QB, int BN, int EMU>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
+  constexpr int NT = NW * 64;           // threads
+  constexpr int BM = NW * 32 * QB;
   constexpr int KS = D / 16;            // MFMA k-steps over the head dim
   constexpr int NKB = BN / 32;          // 32-key blocks per tile
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-  constexpr int KCH = BN * CPR / 256;   // K chunks staged per thread
-  constexpr int VU = (BN / 4) * CPR / 256;  // 4-key x 8-dim V units per thread
-  static_assert(KCH * 256 == BN * CPR, "K staging must divide evenly");
-  static_assert(VU * 256 == (BN / 4) * CPR, "V staging must divide evenly");
+  constexpr int KCH = BN * CPR / NT;    // K chunks staged per thread
+  constexpr int VUN = (BN / 4) * CPR;   // 4-key x 8-dim V units per tile
+  constexpr int VU = (VUN + NT - 1) / NT;  // V units per thread (last may be partial)
+  static_assert(KCH * NT == BN * CPR, "K staging must divide evenly");
+  static_assert(VUN % 64 == 0, "V staging covers whole wavefronts");
   using SM = FwdSmem<D, BN>;
   __shared__ SM sm;
 
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     t = varlen_tile(blockIdx.x, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
     if (t.seq < 0) return;
   } else {
+    if ((int)blockIdx.x >= p.sv.batch * p.hq * p.nm) return;
     t = fwd_tile_fixed(blockIdx.x, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
   }
   int64_t qs, ks0;
@@ -114,13 +117,15 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   int koff[KCH], voffs[VU];
 #pragma unroll
   for (int j = 0; j < KCH; ++j) {
-    const int u = tid + 256 * j;
+    const int u = tid + NT * j;
     koff[j] = ((u / CPR) * (int)kstride + (u % CPR) * 8) * 2;
   }
 #pragma unroll
   for (int j = 0; j < VU; ++j) {
-    const int u = tid + 256 * j;
-    voffs[j] = ((4 * (u / CPR)) * (int)kstride + (u % CPR) * 8) * 2;
+    const int u = imin(tid + NT * j, VUN - 1);   // idle lanes re-read a valid unit
+    int kg, dc;
+    unit_coords<CPR, BN / 4>(u, &kg, &dc);
+    voffs[j] = ((4 * kg) * (int)kstride + dc * 8) * 2;
   }
   bf16x8 kreg[KCH];
   bf16x8 vreg[VU][4];
@@ -139,14 +144,16 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int u = tid + 256 * j;
+      const int u = tid + NT * j;
       const int row = u / CPR, ch = u % CPR;
       *reinterpret_cast<bf16x8*>(&sm.k[buf][row * SM::KR + ch * 8]) = kreg[j];
     }
 #pragma unroll
     for (int j = 0; j < VU; ++j) {
-      const int u = tid + 256 * j;
-      const int kg = u / CPR, dc = u % CPR;
+      const int u = tid + NT * j;
+      if (VUN % NT != 0 && u >= VUN) continue;   // whole wavefronts skip together
+      int kg, dc;
+      unit_coords<CPR, BN / 4>(u, &kg, &dc);
       const int pos = perm16(4 * kg);          // 4 keys stay contiguous
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][qb][i], s[kb][qb][i + 1]));
+          for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kb][qb][i], s[kb][qb][i + 1]);
         mx = fmaxf(mx, xor32(mx));
         mnew[qb] = fmaxf(mref[qb], mx);
         big = big || ((mnew[qb] - mref[qb]) * sl2 > kTau);
@@ -308,7 +315,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 template <int D, int EMU>
 hipError_t launch_d(const FwdParams& p, int grid, hipStream_t stream) {
   using C = FwdCfg<D>;
-  hipLaunchKernelGGL((fwd_kernel<D, C::QB, C::BN, EMU>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, C::NW, C::QB, C::BN, EMU>), dim3(grid), dim3(C::NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -69,10 +69,20 @@ struct BwdParams {
 };
 
 // Tile sizes (rows of the query block and keys of the key block) per head dim.
+#ifndef ATTN71_FWD_NW
+#define ATTN71_FWD_NW 8
+#endif
+#ifndef ATTN71_FWD_QB
+#define ATTN71_FWD_QB 1
+#endif
+#ifndef ATTN71_FWD_BN
+#define ATTN71_FWD_BN 128
+#endif
 template <int D> struct FwdCfg {
-  static constexpr int QB = (D <= 128) ? 2 : 1;   // 32-row query blocks per wave
-  static constexpr int BM = 4 * 32 * QB;
-  static constexpr int BN = (D == 64) ? 128 : 64;  // keys per tile
+  static constexpr int NW = (D <= 128) ? ATTN71_FWD_NW : 4; // wavefronts per workgroup
+  static constexpr int QB = (D <= 128) ? ATTN71_FWD_QB : 1; // 32-row query blocks per wave
+  static constexpr int BM = NW * 32 * QB;
+  static constexpr int BN = (D == 64) ? 128 : (D == 256 ? 64 : ATTN71_FWD_BN);  // keys per tile
 };
 template <int D> struct BwdCfg {
   static constexpr int BN = 128;                  // keys per workgroup (32 per wave)

@@ -50,6 +50,7 @@ A71_HD int xcd_remap(int i, int n, int nx) {
 // Section order over a regular grid of nbh batch-heads x nblk blocks:
 // sections of `sec` batch-heads; inside a section blocks are visited from
 // `first` in the direction given by `reverse`, batch-heads innermost.
+// Requires 0 <= v < nbh * nblk (callers check).
 A71_HD void section_decode(int v, int nbh, int nblk, int sec, bool reverse, int* bh, int* blk) {
   const int per_sec = sec * nblk;
   const int s = v / per_sec;

@@ -126,7 +126,11 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  * separately. `phases` is a mask of ATTN_BWD_*; running the three masks in
  * order on one stream with the same workspace equals attn_bwd(_varlen).
  * cu_seqlens_q/k NULL = fixed length. Arguments a phase does not read may
- * be NULL only if no selected phase reads them. */
+ * be NULL only if no selected phase reads them. Every MAIN phase needs a
+ * PREPROCESS phase of the same workspace before it: it clears the dQ
+ * accumulator and, in deterministic mode, the ordering state. A MAIN phase
+ * run without it still terminates and stays in bounds, but dQ accumulates on
+ * the previous values and the deterministic order is not guaranteed. */
 #define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); clear dQ accumulator, semaphores */
 #define ATTN_BWD_MAIN 2        /* dK, dV; dQ accumulation (reads D, LSE) */
 #define ATTN_BWD_POSTPROCESS 4 /* dQ = bf16(alpha * accumulator) */

@@ -208,3 +208,32 @@ def test_gqa_equals_repeated_kv_on_gpu():
     o2, l2 = ea.fwd(g["q"], kr, vr, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_deterministic_main_without_preprocess_stays_in_bounds():
+    """Regression: a MAIN phase launched again without PREPROCESS used to draw
+    tickets past the grid. It must now terminate in bounds; a later full
+    backward (which clears the state) is again bit-identical to the first."""
+    s, hq, hkv, d = 512, 2, 2, 128
+    inp = make_inputs(1, s, s, hq, hkv, d, seed=111)
+    g = _dev(inp)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+    p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True)
+    ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
+    first = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
+                   workspace=ws)
+    dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
+    ea.set_tuning("spin_limit", 1 << 14)
+    try:
+        ea.bwd_phases(p, ea.BWD_PREPROCESS | ea.BWD_MAIN, g["q"], g["k"], g["v"], o, g["do"], lse,
+                      dq, dk, dv, ws)
+        ea.bwd_phases(p, ea.BWD_MAIN, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
+        torch.cuda.synchronize()
+    finally:
+        ea.set_tuning("spin_limit", 1 << 26)
+    again = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
+                   workspace=ws)
+    torch.cuda.synchronize()
+    assert ea.bwd_status(p, ws) == 0
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)
