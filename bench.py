@@ -28,6 +28,34 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_causal8k.txt")
+
+
+def sources_sha() -> str:
+    """Hash of the kernel sources and build flags (identifies the measured build)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "exact_attention_71_amd")
+    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, only when it was
+    taken on these exact sources (else None)."""
+    try:
+        lines = open(TRAFFIC_FILE).read().split("\n")
+    except OSError:
+        return None
+    sha = sources_sha()
+    for ln in lines:
+        f = dict(kv.split("=", 1) for kv in ln.split() if "=" in kv)
+        if f.get("kernel") == kernel and f.get("workload") == workload and f.get("sources") == sha:
+            return int(f["bytes"])
+    return None
 
 
 def _describe(w) -> str:
@@ -90,6 +118,9 @@ def main() -> int:
     ap.add_argument("--workload", default="causal8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device 3 times (a known-size kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention path "
@@ -104,6 +135,14 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] workload {_describe(w)}", file=sys.stderr, flush=True)
     inp = workload_inputs(w, device=dev)
     lengths = draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number) if w.varlen else None
@@ -203,6 +242,7 @@ def main() -> int:
     fwd_ms = f0.elapsed_time(f1) / args.steps
 
     total_flops = fl["fwd+bwd"] if with_bwd else fl["fwd"]
+    dom_name = f"bwd_main_kernel<{w.head_dim}>" if with_bwd else f"fwd_kernel<{w.head_dim}>"
     value = total_flops / (ms * 1e-3) / 1e12
     dom_flops = fl["bwd"] if with_bwd else fl["fwd"]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -223,10 +263,11 @@ def main() -> int:
                    "fwd_tflops": round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12, 2),
                    "fwd_ms": round(fwd_ms, 4),
                    "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "bwd_main_kernel" if with_bwd else "fwd_kernel",
+        "roofline": {"bound": "mfma", "kernel": dom_name,
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "avg_launch_ms": round(dom_ms, 4)},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom_name, w.name),
+                     "avg_launch_ms": round(dom_ms, 4), "sources": sources_sha()},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -22,11 +22,12 @@ than itself (a library routine, finite differences, closed forms, invariants or
 a number printed on the pages); see ``tests/test_oracle_*.py``.
 """
 from .attention import (attention_forward, attention_backward, attention_probs,
-                        rowsum_do_o, repeat_kv)
+                        rowsum_do_o, repeat_kv, head_forward, head_backward, head_dq_rows,
+                        head_dkdv_cols)
 from .blockwise import blockwise_forward
 from .exp2poly import exp2_cody_waite, fit_exp2_minimax, PAGE_COEFFS
 from .bf16 import round_bf16, bf16_ulp
 
 __all__ = ["attention_forward", "attention_backward", "attention_probs", "rowsum_do_o",
-           "repeat_kv", "blockwise_forward", "exp2_cody_waite", "fit_exp2_minimax",
+           "repeat_kv", "head_forward", "head_backward", "head_dq_rows", "head_dkdv_cols", "blockwise_forward", "exp2_cody_waite", "fit_exp2_minimax",
            "PAGE_COEFFS", "round_bf16", "bf16_ulp"]

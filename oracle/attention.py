@@ -121,6 +121,35 @@ def head_backward(qh, kh, vh, doh, scale, causal):
     return dq, dk, dv
 
 
+def head_dq_rows(qh, kh, vh, doh, scale, causal, rows):
+    """dQ for selected query rows of one (sequence, head), from the definition
+    row by row: P_i from LSE_i, O_i = P_i V, D_i = dO_i . O_i,
+    dS_i = P_i (dO_i V^T - D_i), dQ_i = alpha dS_i K."""
+    rows = np.asarray(rows)
+    _, lse = head_forward(qh, kh, vh, scale, causal, rows=rows)
+    p = head_probs(qh, kh, scale, causal, lse, rows=rows)
+    o = p @ vh
+    dd = np.sum(doh[rows] * o, axis=1)
+    ds = p * (doh[rows] @ vh.T - dd[:, None])
+    return scale * (ds @ kh)
+
+
+def head_dkdv_cols(qh, kh, vh, doh, scale, causal, cols):
+    """This query head's share of dK, dV for selected key rows (columns of P):
+    needs LSE_i and D_i of every query row, then dK_j = alpha sum_i dS_ij q_i,
+    dV_j = sum_i P_ij dO_i."""
+    cols = np.asarray(cols)
+    sq = qh.shape[0]
+    o, lse = head_forward(qh, kh, vh, scale, causal)
+    dd = np.sum(doh * o, axis=1)
+    s = scale * (qh @ kh[cols].T)                          # [Sq, n]
+    p = np.exp(s - lse[:, None])
+    if causal:
+        p = np.where(cols[None, :] <= np.arange(sq)[:, None], p, 0.0)
+    ds = p * (doh @ vh[cols].T - dd[:, None])
+    return scale * (ds.T @ qh), p.T @ doh
+
+
 def _sequences(q, cu_q, cu_k, k):
     """Yield (seq index, q row slice, k row slice) for BSHD or THD inputs."""
     if cu_q is None:

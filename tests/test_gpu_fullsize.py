@@ -1,0 +1,159 @@
+"""Parity at the full sizes of the five workloads, in the launch configuration
+the benchmark times. The oracle computes sampled outputs one by one (query
+rows for O, LSE and dQ; key rows for dK, dV) on the exact bf16 values the GPU
+saw; identities that hold at any size (sum_j dV_j = sum_i dO_i per KV group,
+sum_j dK_j = 0) cover every output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_71_amd as ea
+import oracle
+from parity import GRAD_REL, check_lse, check_o, rel_l2, to64
+from workloads import WORKLOADS, draw_lengths, workload_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+DEV = "cuda:0"
+
+
+def _rows(n, extra=24, seed=0, blocks=(64, 128, 256)):
+    """Tile edges (first/last row of several block sizes) plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, n - 1, n - 2, n // 2}
+    for b in blocks:
+        for m in (1, 2, n // b - 1):
+            for r in (m * b - 1, m * b):
+                if 0 <= r < n:
+                    rows.add(r)
+    rows |= set(int(x) for x in rng.integers(0, n, extra))
+    return np.array(sorted(rows))
+
+
+def _h(x, b, h):
+    """CPU float64 [S, d] slice of a BSHD tensor."""
+    return to64(x[b, :, h])
+
+
+def _check_rows(o, lse, q, k, v, b, h, hk, scale, causal, rows, what):
+    qh, kh, vh = _h(q, b, h), _h(k, b, hk), _h(v, b, hk)
+    o_ref, lse_ref = oracle.head_forward(qh, kh, vh, scale, causal, rows=rows)
+    check_o(o[b, rows, h], o_ref, what)
+    check_lse(lse[b, h, rows], lse_ref, what)
+
+
+def _check_grads_sampled(dq, dk, dv, q, k, v, do, b, hk, group, scale, causal, rows, cols, what):
+    kh, vh = _h(k, b, hk), _h(v, b, hk)
+    dk_ref = np.zeros((cols.size, kh.shape[1]))
+    dv_ref = np.zeros_like(dk_ref)
+    for h in range(hk * group, (hk + 1) * group):
+        qh, doh = _h(q, b, h), _h(do, b, h)
+        dq_ref = oracle.head_dq_rows(qh, kh, vh, doh, scale, causal, rows)
+        assert rel_l2(dq[b, rows, h], dq_ref) <= GRAD_REL, (what, "dq", h)
+        a, c = oracle.head_dkdv_cols(qh, kh, vh, doh, scale, causal, cols)
+        dk_ref += a
+        dv_ref += c
+    assert rel_l2(dk[b, cols, hk], dk_ref) <= GRAD_REL, (what, "dk")
+    assert rel_l2(dv[b, cols, hk], dv_ref) <= GRAD_REL, (what, "dv")
+
+
+def _identities(dk, dv, do, group, what):
+    """sum over keys of dV = sum over queries and grouped heads of dO; sum of dK = 0."""
+    dvs = dv.double().sum(dim=1)                                   # [B, Hkv, d]
+    b, s, hq, d = do.shape
+    dos = do.double().reshape(b, s, hq // group, group, d).sum(dim=(1, 3))
+    assert (torch.linalg.norm(dvs - dos) / torch.linalg.norm(dos)).item() <= GRAD_REL, what
+    dks = dk.double().sum(dim=1)
+    assert (torch.linalg.norm(dks) / torch.linalg.norm(dk.double())).item() <= GRAD_REL, what
+
+
+def test_fwd4k_full_size():
+    w = WORKLOADS["fwd4k"]
+    inp = workload_inputs(w, device=DEV, with_grad=False)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = ea.fwd(q, k, v, causal=False, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    rows = _rows(w.seqlen, seed=2)
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        _check_rows(o, lse, q, k, v, b, h, h, w.scale, False, rows, f"fwd4k b{b} h{h}")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_causal8k_full_size_fwd_bwd():
+    w = WORKLOADS["causal8k"]
+    inp = workload_inputs(w, device=DEV)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    o, lse = ea.fwd(q, k, v, causal=True, softmax_scale=w.scale)
+    dq, dk, dv = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    rows = _rows(w.seqlen, seed=3)
+    cols = _rows(w.seqlen, extra=8, seed=4)
+    # heads 0..7 carry Q, K x3 (large max jumps, rescale path); 8..15 do not
+    for b, h in ((0, 0), (1, 3), (0, 12), (1, 15)):
+        _check_rows(o, lse, q, k, v, b, h, h, w.scale, True, rows, f"causal8k b{b} h{h}")
+    for b, h in ((0, 1), (1, 9)):
+        _check_grads_sampled(dq, dk, dv, q, k, v, do, b, h, 1, w.scale, True, rows, cols,
+                             f"causal8k bwd b{b} h{h}")
+    _identities(dk, dv, do, 1, "causal8k identities")
+
+
+def test_varlen_gqa_full_size_fwd_bwd():
+    w = WORKLOADS["varlen_gqa"]
+    lengths = draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number)
+    inp = workload_inputs(w, device=DEV)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    cu = inp["cu_seqlens_q"].to(DEV)
+    mx = max(lengths)
+    o, lse = ea.fwd_varlen(q, k, v, cu, cu, mx, mx, causal=True, softmax_scale=w.scale)
+    dq, dk, dv = ea.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, causal=True,
+                               softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    cuh = inp["cu_seqlens_q"].tolist()
+    group = w.heads_q // w.heads_kv
+    order = np.argsort(lengths)
+    for s in (int(order[-1]), int(order[0]), int(order[len(order) // 2])):
+        sl = slice(cuh[s], cuh[s + 1])
+        n = lengths[s]
+        qs, ks, vs, dos = (x[sl].unsqueeze(0) for x in (q, k, v, do))
+        rows = _rows(n, extra=12, seed=s)
+        lse_s = lse[:, sl].unsqueeze(0)
+        for h in (0, 13, 31):
+            _check_rows(o[sl].unsqueeze(0), lse_s, qs, ks, vs, 0, h, h // group, w.scale, True,
+                        rows, f"varlen seq{s} len{n} h{h}")
+        if s == int(order[0]):
+            cols = _rows(n, extra=8, seed=s + 100)
+            _check_grads_sampled(dq[sl].unsqueeze(0), dk[sl].unsqueeze(0), dv[sl].unsqueeze(0),
+                                 qs, ks, vs, dos, 0, 1, group, w.scale, True, rows, cols,
+                                 f"varlen bwd seq{s}")
+    # identities per sequence (every output row)
+    for s in range(w.num_seqs):
+        sl = slice(cuh[s], cuh[s + 1])
+        _identities(dk[sl].unsqueeze(0), dv[sl].unsqueeze(0), do[sl].unsqueeze(0), group,
+                    f"varlen identities seq{s}")
+
+
+@pytest.mark.parametrize("name", ["det16k_d64", "det16k_d128", "det16k_d256"])
+def test_det16k_full_size_bit_identical_and_parity(name):
+    w = WORKLOADS[name]
+    inp = workload_inputs(w, device=DEV)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    o, lse = ea.fwd(q, k, v, causal=True, softmax_scale=w.scale)
+    p = ea.make_params(1, w.seqlen, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, w.scale, True, True)
+    ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
+    runs = []
+    for _ in range(3):
+        runs.append(ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale,
+                           deterministic=True, workspace=ws))
+        torch.cuda.synchronize()
+        assert ea.bwd_status(p, ws) == 0
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b), name
+    dq, dk, dv = runs[0]
+    rows = _rows(w.seqlen, extra=16, seed=7)
+    cols = _rows(w.seqlen, extra=4, seed=8)
+    _check_rows(o, lse, q, k, v, 0, 5, 5, w.scale, True, rows, name)
+    _check_grads_sampled(dq, dk, dv, q, k, v, do, 0, 2, 1, w.scale, True, rows, cols, name)
+    _identities(dk, dv, do, 1, name)

@@ -109,3 +109,19 @@ def test_varlen_backward_equals_per_sequence():
                                       inp["do"][None, sl], scale, True)
         for a, b in zip((dq, dk, dv), g):
             np.testing.assert_array_equal(a[sl], b[0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_and_columns_match_full_backward(causal):
+    """The per-row dQ and per-column dK/dV helpers used on full-size outputs
+    agree with the full backward (itself pinned by finite differences)."""
+    inp = make_inputs(1, 90, 90, 1, 1, 16, seed=81)
+    q, k, v, do = (_f64(inp[n])[0, :, 0] for n in ("q", "k", "v", "do"))
+    dq, dk, dv = oracle.head_backward(q, k, v, do, 0.25, causal)
+    rows = np.array([0, 1, 45, 89])
+    np.testing.assert_allclose(oracle.head_dq_rows(q, k, v, do, 0.25, causal, rows), dq[rows],
+                               rtol=0, atol=1e-13)
+    cols = np.array([0, 30, 88, 89])
+    dkc, dvc = oracle.head_dkdv_cols(q, k, v, do, 0.25, causal, cols)
+    np.testing.assert_allclose(dkc, dk[cols], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dvc, dv[cols], rtol=0, atol=1e-13)
