@@ -26,6 +26,7 @@ struct Tuning {
   int tile_order = 0;
   int exp_emulation = 0;
   int spin_limit = 1 << 26;
+  int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
 };
 Tuning g_tuning;
 
@@ -81,6 +82,7 @@ FwdWs fwd_ws(const attn_params* p, bool varlen) {
 
 struct BwdWs {
   size_t dsum = 0, dq_acc = 0, sem = 0, misc = 0, order = 0, tile_prefix = 0, mb_prefix = 0;
+  size_t order_dq = 0, tile_prefix_dq = 0;
   size_t total = 0;
   int64_t n_sem = 0;
 };
@@ -102,6 +104,8 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
     w.order = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
     w.tile_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
     w.mb_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
+    w.order_dq = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
+    w.tile_prefix_dq = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
   }
   w.total = off;
   return w;
@@ -116,6 +120,11 @@ int section_width(int64_t bytes_per_bh) {
 
 int fwd_grid(const attn_params* p, bool varlen) {
   const int bm = fwd_block_m(p->head_dim);
+  if (varlen) return (cdiv(p->total_q, bm) + p->batch) * p->num_heads_q;
+  return p->batch * p->num_heads_q * cdiv(p->seqlen_q, bm);
+}
+int dq_grid(const attn_params* p, bool varlen) {
+  const int bm = dq_block_m(p->head_dim);
   if (varlen) return (cdiv(p->total_q, bm) + p->batch) * p->num_heads_q;
   return p->batch * p->num_heads_q * cdiv(p->seqlen_q, bm);
 }
@@ -215,7 +224,8 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   if (main && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
                !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_INVALID_ARGUMENT;
-  if (post && (!dq || !aligned16(dq))) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((post || (main && g_tuning.bwd_fused_dq == 0)) && (!dq || !aligned16(dq)))
+    return ATTN_ERR_INVALID_ARGUMENT;
   const BwdWs wl = bwd_ws(p, varlen);
   if (ws_bytes < wl.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!ws) return ATTN_ERR_INVALID_ARGUMENT;
@@ -247,12 +257,19 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.alpha = p->softmax_scale;
   bp.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   bp.rows_q = rows_q_of(p, varlen);
-  bp.n_sem = wl.n_sem;
+  const bool fused = g_tuning.bwd_fused_dq != 0;
+  bp.n_sem = fused ? wl.n_sem : 0;
+  bp.zero_acc = fused ? 1 : 0;
   bp.spin_limit = g_tuning.spin_limit;
+  const int bmq = dq_block_m(d);
+  bp.nm_dq = cdiv(p->seqlen_q, bmq);
+  bp.sec_dq = section_width(2ll * p->seqlen_k * d * 2);
   if (varlen) {
     bp.order = reinterpret_cast<int*>(base + wl.order);
     bp.tile_prefix = reinterpret_cast<int*>(base + wl.tile_prefix);
     bp.mb_prefix = reinterpret_cast<int*>(base + wl.mb_prefix);
+    bp.order_dq = reinterpret_cast<int*>(base + wl.order_dq);
+    bp.tile_prefix_dq = reinterpret_cast<int*>(base + wl.tile_prefix_dq);
   }
   if (pre) {
     if (varlen && launch_varlen_schedule(cu_q, cu_k, cu_q, p->batch, p->num_heads_kv, bn,
@@ -260,10 +277,18 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
                                          const_cast<int*>(bp.tile_prefix),
                                          const_cast<int*>(bp.mb_prefix), bm, stream) != hipSuccess)
       return ATTN_ERR_HIP;
+    if (varlen && !fused &&
+        launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bmq,
+                               const_cast<int*>(bp.order_dq), const_cast<int*>(bp.tile_prefix_dq),
+                               nullptr, 1, stream) != hipSuccess)
+      return ATTN_ERR_HIP;
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
-  if (main && launch_bwd_main(bp, d, bwd_grid(p, varlen), stream) != hipSuccess) return ATTN_ERR_HIP;
-  if (post && launch_bwd_post(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (main) {
+    if (launch_bwd_main(bp, d, bwd_grid(p, varlen), fused, stream) != hipSuccess) return ATTN_ERR_HIP;
+    if (!fused && launch_bwd_dq(bp, d, dq_grid(p, varlen), stream) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (post && fused && launch_bwd_post(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
@@ -345,15 +370,15 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* ws
 
 attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,
                             int64_t* count) {
-  if (!count || which < 0 || which > 2 || capacity < 0 || (capacity > 0 && !out))
+  if (!count || which < 0 || which > 3 || capacity < 0 || (capacity > 0 && !out))
     return ATTN_ERR_INVALID_ARGUMENT;
   attn_status st = check_params(p, false);
   if (st != ATTN_OK) return st;
   const int d = p->head_dim;
-  if (which == 0) {
-    const int nm = cdiv(p->seqlen_q, fwd_block_m(d));
+  if (which == 0 || which == 3) {
+    const int nm = cdiv(p->seqlen_q, which == 0 ? fwd_block_m(d) : dq_block_m(d));
     const int sec = section_width(2ll * p->seqlen_k * d * 2);
-    const int n = fwd_grid(p, false);
+    const int n = which == 0 ? fwd_grid(p, false) : dq_grid(p, false);
     *count = n;
     for (int i = 0; i < n && i < capacity; ++i) {
       const Tile t = fwd_tile_fixed(i, p->batch, p->num_heads_q, nm, sec, kNxcd,
@@ -383,6 +408,9 @@ attn_status attn_set_tuning(const char* key, int32_t value) {
   } else if (!std::strcmp(key, "exp_emulation")) {
     if (value != 0 && value != 2) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.exp_emulation = value;
+  } else if (!std::strcmp(key, "bwd_fused_dq")) {
+    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
+    g_tuning.bwd_fused_dq = value;
   } else if (!std::strcmp(key, "spin_limit")) {
     if (value < 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.spin_limit = value;

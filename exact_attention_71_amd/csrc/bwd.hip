@@ -80,9 +80,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t n_pai
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc += (float)a[j] * (float)b[j];
   }
-  float* z = p.dq_acc + base;
+  if (p.zero_acc) {
+    float* z = p.dq_acc + base;
 #pragma unroll
-  for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4*>(z + e) = f32x4{};
+    for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4*>(z + e) = f32x4{};
+  }
 #pragma unroll
   for (int s = L / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, kWave);
   if (sub == 0) {
@@ -132,7 +134,7 @@ struct alignas(16) BwdSmem {
   int ticket;
 };
 
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   constexpr int BN = BwdCfg<D>::BN;     // 128 keys, 32 per wave
   constexpr int BM = BwdCfg<D>::BM;     // queries per step
@@ -149,7 +151,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const bool det = p.deterministic != 0;
+  // Without the fused dQ there is no cross-workgroup reduction: every order
+  // gives the same bits, and the deterministic flag needs no ordering.
+  const bool det = FUSED && p.deterministic != 0;
   const bool causal = p.causal != 0;
 
   // ---- which key block (deterministic: ticket order = shortest first)
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       vf[kk] = buf_load16(vr, off + 32 * kk, 0);
     }
   }
-  {
+  if (FUSED) {
     constexpr int KU = (BN / 4) * CPR;
     for (int u = tid; u < KU; u += 256) {
       const int kg = u / CPR, dc = u % CPR;
@@ -350,6 +354,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
         }
       }
 
+    if (!FUSED) {
+      __syncthreads();          // every wave is done with this step's tiles
+      if (step + 1 < n_steps) {
+        store_step();
+        __syncthreads();
+      }
+      continue;
+    }
     // dS -> LDS as [query][key]
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
@@ -459,12 +471,15 @@ hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stream) {
+hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  switch (d) {
-    case 64: hipLaunchKernelGGL(bwd_main_kernel<64>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(bwd_main_kernel<128>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 256: hipLaunchKernelGGL(bwd_main_kernel<256>, dim3(grid), dim3(256), 0, stream, p); break;
+  switch (d * 2 + (fused ? 1 : 0)) {
+    case 128: hipLaunchKernelGGL((bwd_main_kernel<64, false>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 129: hipLaunchKernelGGL((bwd_main_kernel<64, true>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((bwd_main_kernel<128, false>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 257: hipLaunchKernelGGL((bwd_main_kernel<128, true>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 512: hipLaunchKernelGGL((bwd_main_kernel<256, false>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 513: hipLaunchKernelGGL((bwd_main_kernel<256, true>), dim3(grid), dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -63,6 +63,11 @@ struct BwdParams {
   int causal, deterministic;
   float alpha;
   float scale_log2;
+  const int* order_dq;    // varlen: dQ kernel schedule (by key length)
+  const int* tile_prefix_dq;
+  int nm_dq;              // fixed: query blocks of the dQ kernel per sequence
+  int sec_dq;
+  int zero_acc;           // preprocess clears the fp32 dQ accumulator (fused path)
   int64_t rows_q;         // total query rows (B*Sq or total_q)
   int64_t n_sem;          // semaphore words to clear (deterministic)
   int spin_limit;         // bounded wait for the deterministic chain
@@ -89,6 +94,13 @@ template <int D> struct BwdCfg {
   static constexpr int BM = (D <= 128) ? 64 : 32; // queries per inner step
 };
 
+template <int D> struct DqCfg {
+  static constexpr int NW = (D <= 128) ? 8 : 4;   // wavefronts, 32 query rows each
+  static constexpr int BM = NW * 32;
+  static constexpr int BN = (D <= 128) ? 64 : 32; // keys per tile
+};
+inline int dq_block_m(int d) { return d <= 128 ? DqCfg<128>::BM : DqCfg<256>::BM; }
+
 inline int fwd_block_m(int d) {
   return d == 64 ? FwdCfg<64>::BM : d == 128 ? FwdCfg<128>::BM : FwdCfg<256>::BM;
 }
@@ -97,7 +109,11 @@ inline int bwd_block_m(int d) { return d <= 128 ? 64 : 32; }
 
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stream);
+// fused = true: dQ accumulated with fp32 atomics (or the deterministic
+// semaphore chain) inside the dK/dV kernel; false: dK/dV only.
+hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream);
+// dQ without atomics: one workgroup per query block (see bwd_dq.hip).
+hipError_t launch_bwd_dq(const BwdParams& p, int d, int grid, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
 // Varlen pre-pass: order[] = sequences by decreasing length of key_cu (ties
 // by index), tile_prefix[vs] = first tile of virtual sequence vs with

@@ -109,8 +109,15 @@ attn_status attn_fwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
                             size_t workspace_bytes, hipStream_t stream);
 
 /* Backward, fixed length: dq, dk, dv from q, k, v, the forward's o and lse
- * (required) and dout. Three launches on `stream`: preprocess (D, clears),
- * main (dK, dV, dQ accumulation), postprocess (dQ to bf16). */
+ * (required) and dout. Launches on `stream`: preprocess (D = rowsum(dO o O));
+ * main; postprocess. Two designs, chosen by attn_set_tuning("bwd_fused_dq"):
+ *   0 (default) main = a dK/dV kernel (one workgroup per key block, four
+ *     GEMMs) plus a dQ kernel (one workgroup per query block, S and dP
+ *     recomputed): no atomics, bit-reproducible whatever `deterministic` says;
+ *   1 main = one kernel that also adds each tile's dQ into an fp32 buffer with
+ *     atomics (blog page, 2-CTA backward, dQ atomic accumulation), or, with
+ *     deterministic = 1, in a fixed order behind per-block semaphores (blog
+ *     page, deterministic mode); postprocess converts dQ to bf16. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -131,9 +138,9 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  * accumulator and, in deterministic mode, the ordering state. A MAIN phase
  * run without it still terminates and stays in bounds, but dQ accumulates on
  * the previous values and the deterministic order is not guaranteed. */
-#define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); clear dQ accumulator, semaphores */
-#define ATTN_BWD_MAIN 2        /* dK, dV; dQ accumulation (reads D, LSE) */
-#define ATTN_BWD_POSTPROCESS 4 /* dQ = bf16(alpha * accumulator) */
+#define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); fused design: clear dQ accumulator, semaphores */
+#define ATTN_BWD_MAIN 2        /* dK, dV and dQ (reads D, LSE) */
+#define ATTN_BWD_POSTPROCESS 4 /* fused design: dQ = bf16(alpha * accumulator); else nothing */
 attn_status attn_bwd_phases(const attn_params* p, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_k, int32_t phases, const void* q,
                             const void* k, const void* v, const void* o, const void* dout,
@@ -151,14 +158,17 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* wo
  * same arithmetic the kernels use (scheduling section of the blog page:
  * longest first, L2-sized batch-head sections; here also one contiguous range
  * per XCD). which = 0: forward, out[3*i..3*i+2] = (batch, query head,
- * query block) of workgroup i; which = 1: non-deterministic backward,
- * which = 2: deterministic backward in ticket order, (batch, KV head, key
- * block). *count receives the grid size; at most `capacity` triples are
- * written. No GPU is needed. */
+ * query block) of workgroup i; which = 1: dK/dV (or fused) backward,
+ * which = 2: fused deterministic backward in ticket order, (batch, KV head,
+ * key block); which = 3: dQ kernel, (batch, query head, query block).
+ * *count receives the grid size; at most `capacity` triples are written.
+ * No GPU is needed. */
 attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,
                             int64_t* count);
 
 /* Process-wide tuning knobs (not synchronised with launches in flight):
+ *   "bwd_fused_dq"  0 = dK/dV kernel + dQ kernel (default), 1 = one kernel with
+ *                   dQ atomics / semaphore-ordered adds (see attn_bwd);
  *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
  *                   (batch-head major, blocks ascending, no remap);
  *   "exp_emulation" 0 = every exp2 on v_exp_f32 (default), 2 = 2 of every 8

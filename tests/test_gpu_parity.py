@@ -19,6 +19,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
+@pytest.fixture(params=[0, 1], ids=["split_dq", "fused_dq"])
+def bwd_mode(request):
+    """Run a backward test with the separate dQ kernel and with fused atomics."""
+    ea.set_tuning("bwd_fused_dq", request.param)
+    yield request.param
+    ea.set_tuning("bwd_fused_dq", 0)
+
+
 def _dev(inp):
     return {k: v.to(DEV) for k, v in inp.items()}
 
@@ -43,7 +51,7 @@ def _run_fixed(b, s, hq, hkv, d, causal, seed, scaled=False, det=False, sk=None,
     check_grads((dq, dk, dv), ref, what)
 
 
-def test_small_workload_fwd_bwd():
+def test_small_workload_fwd_bwd(bwd_mode):
     w = WORKLOADS["small"]
     inp = workload_inputs(w)
     g = _dev(inp)
@@ -61,12 +69,12 @@ def test_small_workload_fwd_bwd():
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ragged_lengths(d, causal):
+def test_ragged_lengths(d, causal, bwd_mode):
     _run_fixed(1, 300, 2, 2, d, causal, seed=100 + d)
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (4, 1), (6, 3)])
-def test_grouped_heads(hq, hkv):
+def test_grouped_heads(hq, hkv, bwd_mode):
     _run_fixed(2, 200, hq, hkv, 128, True, seed=7 + hq + hkv)
 
 
@@ -91,7 +99,7 @@ def test_lse_is_optional_and_output_unchanged():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_matches_oracle(causal):
+def test_varlen_matches_oracle(causal, bwd_mode):
     lengths = [1, 17, 300, 0, 513, 64, 129]
     hq, hkv, d = 4, 2, 128
     inp = make_inputs(0, 0, 0, hq, hkv, d, seed=41, lengths=lengths)
@@ -112,7 +120,7 @@ def test_varlen_matches_oracle(causal):
     check_grads((dq, dk, dv), ref, "varlen")
 
 
-def test_varlen_non_causal_different_key_lengths():
+def test_varlen_non_causal_different_key_lengths(bwd_mode):
     lq, lk = [40, 300, 7], [260, 0, 90]
     hq, hkv, d = 2, 1, 64
     inp = make_inputs(0, 0, 0, hq, hkv, d, seed=43, lengths=lq, lengths_k=lk)
@@ -134,7 +142,7 @@ def test_varlen_non_causal_different_key_lengths():
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-def test_deterministic_backward_is_bit_identical(d):
+def test_deterministic_backward_is_bit_identical(d, bwd_mode):
     s, hq, hkv = 640, 4, 2
     inp = make_inputs(1, s, s, hq, hkv, d, seed=51 + d)
     g = _dev(inp)
@@ -155,7 +163,7 @@ def test_deterministic_backward_is_bit_identical(d):
     check_grads(runs[0], ref, f"det d{d}")
 
 
-def test_backward_phases_equal_full_backward():
+def test_backward_phases_equal_full_backward(bwd_mode):
     s, hq, hkv, d = 384, 2, 2, 128
     inp = make_inputs(1, s, s, hq, hkv, d, seed=61)
     g = _dev(inp)
@@ -220,6 +228,7 @@ def test_deterministic_main_without_preprocess_stays_in_bounds():
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
     p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True)
     ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
+    ea.set_tuning("bwd_fused_dq", 1)       # the ticket / semaphore path
     first = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
                    workspace=ws)
     dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
@@ -234,6 +243,7 @@ def test_deterministic_main_without_preprocess_stays_in_bounds():
     again = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
                    workspace=ws)
     torch.cuda.synchronize()
+    ea.set_tuning("bwd_fused_dq", 0)
     assert ea.bwd_status(p, ws) == 0
     for a, b in zip(first, again):
         assert torch.equal(a, b)
