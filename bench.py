@@ -118,6 +118,8 @@ def main() -> int:
     ap.add_argument("--workload", default="causal8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--bwd-fused-dq", action="store_true",
+                    help="time the fused backward (dQ atomics) instead of dK/dV + dQ kernels")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a known-size kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -195,24 +197,31 @@ def main() -> int:
         return torch.cuda.current_stream().cuda_stream
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    dom_start, dom_end = [], []
+    # per-kernel HIP events on the launch stream: name -> list of (start, end)
+    marks = {}
 
-    def step(timed: bool):
-        if not with_bwd:
-            if timed:
-                dom_start.append(ev()); dom_start[-1].record()
-            run_fwd()
-            if timed:
-                dom_end.append(ev()); dom_end[-1].record()
+    def timed(name, fn, on):
+        if not on:
+            fn()
             return
-        run_fwd()
-        run_bwd_phase(ea.BWD_PREPROCESS)
-        if timed:
-            dom_start.append(ev()); dom_start[-1].record()
-        run_bwd_phase(ea.BWD_MAIN)
-        if timed:
-            dom_end.append(ev()); dom_end[-1].record()
-        run_bwd_phase(ea.BWD_POSTPROCESS)
+        a, b = ev(), ev()
+        a.record()
+        fn()
+        b.record()
+        marks.setdefault(name, []).append((a, b))
+
+    if args.bwd_fused_dq:
+        ea.set_tuning("bwd_fused_dq", 1)
+    fused = ea.get_tuning("bwd_fused_dq")
+
+    def step(on: bool):
+        timed("fwd", run_fwd, on)
+        if not with_bwd:
+            return
+        timed("bwd_pre", lambda: run_bwd_phase(ea.BWD_PREPROCESS), on)
+        timed("bwd_main", lambda: run_bwd_phase(ea.BWD_MAIN), on)
+        timed("bwd_dq", lambda: run_bwd_phase(ea.BWD_DQ), on)
+        timed("bwd_post", lambda: run_bwd_phase(ea.BWD_POSTPROCESS), on)
 
     for _ in range(args.warmup):
         step(False)
@@ -226,26 +235,29 @@ def main() -> int:
     t_end.record()
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in zip(dom_start, dom_end)) / len(dom_start)
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step, dominant kernel {dom_ms:.3f} ms",
-          file=sys.stderr, flush=True)
+    kms = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in marks.items()}
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step; per kernel (ms): "
+          + ", ".join(f"{n} {t:.3f}" for n, t in kms.items()), file=sys.stderr, flush=True)
     if with_bwd and w.deterministic:
         assert ea.bwd_status(p, bws, varlen) == 0
 
-    # separate forward-only timing for the breakdown (not part of `value`)
-    f0, f1 = ev(), ev()
-    f0.record()
-    for _ in range(args.steps):
-        run_fwd()
-    f1.record()
-    torch.cuda.synchronize()
-    fwd_ms = f0.elapsed_time(f1) / args.steps
-
     total_flops = fl["fwd+bwd"] if with_bwd else fl["fwd"]
-    dom_name = f"bwd_main_kernel<{w.head_dim}>" if with_bwd else f"fwd_kernel<{w.head_dim}>"
     value = total_flops / (ms * 1e-3) / 1e12
-    dom_flops = fl["bwd"] if with_bwd else fl["fwd"]
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    # algorithmic flops per kernel: forward 2 GEMMs; the key-block backward kernel
+    # S, dP, dV, dK (4 of the 5 backward GEMMs; all 5 when dQ is fused); the dQ
+    # kernel only dQ (its recomputed S and dP are not algorithmic work)
+    half = fl["fwd"] / 2.0
+    kflops = {"fwd": fl["fwd"], "bwd_main": (5 if fused else 4) * half,
+              "bwd_dq": 1 * half}
+    names = {"fwd": f"fwd_kernel<{w.head_dim}>", "bwd_main": f"bwd_main_kernel<{w.head_dim}>",
+             "bwd_dq": f"bwd_dq_kernel<{w.head_dim}>"}
+    dom = max((n for n in kms if n in kflops), key=lambda n: kms[n])
+    dom_ms = kms[dom]
+    dom_name = names[dom]
+    achieved = kflops[dom] / (dom_ms * 1e-3) / 1e12
+    kernels = {names[n]: {"ms": round(kms[n], 4),
+                          "tflops": round(kflops[n] / (kms[n] * 1e-3) / 1e12, 1)}
+               for n in kms if n in kflops and kms[n] > 0.002}
     out = {
         "metric": "attention fwd/bwd TFLOPs/s at hdim128 bf16; % of MI355X BF16 MFMA peak",
         "value": round(value, 2),
@@ -260,8 +272,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
         "config": {"workload": _describe(w), "pass": w.passes,
-                   "fwd_tflops": round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12, 2),
-                   "fwd_ms": round(fwd_ms, 4),
+                   "bwd_design": "fused dQ atomics" if fused else "dK/dV kernel + dQ kernel",
+                   "kernels": kernels,
                    "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": dom_name,
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

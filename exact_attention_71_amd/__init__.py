@@ -13,7 +13,8 @@ Entry points mirror the C ABI in ``include/attn71.h``:
     bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
     bwd_phases(...)          the backward split into preprocess / main / postprocess
     tile_order(...)          the fixed-length tile schedule, evaluated on the host
-    set_tuning(key, value)   process-wide knobs ("tile_order", "exp_emulation", "spin_limit")
+    set_tuning(key, value)   process-wide knobs ("tile_order", "exp_emulation", "spin_limit",
+                             "bwd_fused_dq"); get_tuning(key) reads back what was set
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn71.so")
 
 ATTN_OK = 0
-BWD_PREPROCESS, BWD_MAIN, BWD_POSTPROCESS = 1, 2, 4
+BWD_PREPROCESS, BWD_MAIN, BWD_POSTPROCESS, BWD_DQ, BWD_ALL = 1, 2, 4, 8, 15
 
 
 class AttnError(RuntimeError):
@@ -247,8 +248,18 @@ def tile_order(p: AttnParams, which: int):
     return [tuple(buf[3 * i:3 * i + 3]) for i in range(count.value)]
 
 
+_TUNING = {"tile_order": 0, "exp_emulation": 0, "spin_limit": 1 << 26, "bwd_fused_dq": 0,
+           "fwd_pingpong": 0}
+
+
 def set_tuning(key: str, value: int) -> None:
     _check(_lib().attn_set_tuning(key.encode(), int(value)), "attn_set_tuning")
+    _TUNING[key] = int(value)
+
+
+def get_tuning(key: str) -> int:
+    """Value last set through set_tuning (the library's default otherwise)."""
+    return _TUNING[key]
 
 
 def version() -> int:

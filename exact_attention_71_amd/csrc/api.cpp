@@ -27,6 +27,7 @@ struct Tuning {
   int exp_emulation = 0;
   int spin_limit = 1 << 26;
   int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
+  int fwd_pingpong = 0;   // 1: phase-offset wave groups (d <= 128); 0: one phase per tile
 };
 Tuning g_tuning;
 
@@ -128,8 +129,8 @@ int dq_grid(const attn_params* p, bool varlen) {
   if (varlen) return (cdiv(p->total_q, bm) + p->batch) * p->num_heads_q;
   return p->batch * p->num_heads_q * cdiv(p->seqlen_q, bm);
 }
-int bwd_grid(const attn_params* p, bool varlen) {
-  const int bn = bwd_block_n(p->head_dim);
+int bwd_grid(const attn_params* p, bool varlen, bool fused) {
+  const int bn = fused ? bwd_block_n(p->head_dim) : dkdv_block_n(p->head_dim);
   if (varlen) return (cdiv(p->total_k, bn) + p->batch) * p->num_heads_kv;
   return p->batch * p->num_heads_kv * cdiv(p->seqlen_k, bn);
 }
@@ -203,7 +204,8 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     fp.order = order;
     fp.tile_prefix = tp;
   }
-  if (launch_fwd(fp, d, fwd_grid(p, varlen), g_tuning.exp_emulation, stream) != hipSuccess)
+  if (launch_fwd(fp, d, fwd_grid(p, varlen), g_tuning.exp_emulation, g_tuning.fwd_pingpong != 0,
+                 stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -216,16 +218,18 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   attn_status st = check_params(p, varlen);
   if (st != ATTN_OK) return st;
   if (varlen && !cu_k) return ATTN_ERR_INVALID_ARGUMENT;
-  if (phases <= 0 || phases > 7) return ATTN_ERR_INVALID_ARGUMENT;
+  if (phases <= 0 || phases > ATTN_BWD_ALL) return ATTN_ERR_INVALID_ARGUMENT;
+  const bool fused_mode = g_tuning.bwd_fused_dq != 0;
   const bool pre = phases & ATTN_BWD_PREPROCESS, main = phases & ATTN_BWD_MAIN,
-             post = phases & ATTN_BWD_POSTPROCESS;
+             post = (phases & ATTN_BWD_POSTPROCESS) && fused_mode,
+             dqk = (phases & ATTN_BWD_DQ) && !fused_mode;
   if (pre && (!o || !dout || !aligned16(o) || !aligned16(dout))) return ATTN_ERR_INVALID_ARGUMENT;
-  if (main && (!q || !k || !v || !dout || !lse || !dk || !dv)) return ATTN_ERR_INVALID_ARGUMENT;
-  if (main && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
-               !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u)))
+  if ((main || dqk) && (!q || !k || !v || !dout || !lse)) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((main || dqk) && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+                        (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_INVALID_ARGUMENT;
-  if ((post || (main && g_tuning.bwd_fused_dq == 0)) && (!dq || !aligned16(dq)))
-    return ATTN_ERR_INVALID_ARGUMENT;
+  if (main && (!dk || !dv || !aligned16(dk) || !aligned16(dv))) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((post || dqk) && (!dq || !aligned16(dq))) return ATTN_ERR_INVALID_ARGUMENT;
   const BwdWs wl = bwd_ws(p, varlen);
   if (ws_bytes < wl.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!ws) return ATTN_ERR_INVALID_ARGUMENT;
@@ -246,7 +250,8 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.status = reinterpret_cast<int*>(base + wl.misc + 4);
   bp.sv = make_sv(p, cu_q, cu_k);
   bp.hq = p->num_heads_q; bp.hkv = p->num_heads_kv; bp.group = p->num_heads_q / p->num_heads_kv;
-  const int bn = bwd_block_n(d), bm = bwd_block_m(d);
+  const bool fused = g_tuning.bwd_fused_dq != 0;
+  const int bn = fused ? bwd_block_n(d) : dkdv_block_n(d), bm = bwd_block_m(d);
   bp.nn = cdiv(p->seqlen_k, bn);
   bp.nm = cdiv(p->seqlen_q, bm);
   bp.sec = section_width(2ll * bp.group * p->seqlen_q * d * 2);
@@ -257,7 +262,6 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.alpha = p->softmax_scale;
   bp.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   bp.rows_q = rows_q_of(p, varlen);
-  const bool fused = g_tuning.bwd_fused_dq != 0;
   bp.n_sem = fused ? wl.n_sem : 0;
   bp.zero_acc = fused ? 1 : 0;
   bp.spin_limit = g_tuning.spin_limit;
@@ -285,10 +289,12 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (main) {
-    if (launch_bwd_main(bp, d, bwd_grid(p, varlen), fused, stream) != hipSuccess) return ATTN_ERR_HIP;
-    if (!fused && launch_bwd_dq(bp, d, dq_grid(p, varlen), stream) != hipSuccess) return ATTN_ERR_HIP;
+    const hipError_t e = fused ? launch_bwd_main(bp, d, bwd_grid(p, varlen, true), true, stream)
+                               : launch_bwd_dkdv(bp, d, bwd_grid(p, varlen, false), stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
   }
-  if (post && fused && launch_bwd_post(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (dqk && launch_bwd_dq(bp, d, dq_grid(p, varlen), stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (post && launch_bwd_post(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
@@ -334,7 +340,8 @@ attn_status attn_fwd_varlen(const attn_params* p, const int32_t* cu_q, const int
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return bwd_impl(p, nullptr, nullptr, 7, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, stream);
+  return bwd_impl(p, nullptr, nullptr, ATTN_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, ws,
+                  ws_bytes, stream);
 }
 
 attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
@@ -342,7 +349,8 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_q, const int
                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!cu_q || !cu_k) return ATTN_ERR_INVALID_ARGUMENT;
-  return bwd_impl(p, cu_q, cu_k, 7, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, stream);
+  return bwd_impl(p, cu_q, cu_k, ATTN_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes,
+                  stream);
 }
 
 attn_status attn_bwd_phases(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
@@ -386,10 +394,11 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
       out[3 * i] = t.seq; out[3 * i + 1] = t.head; out[3 * i + 2] = t.block;
     }
   } else {
-    const int nn = cdiv(p->seqlen_k, bwd_block_n(d));
+    const bool fz = which == 2;   // 1: dK/dV kernel; 2: fused deterministic (ticket order)
+    const int nn = cdiv(p->seqlen_k, fz ? bwd_block_n(d) : dkdv_block_n(d));
     const int grp = p->num_heads_q / p->num_heads_kv;
     const int sec = section_width(2ll * grp * p->seqlen_q * d * 2);
-    const int n = bwd_grid(p, false);
+    const int n = bwd_grid(p, false, fz);
     *count = n;
     for (int i = 0; i < n && i < capacity; ++i) {
       const Tile t = bwd_tile_fixed(i, p->batch, p->num_heads_kv, nn, sec, which == 2, kNxcd,
@@ -408,6 +417,9 @@ attn_status attn_set_tuning(const char* key, int32_t value) {
   } else if (!std::strcmp(key, "exp_emulation")) {
     if (value != 0 && value != 2) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.exp_emulation = value;
+  } else if (!std::strcmp(key, "fwd_pingpong")) {
+    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
+    g_tuning.fwd_pingpong = value;
   } else if (!std::strcmp(key, "bwd_fused_dq")) {
     if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.bwd_fused_dq = value;

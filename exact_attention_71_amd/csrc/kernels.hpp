@@ -101,17 +101,27 @@ template <int D> struct DqCfg {
 };
 inline int dq_block_m(int d) { return d <= 128 ? DqCfg<128>::BM : DqCfg<256>::BM; }
 
+template <int D> struct DkdvCfg {
+  static constexpr int NW = (D <= 128) ? 8 : 4;   // wavefronts, 32 keys each
+  static constexpr int BN = NW * 32;              // keys per workgroup
+  static constexpr int BM = (D == 64) ? 64 : 32;  // queries per step
+};
+inline int dkdv_block_n(int d) { return d <= 128 ? DkdvCfg<128>::BN : DkdvCfg<256>::BN; }
+
 inline int fwd_block_m(int d) {
   return d == 64 ? FwdCfg<64>::BM : d == 128 ? FwdCfg<128>::BM : FwdCfg<256>::BM;
 }
 inline int bwd_block_n(int) { return 128; }
 inline int bwd_block_m(int d) { return d <= 128 ? 64 : 32; }
 
-hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, bool pingpong,
+                      hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 // fused = true: dQ accumulated with fp32 atomics (or the deterministic
 // semaphore chain) inside the dK/dV kernel; false: dK/dV only.
 hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream);
+// dK, dV only: one workgroup per DkdvCfg<d>::BN keys (see bwd_dkdv.hip).
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int grid, hipStream_t stream);
 // dQ without atomics: one workgroup per query block (see bwd_dq.hip).
 hipError_t launch_bwd_dq(const BwdParams& p, int d, int grid, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);

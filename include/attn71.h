@@ -130,8 +130,10 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
                             size_t workspace_bytes, hipStream_t stream);
 
 /* The backward split into its phases, for callers that schedule or time them
- * separately. `phases` is a mask of ATTN_BWD_*; running the three masks in
- * order on one stream with the same workspace equals attn_bwd(_varlen).
+ * separately. `phases` is a mask of ATTN_BWD_*; running the masks in the
+ * order PREPROCESS, MAIN, DQ, POSTPROCESS on one stream with the same
+ * workspace equals attn_bwd(_varlen) (MAIN and DQ are independent of each
+ * other and may also run in either order).
  * cu_seqlens_q/k NULL = fixed length. Arguments a phase does not read may
  * be NULL only if no selected phase reads them. Every MAIN phase needs a
  * PREPROCESS phase of the same workspace before it: it clears the dQ
@@ -139,8 +141,10 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  * run without it still terminates and stays in bounds, but dQ accumulates on
  * the previous values and the deterministic order is not guaranteed. */
 #define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); fused design: clear dQ accumulator, semaphores */
-#define ATTN_BWD_MAIN 2        /* dK, dV and dQ (reads D, LSE) */
+#define ATTN_BWD_MAIN 2        /* key-block kernel: dK, dV (fused design: + dQ accumulation) */
 #define ATTN_BWD_POSTPROCESS 4 /* fused design: dQ = bf16(alpha * accumulator); else nothing */
+#define ATTN_BWD_DQ 8          /* split design: the query-block dQ kernel; else nothing */
+#define ATTN_BWD_ALL 15
 attn_status attn_bwd_phases(const attn_params* p, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_k, int32_t phases, const void* q,
                             const void* k, const void* v, const void* o, const void* dout,
@@ -169,6 +173,9 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
 /* Process-wide tuning knobs (not synchronised with launches in flight):
  *   "bwd_fused_dq"  0 = dK/dV kernel + dQ kernel (default), 1 = one kernel with
  *                   dQ atomics / semaphore-ordered adds (see attn_bwd);
+ *   "fwd_pingpong"  1 = forward with two wave groups offset by one phase so
+ *                   MFMA and softmax overlap (head_dim <= 128; measured slower on
+ *                   MI355X so far), 0 = one phase per key tile (default);
  *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
  *                   (batch-head major, blocks ascending, no remap);
  *   "exp_emulation" 0 = every exp2 on v_exp_f32 (default), 2 = 2 of every 8

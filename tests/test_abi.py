@@ -89,7 +89,9 @@ def test_backward_requires_lse_and_workspace():
     assert lib.attn_bwd(ctypes.byref(p), *([FAKE] * 9), None, need, None) == INVALID
     assert lib.attn_bwd_phases(ctypes.byref(p), None, None, 0, *([FAKE] * 9), FAKE, need,
                                None) == INVALID
-    assert lib.attn_bwd_phases(ctypes.byref(p), FAKE, None, 7, *([FAKE] * 9), FAKE, need,
+    assert lib.attn_bwd_phases(ctypes.byref(p), FAKE, None, 15, *([FAKE] * 9), FAKE, need,
+                               None) == INVALID
+    assert lib.attn_bwd_phases(ctypes.byref(p), None, None, 16, *([FAKE] * 9), FAKE, need,
                                None) == INVALID
 
 
@@ -155,10 +157,12 @@ def test_forward_tile_order_is_a_permutation_longest_first(b, s, hq, hkv, d, cau
                                          (1, 3000, 8, 2, 64)])
 def test_backward_tile_orders(b, s, hq, hkv, d):
     p = _p(batch=b, seqlen_q=s, seqlen_k=s, heads_q=hq, heads_kv=hkv, head_dim=d, causal=True)
+    nn_dkdv = -(-s // (256 if d <= 128 else 128))
+    lpt = ea.tile_order(p, 1)
+    assert sorted(lpt) == sorted((bb, h, n) for bb in range(b) for h in range(hkv)
+                                 for n in range(nn_dkdv))
     nn = -(-s // 128)
     full = sorted((bb, h, n) for bb in range(b) for h in range(hkv) for n in range(nn))
-    lpt = ea.tile_order(p, 1)
-    assert sorted(lpt) == full
     det = ea.tile_order(p, 2)
     assert sorted(det) == full
     # deterministic order: for each (batch, KV head) key blocks strictly descending, so every

@@ -19,11 +19,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(params=[0, 1], ids=["split_dq", "fused_dq"])
+@pytest.fixture(params=[(1, 0), (0, 0), (1, 1)],
+                ids=["pingpong-splitdq", "plainfwd-splitdq", "pingpong-fuseddq"])
 def bwd_mode(request):
-    """Run a backward test with the separate dQ kernel and with fused atomics."""
-    ea.set_tuning("bwd_fused_dq", request.param)
+    """Kernel designs under test: forward ping-pong on/off, backward with the
+    separate dQ kernel or with fused dQ atomics."""
+    pp, fused = request.param
+    ea.set_tuning("fwd_pingpong", pp)
+    ea.set_tuning("bwd_fused_dq", fused)
     yield request.param
+    ea.set_tuning("fwd_pingpong", 0)
     ea.set_tuning("bwd_fused_dq", 0)
 
 
@@ -82,7 +87,7 @@ def test_non_causal_unequal_lengths():
     _run_fixed(2, 130, 2, 1, 64, False, seed=3, sk=333)
 
 
-def test_scaled_heads_exercise_rescale():
+def test_scaled_heads_exercise_rescale(bwd_mode):
     """Q, K x3 on half the heads: logit std ~9, max jumps above tau occur."""
     _run_fixed(1, 1024, 4, 4, 128, True, seed=31, scaled=True)
     _run_fixed(1, 700, 2, 2, 64, False, seed=32, scaled=True)
@@ -172,14 +177,14 @@ def test_backward_phases_equal_full_backward(bwd_mode):
     ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
     full = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True)
     dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
-    for ph in (ea.BWD_PREPROCESS, ea.BWD_MAIN, ea.BWD_POSTPROCESS):
+    for ph in (ea.BWD_PREPROCESS, ea.BWD_MAIN, ea.BWD_DQ, ea.BWD_POSTPROCESS):
         ea.bwd_phases(p, ph, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
     torch.cuda.synchronize()
     for a, b in zip(full, (dq, dk, dv)):
         assert torch.equal(a, b)
 
 
-def test_forward_independent_of_tile_order():
+def test_forward_independent_of_tile_order(bwd_mode):
     """No cross-tile reduction in the forward: any tile order gives the same bits."""
     inp = make_inputs(2, 1024, 1024, 8, 8, 128, seed=71, with_grad=False)
     g = _dev(inp)
@@ -193,7 +198,7 @@ def test_forward_independent_of_tile_order():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_exp_emulation_variant_matches_oracle():
+def test_exp_emulation_variant_matches_oracle(bwd_mode):
     inp = make_inputs(1, 512, 512, 2, 2, 128, seed=81, scaled_heads=True, with_grad=False)
     g = _dev(inp)
     ea.set_tuning("exp_emulation", 2)
@@ -234,7 +239,7 @@ def test_deterministic_main_without_preprocess_stays_in_bounds():
     dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
     ea.set_tuning("spin_limit", 1 << 14)
     try:
-        ea.bwd_phases(p, ea.BWD_PREPROCESS | ea.BWD_MAIN, g["q"], g["k"], g["v"], o, g["do"], lse,
+        ea.bwd_phases(p, ea.BWD_PREPROCESS | ea.BWD_MAIN | ea.BWD_POSTPROCESS, g["q"], g["k"], g["v"], o, g["do"], lse,
                       dq, dk, dv, ws)
         ea.bwd_phases(p, ea.BWD_MAIN, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
         torch.cuda.synchronize()
