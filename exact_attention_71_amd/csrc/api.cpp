@@ -82,7 +82,7 @@ FwdWs fwd_ws(const attn_params* p, bool varlen) {
 }
 
 struct BwdWs {
-  size_t dsum = 0, dq_acc = 0, sem = 0, misc = 0, order = 0, tile_prefix = 0, mb_prefix = 0;
+  size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, order = 0, tile_prefix = 0, mb_prefix = 0;
   size_t order_dq = 0, tile_prefix_dq = 0;
   size_t total = 0;
   int64_t n_sem = 0;
@@ -97,6 +97,7 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
   const int64_t rq = rows_q_of(p, varlen);
   size_t off = 0;
   w.dsum = off; off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q));
+  w.lse2 = off; off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q));
   w.dq_acc = off; off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q * p->head_dim));
   w.n_sem = p->deterministic ? bwd_mblocks(p, varlen) * p->num_heads_q : 0;
   w.sem = off; off = align_up(off + sizeof(int) * (size_t)w.n_sem);
@@ -244,6 +245,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.dout = dout; bp.lse = lse;
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.dsum = reinterpret_cast<float*>(base + wl.dsum);
+  bp.lse2 = reinterpret_cast<float*>(base + wl.lse2);
   bp.dq_acc = reinterpret_cast<float*>(base + wl.dq_acc);
   bp.sem = reinterpret_cast<int*>(base + wl.sem);
   bp.ticket = reinterpret_cast<int*>(base + wl.misc);

@@ -12,8 +12,8 @@
 // first in that mode, so the chain rarely waits.
 //
 // Kernels:
-//   bwd_pre   D = rowsum(dO o O) (fp32), zero the dQ accumulator and the
-//             semaphores / ticket / status words;
+//   bwd_pre   D = rowsum(dO o O) and LSE * log2(e) (fp32), zero the dQ
+//             accumulator and the semaphores / ticket / status words;
 //   bwd_main  per (sequence, KV head, 128-key block): dK, dV in registers,
 //             dQ atomics; all query heads of the KV group are walked here so
 //             dK, dV need no cross-workgroup reduction;
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t n_pai
       off = (b * p.hq + h) * p.sv.seqlen_q + s;
     }
     p.dsum[off] = acc;
+    p.lse2[off] = p.lse[off] * 1.4426950408889634f;
   }
 }
 
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   __shared__ SM sm;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   // Without the fused dQ there is no cross-workgroup reduction: every order
   // gives the same bits, and the deterministic flag needs no ordering.
   const bool det = FUSED && p.deterministic != 0;

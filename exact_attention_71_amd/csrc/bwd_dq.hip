@@ -74,7 +74,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int qw0 = m0 + w * 32;
   const int myq = qw0 + c;
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
@@ -189,11 +190,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -lse2));
-          if (need_mask) {
+          float x = __builtin_fmaf(s[kb][i], sl2, -lse2);
+          if (need_mask) {   // select on the exponent: 2^-inf = 0, no per-lane branch
             const int key = k0 + kb * 32 + c_row(i, g);
-            if (key >= lk || (causal && key > myq)) pv = 0.0f;
+            const bool hide = (key >= lk) | (causal & (key > myq));
+            x = hide ? neg_inf() : x;
           }
+          const float pv = fast_exp2(x);
           dp[kb][i] = pv * (dp[kb][i] - dsum);
         }
       // dQ^T += K^T dS^T

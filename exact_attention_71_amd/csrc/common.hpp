@@ -33,6 +33,34 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ int c_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
+// The same MFMA with the accumulator pinned to AGPRs, for long-lived
+// accumulators in kernels whose VGPRs are full (the compiler's VGPR/AGPR form
+// choice is all-or-nothing per function). The compiler does not see hazards
+// inside inline asm, so the two cases that apply here are covered by hand:
+// s_nop 1 gives the 2 wait states a VALU-written A/B operand needs before an
+// MFMA reads it, and agpr_fence() must separate the last accumulation from
+// any non-MFMA read of the accumulator. Back-to-back accumulation into the
+// same registers needs no wait states.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Zero accumulator defined directly in AGPRs (an MFMA of zero operands with
+// C = 0), so a loop-carried accumulator never has a VGPR definition. The
+// zero operand is written by VALU just before, hence the same s_nop 1.
+__device__ __forceinline__ f32x16 agpr_zero() {
+  f32x16 acc;
+  const bf16x8 z = {};
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+  return acc;
+}
+
+// 16 wait states between the last MFMA that wrote acc and the reads after it
+// (the compiler itself places 11 to 12 after this MFMA before a VALU read).
+__device__ __forceinline__ void agpr_fence(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
 // Eight fp32 -> eight bf16 (round to nearest even) as one MFMA operand.
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
                                         float a5, float a6, float a7) {
@@ -163,6 +191,77 @@ __device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, int voff, int soff) {
 
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (no VGPR staging). One instruction moves 64
+// lanes x 16 bytes (or x 4 bytes) into LDS at dst + 16 * lane (4 * lane); dst
+// must be the same for the whole wavefront. Completion is tracked by vmcnt
+// only, so consumers wait with wait_vm<N>() and then a workgroup barrier.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(rsrc_t r, void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(const float* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Row swizzle of tiles filled by dma16: slot ch (16 bytes) of row r holds
+// logical chunk ch ^ dma_swz<D>(r). Chosen so that (a) 16 consecutive rows
+// read at one logical chunk (ds_read_b128 of an MFMA operand) and (b) the
+// 4 rows x 4 chunks one 32-lane half of a transposing read touches (rows
+// 4a .. 4a+3 and 8 + 4a .. 8 + 4a + 3, chunks 4b .. 4b+3) fall in distinct
+// 16-byte bank groups. For r < 8, dma_swz(r + 8) == dma_swz(r) ^ 2.
+template <int D>
+__device__ __forceinline__ int dma_swz(int r) {
+  if constexpr (D >= 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {   // 128-byte rows: two rows per 256-byte bank line
+    const int t = (r >> 1) & 7;
+    return ((t & 1) << 2) | (t >> 1);
+  }
+}
+
+// gfx950 transposing LDS read of 4 x 16-bit values. Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8 bytes read by lanes
+// 4j + i / 4 as its element j: if lane 4j + t reads row j, columns 4t .. 4t+3
+// of a 16-bit matrix, lane i ends up with column i, rows 0..3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ bf16x4 ds_read_tr(uint32_t lds_byte) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_byte));
+  return __builtin_bit_cast(bf16x4, x);
+}
+
+// Reads at a 32-bit LDS byte address (no generic-pointer conversion).
+__device__ __forceinline__ bf16x8 lds_ld16(uint32_t lds_byte) {
+  return *(const lds_bf16x8*)(lds_byte);
+}
+__device__ __forceinline__ f32x4 lds_ldf4(uint32_t lds_byte) {
+  return *(const lds_f32x4*)(lds_byte);
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)(p);
+}
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 }  // namespace attn71

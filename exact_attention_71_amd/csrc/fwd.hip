@@ -91,7 +91,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
   const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int qw0 = m0 + w * 32 * QB;     // first query row of this wave
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const bf16* __restrict__ qp = static_cast<const bf16*>(p.q);
@@ -359,7 +360,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int grp = w >> 2;               // 0: group A (stages K), 1: group B (stages V)
   const int gtid = tid & (GT - 1);
   const int qw0 = m0 + w * 32;

@@ -47,6 +47,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* dsum;            // D = rowsum(dO o O), same layout as LSE
+  float* lse2;            // LSE * log2(e), same layout as LSE
   float* dq_acc;          // fp32 [rows][Hq][d]
   int* sem;               // deterministic: one counter per (query block, query head)
   int* ticket;            // deterministic: workgroup ticket counter
@@ -102,8 +103,8 @@ template <int D> struct DqCfg {
 inline int dq_block_m(int d) { return d <= 128 ? DqCfg<128>::BM : DqCfg<256>::BM; }
 
 template <int D> struct DkdvCfg {
-  static constexpr int NW = (D <= 128) ? 8 : 4;   // wavefronts, 32 keys each
-  static constexpr int BN = NW * 32;              // keys per workgroup
+  static constexpr int KB = (D <= 128) ? 2 : 1;   // 32-key blocks per wavefront
+  static constexpr int BN = 4 * 32 * KB;          // keys per workgroup (four wavefronts)
   static constexpr int BM = (D == 64) ? 64 : 32;  // queries per step
 };
 inline int dkdv_block_n(int d) { return d <= 128 ? DkdvCfg<128>::BN : DkdvCfg<256>::BN; }
