@@ -24,7 +24,11 @@ FLAGS = [
     # packed fp32 VALU ops stay off: the compiler may not form v_pk_{add,mul,fma}_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in VGPR form: avoids AGPR<->VGPR copies of live tiles
+    # (long-lived accumulators are pinned to AGPRs by inline asm instead)
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # fully unrolled hand-scheduled steps exceed the default #pragma unroll size
+    # limit; a partial unroll would index register arrays dynamically
+    "-mllvm", "-pragma-unroll-threshold=65536",
     # fp32 atomics as global_atomic_add_f32 (no compare-and-swap loops)
     "-munsafe-fp-atomics",
     "-Wall", "-Wno-unused-function",

@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { dk[kb][db] = agpr_zero(); dv[kb][db] = agpr_zero(); }
 
+  const uint32_t lds_q = lds_addr(qtile), lds_l = lds_addr(lsed);   // LDS byte addresses
   // Steps walk (query head of the group, query block) with the block fastest.
   // Cursors replace a division per step: the issue cursor runs NS - 1 steps
   // ahead of the compute cursor (which only needs the block).
@@ -133,15 +134,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int slot = base + lane;
       const int r = slot / SPR, pos = slot % SPR;
       const int voff = (r * (int)qstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
-      dma16(qr, qtile + st * TILE + base * 16, voff);
-      dma16(orr, otile + st * TILE + base * 16, voff);
+      dma16(qr, lds_q + st * TILE + base * 16, voff);
+      dma16(orr, lds_q + (NS + st) * TILE + base * 16, voff);
     }
     if (w < NLD) {
       const int idx = 64 * w + lane;                // [LSE * log2 e rows | D rows]
       const bool is_l = idx < BM;
       const int r = imin(i_m * BM + (idx & (BM - 1)), lq - 1);
       const int64_t so = lse_seq + (int64_t)i_hq * lse_head + r;
-      dma4(is_l ? p.lse2 + so : p.dsum + so, lsed + st * 2 * BM + 64 * w);
+      dma4(is_l ? p.lse2 + so : p.dsum + so, lds_l + (st * 2 * BM + 64 * w) * 4);
     }
     if (++i_m == nm) { i_m = m_first; ++i_hq; }
   };
@@ -171,7 +172,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // + NS * TILE): ar[kk] for the S / dP operands, at[db][h] for the two
   // transposing reads. They move by one slot per step; slot offsets are
   // multiples of TILE, above every bit the XORs touch.
-  const uint32_t lds_q = lds_addr(qtile), lds_l = lds_addr(lsed);
   uint32_t ar[KS], at[NDB][2];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_q + (a_rm ^ (32 * kk));
@@ -192,132 +192,146 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   };
   static_assert(TILE % 8192 == 0 || TILE >= 2 * RB * 32, "slot offsets clear the XOR bits");
 
-  // One step on ring slot st for query block mq0. Masking (causal diagonal,
-  // key tail) is one compare and one select per element: register i of a
+  // One step for query block mq0. Masking (causal diagonal, key tail) sets
+  // S = -inf in a branch of its own on the steps that need it: register i of a
   // tile is query row mq0 + 32 qb + 8 (i / 4) + 4 g + i % 4, so with
   // rel = key - mq0 - 4g the pair is hidden iff rel > 32 qb + 8 (i / 4) + i % 4
   // (rel = INT_MAX for keys past the sequence, -1 where nothing is hidden).
-  // A second, unmasked copy of the body would split the AGPR accumulators
-  // over two paths, which the register allocator answers with spills.
+  // Only S crosses that branch; a second copy of the whole body would split
+  // the AGPR accumulators over two paths (the allocator answers with spills).
   auto step_body = [&](int mq0, bool need_mask) {
     constexpr int OT = NS * TILE;   // dO tile offset from the Q tile
     int rel[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = wk0 + 32 * kb + c;
-      rel[kb] = !need_mask ? -1 : key >= lk ? 0x7fffffff : (causal ? key - mq0 - 4 * g : -1);
+      rel[kb] = key >= lk ? 0x7fffffff : (causal ? key - mq0 - 4 * g : -1);
     }
-    // The step runs in phases (S, P, dV, dP, dS, dK) fenced against the
-    // scheduler so that at most two 32 x 32 fp32 tiles per key block are
-    // live next to the resident K and V fragments.
-    // ---- S = Q K^T (query on the register, key on the lane)
-    f32x16 s[NQB][KB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const bf16x8 aq = lds_ld16(ar[kk] + qb * 32 * RB);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = mfma32(aq, kf[kb][kk], s[qb][kb]);
+    // Hand schedule (one wave per SIMD: nothing else hides this wave's VALU
+    // work, and issue is in order). The step reads one stream of LDS operand
+    // fragments, two ahead of use: NG1 of Q (S), NG1 of dO (dP), NG2 of dO^T
+    // (dV^T), NG2 of Q^T (dK^T). After each dP MFMA comes its slice of the
+    // P = exp(...) work and after each dV^T MFMA its slice of dS = P o (dP - D),
+    // so that VALU runs while the MFMA executes; sched_barrier pins the order.
+    constexpr int NG1 = KS * NQB, NG2 = NQB * 2 * NDB, NF = 2 * NG1 + 2 * NG2;
+    constexpr int E = NQB * KB * 16;               // P (or dS) elements per lane
+    constexpr int PPM = E / (NG1 * KB);            // P elements per dP MFMA
+    constexpr int SPM = E / (NG2 * KB);            // dS elements per dV^T MFMA
+    static_assert(PPM * NG1 * KB == E && SPM * NG2 * KB == E, "even slices");
+    auto fetch = [&](int f) -> bf16x8 {
+      if (f < 2 * NG1) {   // Q (then dO): fragment (kk, qb)
+        const int x = f % NG1, kk = x / NQB, qb = x % NQB;
+        return lds_ld16(ar[kk] + (f < NG1 ? 0 : OT) + qb * 32 * RB);
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- P = 2^(S scale log2 e - LSE log2 e), masked on the exponent
-    bf16x8 pb[NQB][KB][2];
+      const int x = (f - 2 * NG1) % NG2;           // dO^T (then Q^T): (qb, tt, db)
+      const int qb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
+      const int off = (f < 2 * NG1 + NG2 ? OT : 0) + (qb * 32 + 16 * tt) * RB;
+      return cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
+    };
+    f32x16 s[NQB][KB], dp[NQB][KB];
+    bf16x8 pb[NQB][KB][2], sb[NQB][KB][2];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = lds_ldf4(al + 4 * (qb * 32 + 8 * j));
+      for (int kb = 0; kb < KB; ++kb) { s[qb][kb] = f32x16{}; dp[qb][kb] = f32x16{}; }
+    // element e of the P / dS pass: (qb, j, kb, r) -> register 4j + r of tile (qb, kb).
+    // Row values (LSE log2 e, then D) come in blocks of 4 rows (qb, j), read one
+    // block ahead: LDS returns in order, so a read issued just before its use
+    // would make the wait drain the operand fragments prefetched after it.
+    constexpr int NJ = 4 * NQB;
+    auto row_read = [&](int b) {   // block b of [LSE blocks | D blocks]
+      const int x = b % NJ;
+      return lds_ldf4(al + 4 * ((b < NJ ? 0 : BM) + (x / 4) * 32 + 8 * (x % 4)));
+    };
+    f32x4 rv_cur = {}, rv_next = row_read(0);
+    auto row_block = [&](int b) {  // entering block b: rotate and prefetch b + 1
+      rv_cur = rv_next;
+      if (b + 1 < 2 * NJ) rv_next = row_read(b + 1);
+    };
+    auto p_elem = [&](int e) {
+      const int qb = e / (KB * 16), rem = e % (KB * 16);
+      const int j = rem / (KB * 4), kb = (rem / 4) % KB, r = rem % 4;
+      if (kb == 0 && r == 0) row_block(qb * 4 + j);
+      float pv = fast_exp2(__builtin_fmaf(s[qb][kb][4 * j + r], sl2, -rv_cur[r]));
+      pin(pv);
+      s[qb][kb][4 * j + r] = pv;
+      if ((j & 1) && kb == KB - 1 && r == 3) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = __builtin_fmaf(s[qb][kb][4 * j + r], sl2, -l4[r]);
-            s[qb][kb][4 * j + r] = fast_exp2(rel[kb] > qb * 32 + 8 * j + r ? neg_inf() : x);
-          }
+        for (int k2 = 0; k2 < KB; ++k2) pb[qb][k2][j >> 1] = pack_half(s[qb][k2], j >> 1);
       }
+    };
+    auto s_elem = [&](int e) {
+      const int qb = e / (KB * 16), rem = e % (KB * 16);
+      const int j = rem / (KB * 4), kb = (rem / 4) % KB, r = rem % 4;
+      if (kb == 0 && r == 0) row_block(NJ + qb * 4 + j);
+      float ds = s[qb][kb][4 * j + r] * (dp[qb][kb][4 * j + r] - rv_cur[r]);
+      pin(ds);
+      dp[qb][kb][4 * j + r] = ds;
+      if ((j & 1) && kb == KB - 1 && r == 3) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+        for (int k2 = 0; k2 < KB; ++k2) sb[qb][k2][j >> 1] = pack_half(dp[qb][k2], j >> 1);
+      }
+    };
+    bf16x8 f0 = fetch(0), f1 = fetch(1);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int f = 0; f < NF; ++f) {
+      const bf16x8 cur = f0;
+      f0 = f1;
+      if (f + 2 < NF) f1 = fetch(f + 2);
+      if (f < NG1) {                                  // S = Q K^T
+        const int kk = f / NQB, qb = f % NQB;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) pb[qb][kb][tt] = pack_half(s[qb][kb], tt);
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dV^T += dO^T P over every 32-dim block (A by transposing reads)
+        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = mfma32(cur, kf[kb][kk], s[qb][kb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (f == NG1 - 1 && need_mask) {   // causal diagonal and key tail: S = -inf
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+          for (int q2 = 0; q2 < NQB; ++q2)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int toff = (qb * 32 + 16 * tt) * RB;
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 ao = cat8(ds_read_tr(at[db][0] + OT + toff), ds_read_tr(at[db][1] + OT + toff));
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mfma32_agpr(dv[kb][db], ao, pb[qb][kb][tt]);
+              for (int i = 0; i < 16; ++i)
+                s[q2][kb][i] = rel[kb] > q2 * 32 + 8 * (i >> 2) + (i & 3) ? neg_inf() : s[q2][kb][i];
         }
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dP = dO V^T
-    f32x16 dp[NQB][KB];
+      } else if (f < 2 * NG1) {                       // dP = dO V^T, with P
+        const int x = f - NG1, kk = x / NQB, qb = x % NQB;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+        for (int kb = 0; kb < KB; ++kb) {
+          dp[qb][kb] = mfma32(cur, vf[kb][kk], dp[qb][kb]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = f32x16{};
+          for (int e = 0; e < PPM; ++e) p_elem((x * KB + kb) * PPM + e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if (f < 2 * NG1 + NG2) {                 // dV^T += dO^T P, with dS
+        const int x = f - 2 * NG1;
+        const int qb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+        for (int kb = 0; kb < KB; ++kb) {
+          mfma32_agpr(dv[kb][db], cur, pb[qb][kb][tt]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const bf16x8 ao = lds_ld16(ar[kk] + OT + qb * 32 * RB);
+          for (int e = 0; e < SPM; ++e) s_elem((x * KB + kb) * SPM + e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {                                        // dK^T += Q^T dS
+        const int x = f - 2 * NG1 - NG2;
+        const int qb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = mfma32(ao, vf[kb][kk], dp[qb][kb]);
+        for (int kb = 0; kb < KB; ++kb) mfma32_agpr(dk[kb][db], cur, sb[qb][kb][tt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dS = P o (dP - D)
-    bf16x8 sb[NQB][KB][2];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 d4 = lds_ldf4(al + 4 * (BM + qb * 32 + 8 * j));
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            dp[qb][kb][4 * j + r] = s[qb][kb][4 * j + r] * (dp[qb][kb][4 * j + r] - d4[r]);
-      }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) sb[qb][kb][tt] = pack_half(dp[qb][kb], tt);
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dK^T += Q^T dS
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int toff = (qb * 32 + 16 * tt) * RB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 aq = cat8(ds_read_tr(at[db][0] + toff), ds_read_tr(at[db][1] + toff));
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mfma32_agpr(dk[kb][db], aq, sb[qb][kb][tt]);
-        }
-      }
   };
 
-  // ---- prologue: fill NS - 1 ring slots
+  // ---- prologue: fill NS - 1 ring slots. The full wait also retires the K / V
+  // fragment loads: the compiler then knows them complete and places no wait
+  // of its own inside the loop (where the outstanding ring loads, which it
+  // cannot see, would make such a wait stall on the prefetch).
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < n_steps) issue(s);
-  if (n_steps > 0) wait_next(n_steps > 1);
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
 
   for (int step = 0; step < n_steps; ++step) {
     const int st = step % NS;

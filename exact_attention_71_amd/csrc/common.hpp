@@ -45,6 +45,11 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Keeps a value's computation where it stands in the source: sched_barrier
+// only orders instructions with side effects, so pure VALU results would
+// otherwise be placed next to their (later) uses by instruction selection.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // Zero accumulator defined directly in AGPRs (an MFMA of zero operands with
 // C = 0), so a loop-carried accumulator never has a VGPR definition. The
 // zero operand is written by VALU just before, hence the same s_nop 1.
@@ -199,14 +204,22 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, int voff, int soff) {
 // must be the same for the whole wavefront. Completion is tracked by vmcnt
 // only, so consumers wait with wait_vm<N>() and then a workgroup barrier.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(rsrc_t r, void* dst, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+// Written as inline asm: given the builtins, the compiler cannot tell which
+// LDS bytes a load fills, so it makes later LDS reads wait for every such
+// load in flight (vmcnt(0)), including those that prefetch a later step into
+// another buffer. Hidden from it, the loads are ordered by the explicit
+// wait_vm<N>() + barrier alone; its own vmcnt waits only grow more
+// conservative with extra loads outstanding (they complete in order). M0
+// carries the LDS address; s_nop 0 is the one wait state between writing M0
+// and an LDS-DMA read of it. Nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_byte, int voff) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(lds_byte), "s"(r) : "memory", "m0");
 }
 
-__device__ __forceinline__ void dma4(const float* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+__device__ __forceinline__ void dma4(const float* src, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_byte) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
