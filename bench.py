@@ -4,14 +4,15 @@
 
 One step = one forward (attn_fwd: online softmax, tau = 8 conditional
 rescale, LSE) plus one backward (attn_bwd phases: D = rowsum(dO o O) and
-clears, the dK/dV/dQ main kernel, dQ conversion) over one batch of seeded
-synthetic bf16 inputs already resident in HBM. Throughput counts algorithmic
-flops: forward 4*B*H*Sq*Sk*d, backward 2.5x, both halved for causal.
+LSE*log2 e, the key-block dK/dV kernel, the query-block dQ kernel) over one
+batch of seeded synthetic bf16 inputs already resident in HBM. Throughput
+counts algorithmic flops: forward 4*B*H*Sq*Sk*d, backward 2.5x, both halved
+for causal.
 
 Prints one JSON line. The "roofline" object covers the dominant kernel (the
-backward main kernel for fwd+bwd workloads, the forward kernel for forward-only
-ones), timed with HIP events on the stream it runs on. "cpu_baseline" times
-the float64 oracle on a bounded sample of the same workload.
+longest-running one; the dK/dV kernel for the fwd+bwd workloads), timed with
+HIP events on the stream it runs on. "cpu_baseline" times the float64 oracle
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -249,7 +250,8 @@ def main() -> int:
     half = fl["fwd"] / 2.0
     kflops = {"fwd": fl["fwd"], "bwd_main": (5 if fused else 4) * half,
               "bwd_dq": 1 * half}
-    names = {"fwd": f"fwd_kernel<{w.head_dim}>", "bwd_main": f"bwd_main_kernel<{w.head_dim}>",
+    names = {"fwd": f"fwd_kernel<{w.head_dim}>",
+             "bwd_main": f"{'bwd_main' if fused else 'bwd_dkdv'}_kernel<{w.head_dim}>",
              "bwd_dq": f"bwd_dq_kernel<{w.head_dim}>"}
     dom = max((n for n in kms if n in kflops), key=lambda n: kms[n])
     dom_ms = kms[dom]
