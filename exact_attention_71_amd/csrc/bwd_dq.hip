@@ -12,9 +12,12 @@
 // are per-lane scalars, and dQ is written once, in bf16. No cross-workgroup
 // reduction: the result is bit-reproducible by construction.
 //
-// Per workgroup: NW wavefronts x 32 query rows. LDS per key tile (double
-// buffered): K row-major (A of S^T), V row-major (A of dP^T), K^T with the
-// key order permuted inside each 16 keys (A of dQ^T).
+// Per workgroup: NW wavefronts x 32 query rows (two per SIMD: one wave's
+// MFMAs overlap the other's elementwise work). K and V tiles of BN keys stream
+// into a three-deep LDS ring by direct global->LDS loads issued two tiles
+// ahead (row-major, XOR row swizzle dma_swz). ds_read_b128 gives the A
+// operands of S^T and dP^T; the transposing read ds_read_b64_tr_b16 gives K^T,
+// the A operand of dQ^T, from the same K tile.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "schedule.hpp"
@@ -23,30 +26,27 @@ namespace attn71 {
 
 namespace {
 
-template <int D, int BN>
-struct alignas(16) DqSmem {
-  static constexpr int KR = D + 8;    // K, V row stride (elements)
-  static constexpr int TR = BN + 8;   // K^T row stride
-  alignas(16) bf16 k[2][BN * KR];
-  alignas(16) bf16 v[2][BN * KR];
-  alignas(16) bf16 kt[2][D * TR];
-};
-
 template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
-  constexpr int KS = D / 16;
-  constexpr int NKB = BN / 32;
-  constexpr int NDB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int KUN = (BN / 4) * CPR;        // 4-key x 8-dim units of K
-  constexpr int KU = (KUN + NT - 1) / NT;
-  constexpr int VCH = BN * CPR / NT;         // 16-byte chunks of V per thread
-  static_assert(VCH * NT == BN * CPR, "V staging must divide evenly");
-  static_assert(KUN % 64 == 0, "K staging covers whole wavefronts");
-  using SM = DqSmem<D, BN>;
-  __shared__ SM sm;
+  constexpr int KS = D / 16;            // k-steps of S^T and dP^T
+  constexpr int NKB = BN / 32;          // 32-key blocks per tile
+  constexpr int NDB = D / 32;           // 32-dim blocks of dQ^T
+  constexpr int RB = 2 * D;             // bytes per tile row
+  constexpr int SPR = D / 8;            // 16-byte slots per row
+  constexpr int TILE = BN * RB;         // bytes of one K (or V) tile
+  constexpr int NS = 3;                 // ring depth
+  static_assert(NS == 3, "wait_next() counts at most one later tile in flight");
+  constexpr int CH = TILE / (16 * NT);  // dma16 per thread per tile
+  static_assert(CH * 16 * NT == TILE, "tile split over the workgroup");
+  constexpr int OPS = 2 * CH;           // ring loads per thread per tile (K and V)
+  static_assert(OPS < 64, "vmcnt range");
+  static_assert(BM == DqCfg<D>::BM && BN == DqCfg<D>::BN, "host and kernel tiling agree");
+  // [NS] K tiles | [NS] V tiles
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];
+  const uint32_t lds_k = lds_addr(smem);
+  constexpr int VT = NS * TILE;         // V tile offset from the K tile
 
   Tile t;
   if (p.sv.cu_q) {
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const float sl2 = p.scale_log2;
 
-  // ---- this lane's query row: Q and dO as B operands, LSE and D as scalars
+  // ---- this lane's query row: Q and dO as B operands, LSE log2 e and D as scalars
   const int64_t qbytes = ((int64_t)(lq - 1) * qstride + D) * 2;
   const rsrc_t qr = make_rsrc(static_cast<const bf16*>(p.q) + qs * qstride + (int64_t)h * D, qbytes);
   const rsrc_t dr = make_rsrc(static_cast<const bf16*>(p.dout) + qs * qstride + (int64_t)h * D, qbytes);
@@ -98,124 +98,146 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   if (myq < lq) {
     const int64_t so = p.sv.cu_q ? (int64_t)h * p.sv.total_q + qs + myq
                                  : ((int64_t)t.seq * p.hq + h) * p.sv.seqlen_q + myq;
-    lse2 = p.lse[so] * 1.4426950408889634f;
+    lse2 = p.lse2[so];
     dsum = p.dsum[so];
   }
 
-  // ---- K / V staging
+  // ---- K / V ring: tile n into slot n % NS. Keys past the sequence read as
+  // zero (buffer range) and are masked below.
   const int64_t kv_bytes = ((int64_t)(lk - 1) * kstride + D) * 2;
   const bf16* kbase = static_cast<const bf16*>(p.k) + ks0 * kstride + (int64_t)kvh * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + ks0 * kstride + (int64_t)kvh * D;
-  int koffs[KU], voffs[VCH];
+  int voffs[CH];
 #pragma unroll
-  for (int j = 0; j < KU; ++j) {
-    const int u = imin(tid + NT * j, KUN - 1);
-    int kg, dc;
-    unit_coords<CPR, BN / 4>(u, &kg, &dc);
-    koffs[j] = ((4 * kg) * (int)kstride + dc * 8) * 2;
+  for (int i = 0; i < CH; ++i) {
+    const int slot = (i * NW + w) * 64 + lane;
+    const int r = slot / SPR, pos = slot % SPR;
+    voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
   }
-#pragma unroll
-  for (int j = 0; j < VCH; ++j) {
-    const int u = tid + NT * j;
-    voffs[j] = ((u / CPR) * (int)kstride + (u % CPR) * 8) * 2;
-  }
-  bf16x8 kreg[KU][4], vreg[VCH];
-  auto load_tile = [&](int n) {
+  auto issue = [&](int n) {
     const int64_t t0 = (int64_t)n * BN * kstride;
     const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
     const rsrc_t vr = make_rsrc(vbase + t0, kv_bytes - 2 * t0);
+    const int st = n % NS;
 #pragma unroll
-    for (int j = 0; j < KU; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) kreg[j][r] = buf_load16(kr, koffs[j] + r * (int)kstride * 2, 0);
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) vreg[j] = buf_load16(vr, voffs[j], 0);
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t dst = lds_k + st * TILE + (i * NW + w) * 1024;
+      dma16(kr, dst, voffs[i]);
+      dma16(vr, dst + VT, voffs[i]);
+    }
   };
-  auto store_tile = [&](int buf) {
+  auto wait_next = [&](bool later_issued) {
+    if (later_issued) wait_vm<OPS>(); else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // per-lane LDS addresses of slot 0 (see dma_swz): ar[kk] for the A operands of
+  // S^T / dP^T (key row c of each 32-key block, logical chunk 2kk + g), at[db][h]
+  // for the transposing reads of K^T (16-lane group (g, dh), lane s16 reads key
+  // row 4g + s16/4 (+8 for k slots 4..7), dims 32db + 16dh + 4(s16%4)). Row
+  // rq + 8 has dma_swz(rq) ^ 2, so the second read is at (a_t ^ 32) + 8 RB.
+  const int a_rm = c * RB + 16 * (g ^ dma_swz<D>(c));
+  const int s16 = lane & 15, dh = (lane >> 4) & 1;
+  const int rq = 4 * g + (s16 >> 2);
+  const int cl = 2 * dh + ((s16 & 3) >> 1);
+  const int a_t = rq * RB + 16 * (cl ^ dma_swz<D>(rq)) + 8 * (s16 & 1);
+  uint32_t ar[KS], at[NDB][2];
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int u = tid + NT * j;
-      if (KUN % NT != 0 && u >= KUN) continue;
-      int kg, dc;
-      unit_coords<CPR, BN / 4>(u, &kg, &dc);
+  for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_k + (a_rm ^ (32 * kk));
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<bf16x8*>(&sm.k[buf][(4 * kg + r) * SM::KR + dc * 8]) = kreg[j][r];
-      const int pos = perm16(4 * kg);
+  for (int db = 0; db < NDB; ++db) {
+    at[db][0] = lds_k + (a_t ^ (64 * db));
+    at[db][1] = lds_k + (a_t ^ (64 * db + 32)) + 8 * RB;
+  }
+  auto advance_slot = [&](int st) {
+    const int dq = st == NS - 1 ? -(NS - 1) * TILE : TILE;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 x;
-        x[0] = kreg[j][0][e]; x[1] = kreg[j][1][e]; x[2] = kreg[j][2][e]; x[3] = kreg[j][3][e];
-        *reinterpret_cast<bf16x4*>(&sm.kt[buf][(dc * 8 + e) * SM::TR + pos]) = x;
-      }
-    }
+    for (int kk = 0; kk < KS; ++kk) ar[kk] += dq;
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int u = tid + NT * j;
-      *reinterpret_cast<bf16x8*>(&sm.v[buf][(u / CPR) * SM::KR + (u % CPR) * 8]) = vreg[j];
-    }
+    for (int db = 0; db < NDB; ++db) { at[db][0] += dq; at[db][1] += dq; }
   };
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // One key tile. Register i of an S^T tile is key k0 + 32 kb + 8 (i / 4) +
+  // 4 g + i % 4, so with lim = min(q, lk - 1) - k0 - 4g (q only when causal)
+  // the pair is hidden iff 32 kb + 8 (i / 4) + i % 4 > lim. The operands come
+  // as one stream of fragments two ahead of use: NG1 of K (S^T), NG1 of V
+  // (dP^T), NG2 of K^T (dQ^T).
+  constexpr int NG1 = KS * NKB, NG2 = NKB * 2 * NDB, NF = 2 * NG1 + NG2;
+  auto tile_body = [&](int k0, bool need_mask) {
+    auto fetch = [&](int f) -> bf16x8 {
+      if (f < 2 * NG1) {
+        const int x = f % NG1, kk = x / NKB, kb = x % NKB;
+        return lds_ld16(ar[kk] + (f < NG1 ? 0 : VT) + kb * 32 * RB);
+      }
+      const int x = f - 2 * NG1;
+      const int kb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
+      const int off = (kb * 32 + 16 * tt) * RB;
+      return cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
+    };
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+    bf16x8 f0 = fetch(0), f1 = fetch(1);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const bf16x8 cur = f0;
+      f0 = f1;
+      if (f + 2 < NF) f1 = fetch(f + 2);
+      if (f < NG1) {                                  // S^T = K Q^T
+        const int kk = f / NKB, kb = f % NKB;
+        s[kb] = mfma32(cur, qf[kk], s[kb]);
+      } else if (f < 2 * NG1) {                       // dP^T = V dO^T
+        const int x = f - NG1, kk = x / NKB, kb = x % NKB;
+        dp[kb] = mfma32(cur, df[kk], dp[kb]);
+        if (x == NG1 - 1) {
+          // ---- P^T = 2^(S^T scale log2 e - LSE log2 e), dS^T = P^T o (dP^T - D)
+          if (need_mask) {
+            const int lim = imin(causal ? myq : 0x7fffffff, lk - 1) - k0 - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                s[kb][i] = 32 * kb + 8 * (i >> 2) + (i & 3) > lim ? neg_inf() : s[kb][i];
+          }
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float pv = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -lse2));
+              dp[kb][i] = pv * (dp[kb][i] - dsum);
+            }
+        }
+      } else {                                        // dQ^T += K^T dS^T
+        const int x = f - 2 * NG1;
+        const int kb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
+        dqacc[db] = mfma32(cur, pack_half(dp[kb], tt), dqacc[db]);
+      }
+    }
+  };
+
+  // ---- prologue: fill NS - 1 ring slots. The full wait also retires the Q / dO
+  // fragment loads, so the compiler places no wait of its own in the loop
+  // (where the ring loads, which it cannot see, would make it stall).
+#pragma unroll
+  for (int n = 0; n < NS - 1; ++n)
+    if (n < n_tiles) issue(n);
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
 
   for (int n = 0; n < n_tiles; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < n_tiles) load_tile(n + 1);
+    const int st = n % NS;
+    if (n + NS - 1 < n_tiles) issue(n + NS - 1);
     const int k0 = n * BN;
+    // whole wave below the diagonal's start: no visible pair in this tile
     const bool active = !(causal && k0 > qw0 + 31);
-    if (active) {
-      f32x16 s[NKB], dp[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int o = (kb * 32 + c) * SM::KR + (2 * kk + g) * 8;
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.k[buf][o]);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.v[buf][o]);
-          s[kb] = mfma32(ak, qf[kk], s[kb]);
-          dp[kb] = mfma32(av, df[kk], dp[kb]);
-        }
-      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = __builtin_fmaf(s[kb][i], sl2, -lse2);
-          if (need_mask) {   // select on the exponent: 2^-inf = 0, no per-lane branch
-            const int key = k0 + kb * 32 + c_row(i, g);
-            const bool hide = (key >= lk) | (causal & (key > myq));
-            x = hide ? neg_inf() : x;
-          }
-          const float pv = fast_exp2(x);
-          dp[kb][i] = pv * (dp[kb][i] - dsum);
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 sb = pack_half(dp[kb], tt);
-          const int col = kb * 32 + 16 * tt + 8 * g;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                &sm.kt[buf][(db * 32 + c) * SM::TR + col]);
-            dqacc[db] = mfma32(a, sb, dqacc[db]);
-          }
-        }
-    }
-    if (n + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+    const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+    if (active) tile_body(k0, need_mask);
+    advance_slot(st);
+    if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
   }
 
   // ---- dQ = alpha * dQ^T, bf16, this lane's query row
