@@ -114,8 +114,10 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # steady state: the GPU's clocks ramp up over the first ~10 ms of sustained
+    # MFMA load, so the default warmup covers about 50 ms of steps
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="causal8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)

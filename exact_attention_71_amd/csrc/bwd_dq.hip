@@ -164,9 +164,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   // One key tile. Register i of an S^T tile is key k0 + 32 kb + 8 (i / 4) +
   // 4 g + i % 4, so with lim = min(q, lk - 1) - k0 - 4g (q only when causal)
   // the pair is hidden iff 32 kb + 8 (i / 4) + i % 4 > lim. The operands come
-  // as one stream of fragments two ahead of use: NG1 of K (S^T), NG1 of V
+  // as one stream of fragments PF ahead of use: NG1 of K (S^T), NG1 of V
   // (dP^T), NG2 of K^T (dQ^T).
   constexpr int NG1 = KS * NKB, NG2 = NKB * 2 * NDB, NF = 2 * NG1 + NG2;
+  constexpr int PF = 2;                 // fragments in flight ahead of use
   auto tile_body = [&](int k0, bool need_mask) {
     auto fetch = [&](int f) -> bf16x8 {
       if (f < 2 * NG1) {
@@ -181,12 +182,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
     f32x16 s[NKB], dp[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
-    bf16x8 f0 = fetch(0), f1 = fetch(1);
+    bf16x8 fq[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fq[i] = fetch(i);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const bf16x8 cur = f0;
-      f0 = f1;
-      if (f + 2 < NF) f1 = fetch(f + 2);
+      const bf16x8 cur = fq[0];
+#pragma unroll
+      for (int i = 0; i + 1 < PF; ++i) fq[i] = fq[i + 1];
+      if (f + PF < NF) fq[PF - 1] = fetch(f + PF);
       if (f < NG1) {                                  // S^T = K Q^T
         const int kk = f / NKB, kb = f % NKB;
         s[kb] = mfma32(cur, qf[kk], s[kb]);

@@ -15,11 +15,11 @@
 //    (lane % 32) and half of the keys of each 32-key block: the row max needs
 //    one exchange with lane ^ 32, the rescale factor is a per-lane scalar, and
 //    the accumulator of S^T is already the B operand of O^T = V^T P^T;
-//  * K tiles sit in LDS row-major with a 16-byte-slot XOR swizzle; V tiles are
-//    written transposed (V^T, key order permuted inside each 16 keys) so the
-//    A operand of the PV product is one 16-byte LDS read per lane;
-//  * K/V for tile n+1 are fetched into registers while tile n computes and
-//    written to the other LDS buffer: one barrier per tile;
+//  * K and V tiles stream into an LDS ring (two or three slots) by direct
+//    global->LDS loads issued ahead of use, row-major under an XOR row
+//    swizzle: ds_read_b128 gives the A operand of S^T (K), and the transposing
+//    read ds_read_b64_tr_b16 gives the A operand of O^T += V^T P^T (V^T) with
+//    the key order of the S^T accumulator; one barrier per tile;
 //  * the rescale decision is one ballot per wavefront (any row over tau);
 //  * exp2 runs on v_exp_f32; EMU > 0 moves EMU of every 8 elements to the
 //    Cody-Waite + Horner polynomial on the FMA path.
@@ -62,14 +62,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
   constexpr int KS = D / 16;            // MFMA k-steps over the head dim
   constexpr int NKB = BN / 32;          // 32-key blocks per tile
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-  constexpr int KCH = BN * CPR / NT;    // K chunks staged per thread
-  constexpr int VUN = (BN / 4) * CPR;   // 4-key x 8-dim V units per tile
-  constexpr int VU = (VUN + NT - 1) / NT;  // V units per thread (last may be partial)
-  static_assert(KCH * NT == BN * CPR, "K staging must divide evenly");
-  static_assert(VUN % 64 == 0, "V staging covers whole wavefronts");
-  using SM = FwdSmem<D, BN>;
-  __shared__ SM sm;
+  constexpr int RB = 2 * D;             // bytes per K / V row in LDS
+  constexpr int SPR = D / 8;            // 16-byte slots per row
+  constexpr int TILE = BN * RB;         // bytes of one K (or V) tile
+  constexpr int NS = (3 * 2 * TILE <= 160 * 1024) ? 3 : 2;   // ring depth
+  constexpr int CH = TILE / (16 * NT);  // dma16 per thread per tile
+  static_assert(CH * 16 * NT == TILE, "tile split over the workgroup");
+  constexpr int OPS = 2 * CH;           // ring loads per thread per tile (K and V)
+  static_assert(OPS < 64, "vmcnt range");
+  // [NS] K tiles | [NS] V tiles
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];
+  const uint32_t lds_k = lds_addr(smem);
+  constexpr int VT = NS * TILE;         // V tile offset from the K tile
 
   // ---- which tile
   Tile t;
@@ -111,60 +115,70 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
     for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = buf_load16(qr, voff + 32 * kk, 0);
   }
 
-  // ---- K/V staging: buffers cover exactly this sequence's rows of this KV head
+  // ---- K / V ring: tile n into slot n % NS, loaded NS - 1 tiles ahead by
+  // direct global->LDS loads (row-major, XOR row swizzle dma_swz). Buffers
+  // cover exactly this sequence's rows of this KV head: keys past the end
+  // read as zero and are masked.
   const int64_t kv_bytes = ((int64_t)(lk - 1) * kstride + D) * 2;
   const bf16* kbase = kp + ks0 * kstride + (int64_t)kvh * D;
   const bf16* vbase = vp + ks0 * kstride + (int64_t)kvh * D;
-  int koff[KCH], voffs[VU];
+  int voffs[CH];
 #pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int u = tid + NT * j;
-    koff[j] = ((u / CPR) * (int)kstride + (u % CPR) * 8) * 2;
+  for (int i = 0; i < CH; ++i) {
+    const int slot = (i * NW + w) * 64 + lane;
+    const int r = slot / SPR, pos = slot % SPR;
+    voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
   }
-#pragma unroll
-  for (int j = 0; j < VU; ++j) {
-    const int u = imin(tid + NT * j, VUN - 1);   // idle lanes re-read a valid unit
-    int kg, dc;
-    unit_coords<CPR, BN / 4>(u, &kg, &dc);
-    voffs[j] = ((4 * kg) * (int)kstride + dc * 8) * 2;
-  }
-  bf16x8 kreg[KCH];
-  bf16x8 vreg[VU][4];
-  auto load_tile = [&](int n) {
+  auto issue = [&](int n) {
     // one resource per tile (scalar math): the range check covers the tail
     const int64_t t0 = (int64_t)n * BN * kstride;
     const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
     const rsrc_t vr = make_rsrc(vbase + t0, kv_bytes - 2 * t0);
+    const int st = n % NS;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) kreg[j] = buf_load16(kr, koff[j], 0);
-#pragma unroll
-    for (int j = 0; j < VU; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[j][r] = buf_load16(vr, voffs[j] + r * (int)kstride * 2, 0);
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t dst = lds_k + st * TILE + (i * NW + w) * 1024;
+      dma16(kr, dst, voffs[i]);
+      dma16(vr, dst + VT, voffs[i]);
+    }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int u = tid + NT * j;
-      const int row = u / CPR, ch = u % CPR;
-      *reinterpret_cast<bf16x8*>(&sm.k[buf][row * SM::KR + ch * 8]) = kreg[j];
+  // wait until the next tile is in LDS (with NS = 3 the tile after it may
+  // still be in flight), then make it visible to the workgroup
+  auto wait_next = [&](bool later_issued) {
+    if constexpr (NS == 3) {
+      if (later_issued) wait_vm<OPS>(); else wait_vm<0>();
+    } else {
+      (void)later_issued;
+      wait_vm<0>();
     }
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // per-lane LDS addresses of the current slot (see dma_swz): ar[kk] for the A
+  // operand of S^T (key row c of each 32-key block, logical chunk 2kk + g),
+  // at[db][h] for the transposing reads of V^T (16-lane group (g, dh), lane
+  // s16 reads key row 4g + s16/4 (+8 for k slots 4..7), dims
+  // 32db + 16dh + 4(s16%4)): the key order matches the registers of the S^T
+  // accumulator that become P^T. Row rq + 8 has dma_swz(rq) ^ 2.
+  const int a_rm = c * RB + 16 * (g ^ dma_swz<D>(c));
+  const int s16 = lane & 15, dh = (lane >> 4) & 1;
+  const int rq = 4 * g + (s16 >> 2);
+  const int cl = 2 * dh + ((s16 & 3) >> 1);
+  const int a_t = rq * RB + 16 * (cl ^ dma_swz<D>(rq)) + 8 * (s16 & 1);
+  uint32_t ar[KS], at[NDB][2];
 #pragma unroll
-    for (int j = 0; j < VU; ++j) {
-      const int u = tid + NT * j;
-      if (VUN % NT != 0 && u >= VUN) continue;   // whole wavefronts skip together
-      int kg, dc;
-      unit_coords<CPR, BN / 4>(u, &kg, &dc);
-      const int pos = perm16(4 * kg);          // 4 keys stay contiguous
+  for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_k + (a_rm ^ (32 * kk));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dc * 8 + e;
-        bf16x4 x;
-        x[0] = vreg[j][0][e]; x[1] = vreg[j][1][e]; x[2] = vreg[j][2][e]; x[3] = vreg[j][3][e];
-        const int off = d * SM::VR + pos;
-        *reinterpret_cast<bf16x4*>(&sm.vt[buf][off]) = x;
-      }
-    }
+  for (int db = 0; db < NDB; ++db) {
+    at[db][0] = lds_k + VT + (a_t ^ (64 * db));
+    at[db][1] = lds_k + VT + (a_t ^ (64 * db + 32)) + 8 * RB;
+  }
+  auto advance_slot = [&](int st) {
+    const int dq = st == NS - 1 ? -(NS - 1) * TILE : TILE;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) ar[kk] += dq;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { at[db][0] += dq; at[db][1] += dq; }
   };
 
   f32x16 oacc[QB][NDB];
@@ -178,15 +192,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
   }
   const float sl2 = p.scale_log2;
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // ---- prologue: fill NS - 1 slots. The full wait also retires the Q loads,
+  // so the compiler places no wait of its own in the loop (where the ring
+  // loads, which it cannot see, would make it stall).
+#pragma unroll
+  for (int n = 0; n < NS - 1; ++n)
+    if (n < n_tiles) issue(n);
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
 
   for (int n = 0; n < n_tiles; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < n_tiles) load_tile(n + 1);
+    const int st = n % NS;
+    if (n + NS - 1 < n_tiles) issue(n + NS - 1);
     const int k0 = n * BN;
     const bool active = !(causal && k0 > qw0 + 32 * QB - 1);
     if (active) {
@@ -200,8 +217,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
       for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &sm.k[buf][(kb * 32 + c) * SM::KR + (2 * kk + g) * 8]);
+          const bf16x8 a = lds_ld16(ar[kk] + kb * 32 * RB);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(a, qf[qb][kk], s[kb][qb]);
         }
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
           }
         lsum[qb] += acc;
       }
-      // O^T += V^T P^T
+      // O^T += V^T P^T (A of the PV product by transposing reads of V)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -270,19 +286,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
           bf16x8 pb[QB];
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_half(s[kb][qb], tt);
-          const int slot = kb * 4 + tt * 2 + g;
+          const int off = (kb * 32 + 16 * tt) * RB;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + c;
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(&sm.vt[buf][d * SM::VR + slot * 8]);
+            const bf16x8 a = cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(a, pb[qb], oacc[qb][db]);
           }
         }
     }
-    if (n + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+    advance_slot(st);
+    if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
   }
 
   // ---- epilogue: O = O_acc / l (true statistics), LSE = alpha*m + ln(l)
