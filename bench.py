@@ -68,6 +68,36 @@ def _describe(w) -> str:
             + (" det" if w.deterministic else "") + (" QKx3 half heads" if w.scaled_heads else ""))
 
 
+def device_info(torch) -> dict:
+    """CU count and peak engine clock as the runtime reports them (clock via
+    hipDeviceGetAttribute(hipDeviceAttributeClockRate = 5), in kHz)."""
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count}
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0 and val.value > 0:
+            mhz = val.value / 1000.0
+            out["peak_clock_mhz"] = mhz
+            # dense bf16 MFMA: 4096 flop per CU per clock (1024 per SIMD)
+            out["peak_bf16_tflops_at_clock"] = round(out["cus"] * 4096 * mhz * 1e6 / 1e12, 1)
+            out["clock_source"] = "hipDeviceGetAttribute(ClockRate)"
+    except OSError:  # pragma: no cover
+        pass
+    return out
+
+
+def host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float = 20.0) -> dict:
     """Float64 oracle on a bounded sample: whole (sequence, head) slabs of the
     workload, fwd (+bwd), until about budget_s seconds have been spent."""
@@ -106,9 +136,44 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
             break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"{heads} of {w.heads_q * (w.num_seqs if w.varlen else w.batch)} "
                       f"(sequence, head) slabs at length {sl}, {w.passes}, float64 numpy, "
                       f"{dt:.1f} s"}
+
+
+def sweep_tau_exp(torch, ea, args) -> int:
+    """Forward throughput vs the rescale threshold tau and the share of exp2
+    evaluated on the FMA path (accuracy of the same settings against the
+    oracle: tests/test_gpu_parity.py::test_tau_and_exp_emulation_variants_match_oracle)."""
+    from workloads import Workload, workload_flops, workload_inputs
+    for d in (64, 128, 256):
+        w = Workload(f"sweep_d{d}", 6, 1, 8, 8, 16384, d, True, "fwd", scaled_heads=True)
+        inp = workload_inputs(w, device="cuda:0")
+        q, k, v = inp["q"], inp["k"], inp["v"]
+        fl = workload_flops(w)["fwd"]
+        o = torch.empty_like(q)
+        lse = torch.empty((1, 8, 16384), dtype=torch.float32, device="cuda:0")
+        for tau in (0, 4, 8, 16):
+            for emu in (0, 1, 2, 4):
+                ea.set_tuning("tau", tau)
+                ea.set_tuning("exp_emulation", emu)
+                for _ in range(args.warmup):
+                    ea.fwd(q, k, v, causal=True, out=o, lse_out=lse)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                a.record()
+                for _ in range(args.steps):
+                    ea.fwd(q, k, v, causal=True, out=o, lse_out=lse)
+                b.record()
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / args.steps
+                print(json.dumps({"sweep": "tau_exp", "head_dim": d, "tau": tau, "exp_emulation": emu,
+                                  "fwd_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}),
+                      flush=True)
+    ea.set_tuning("tau", 8)
+    ea.set_tuning("exp_emulation", -1)
+    return 0
 
 
 def main() -> int:
@@ -123,6 +188,10 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--bwd-fused-dq", action="store_true",
                     help="time the fused backward (dQ atomics) instead of dK/dV + dQ kernels")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: forward throughput over tau in {0,4,8,16} x "
+                         "exp_emulation in {0,1,2,4} x d in {64,128,256} (B1 H8 S16384 causal, "
+                         "Q,K x3 on half the heads), one JSON line per setting")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a known-size kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -140,6 +209,8 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.sweep:
+        return sweep_tau_exp(torch, ea, args)
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -244,6 +315,37 @@ def main() -> int:
     if with_bwd and w.deterministic:
         assert ea.bwd_status(p, bws, varlen) == 0
 
+    # each public entry point as one ABI call (attn_fwd[_varlen]; attn_bwd[_varlen]
+    # = every backward launch), hipEvent-timed on the stream, median and min
+    def run_bwd_all():
+        st = stream()
+        if varlen:
+            r = lib.attn_bwd_varlen(ctypes.byref(p), cu_q.data_ptr(), cu_k.data_ptr(), q.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    bws.data_ptr(), bws.numel(), st)
+        else:
+            r = lib.attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             bws.data_ptr(), bws.numel(), st)
+        assert r == 0, r
+
+    def abi_times(fn, n):
+        ts = []
+        for _ in range(n):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4), "calls": n}
+
+    abi = {"attn_fwd" + ("_varlen" if varlen else ""): abi_times(run_fwd, 20)}
+    if with_bwd:
+        abi["attn_bwd" + ("_varlen" if varlen else "")] = abi_times(run_bwd_all, 20)
+
     total_flops = fl["fwd+bwd"] if with_bwd else fl["fwd"]
     value = total_flops / (ms * 1e-3) / 1e12
     # algorithmic flops per kernel: forward 2 GEMMs; the key-block backward kernel
@@ -277,7 +379,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
         "config": {"workload": _describe(w), "pass": w.passes,
                    "bwd_design": "fused dQ atomics" if fused else "dK/dV kernel + dQ kernel",
-                   "kernels": kernels,
+                   "kernels": kernels, "abi_ms": abi, "device": device_info(torch),
                    "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": dom_name,
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -13,7 +13,7 @@ Entry points mirror the C ABI in ``include/attn71.h``:
     bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
     bwd_phases(...)          the backward split into preprocess / main / postprocess
     tile_order(...)          the fixed-length tile schedule, evaluated on the host
-    set_tuning(key, value)   process-wide knobs ("tile_order", "exp_emulation", "spin_limit",
+    set_tuning(key, value)   process-wide knobs ("tile_order", "exp_emulation", "tau", "spin_limit",
                              "bwd_fused_dq"); get_tuning(key) reads back what was set
 """
 from __future__ import annotations
@@ -248,7 +248,7 @@ def tile_order(p: AttnParams, which: int):
     return [tuple(buf[3 * i:3 * i + 3]) for i in range(count.value)]
 
 
-_TUNING = {"tile_order": 0, "exp_emulation": 0, "spin_limit": 1 << 26, "bwd_fused_dq": 0,
+_TUNING = {"tile_order": 0, "exp_emulation": -1, "tau": 8, "spin_limit": 1 << 26, "bwd_fused_dq": 0,
            "fwd_pingpong": 0}
 
 

@@ -24,7 +24,8 @@ constexpr size_t kAlign = 256;
 
 struct Tuning {
   int tile_order = 0;
-  int exp_emulation = 0;
+  int exp_emulation = -1; // -1: automatic (2 of 8 at head_dim 256, else none; measured)
+  int tau = 8;            // rescale threshold (log2 units); the pages' log2(256)
   int spin_limit = 1 << 26;
   int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
   int fwd_pingpong = 0;   // 1: phase-offset wave groups (d <= 128); 0: one phase per tile
@@ -195,6 +196,7 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   fp.causal = p->causal;
   fp.alpha = p->softmax_scale;
   fp.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  fp.tau = static_cast<float>(g_tuning.tau);
   if (varlen) {
     char* base = static_cast<char*>(ws);
     int* order = reinterpret_cast<int*>(base + wl.order);
@@ -205,7 +207,10 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     fp.order = order;
     fp.tile_prefix = tp;
   }
-  if (launch_fwd(fp, d, fwd_grid(p, varlen), g_tuning.exp_emulation, g_tuning.fwd_pingpong != 0,
+  // the FMA-path exp2 pays off only where the forward runs one wave per SIMD
+  // (head_dim 256: +8 % measured); elsewhere v_exp_f32 alone is faster
+  const int emu = g_tuning.exp_emulation >= 0 ? g_tuning.exp_emulation : (d == 256 ? 2 : 0);
+  if (launch_fwd(fp, d, fwd_grid(p, varlen), emu, g_tuning.fwd_pingpong != 0,
                  stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -417,8 +422,12 @@ attn_status attn_set_tuning(const char* key, int32_t value) {
     if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.tile_order = value;
   } else if (!std::strcmp(key, "exp_emulation")) {
-    if (value != 0 && value != 2) return ATTN_ERR_INVALID_ARGUMENT;
+    if (value != -1 && value != 0 && value != 1 && value != 2 && value != 4)
+      return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.exp_emulation = value;
+  } else if (!std::strcmp(key, "tau")) {
+    if (value < 0 || value > 64) return ATTN_ERR_INVALID_ARGUMENT;
+    g_tuning.tau = value;
   } else if (!std::strcmp(key, "fwd_pingpong")) {
     if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.fwd_pingpong = value;

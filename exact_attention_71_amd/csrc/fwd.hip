@@ -250,7 +250,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
           for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kb][qb][i], s[kb][qb][i + 1]);
         mx = fmaxf(mx, xor32(mx));
         mnew[qb] = fmaxf(mref[qb], mx);
-        big = big || ((mnew[qb] - mref[qb]) * sl2 > kTau);
+        big = big || ((mnew[qb] - mref[qb]) * sl2 > p.tau);
       }
       if (wave_any(big)) {
 #pragma unroll
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
         for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kb][i], s[kb][i + 1]);
       mx = fmaxf(mx, xor32(mx));
       const float mnew = fmaxf(mref, mx);
-      if (wave_any((mnew - mref) * sl2 > kTau)) {
+      if (wave_any((mnew - mref) * sl2 > p.tau)) {
         const float fac = (mref == neg_inf()) ? 0.0f : fast_exp2((mref - mnew) * sl2);
         lsum *= fac;
 #pragma unroll
@@ -585,16 +585,19 @@ hipError_t launch_d(const FwdParams& p, int grid, bool pingpong, hipStream_t str
 
 }  // namespace
 
-// exp_emulation: 0 = all exp2 on v_exp_f32; 2 = 2 of every 8 on the FMA path.
-// pingpong: use the two-group phase-offset kernel where it exists (d <= 128).
+// exp_emulation: 0 = all exp2 on v_exp_f32; E = 1, 2, 4: E of every 8 on the
+// FMA path. pingpong: use the two-group phase-offset kernel where it exists
+// (d <= 128).
 hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, bool pingpong,
                       hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const bool emu = exp_emulation == 2;
-  switch (d) {
-    case 64: return emu ? launch_d<64, 2>(p, grid, pingpong, stream) : launch_d<64, 0>(p, grid, pingpong, stream);
-    case 128: return emu ? launch_d<128, 2>(p, grid, pingpong, stream) : launch_d<128, 0>(p, grid, pingpong, stream);
-    case 256: return emu ? launch_d<256, 2>(p, grid, pingpong, stream) : launch_d<256, 0>(p, grid, pingpong, stream);
+  switch (d * 8 + exp_emulation) {
+#define ATTN71_FWD_CASE(D, E) \
+    case D * 8 + E: return launch_d<D, E>(p, grid, pingpong, stream);
+    ATTN71_FWD_CASE(64, 0) ATTN71_FWD_CASE(64, 1) ATTN71_FWD_CASE(64, 2) ATTN71_FWD_CASE(64, 4)
+    ATTN71_FWD_CASE(128, 0) ATTN71_FWD_CASE(128, 1) ATTN71_FWD_CASE(128, 2) ATTN71_FWD_CASE(128, 4)
+    ATTN71_FWD_CASE(256, 0) ATTN71_FWD_CASE(256, 1) ATTN71_FWD_CASE(256, 2) ATTN71_FWD_CASE(256, 4)
+#undef ATTN71_FWD_CASE
     default: return hipErrorInvalidValue;
   }
 }

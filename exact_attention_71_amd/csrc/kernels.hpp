@@ -8,7 +8,7 @@ namespace attn71 {
 
 // Softmax rescale threshold in base-2 units: tau = log2(256) = 8.0
 // (FlashAttention-4 digest page, item 3; blog page, forward rescaling equation).
-constexpr float kTau = 8.0f;
+constexpr float kTau = 8.0f;   // default rescale threshold, log2 units (log2 256)
 
 struct SeqView {
   const int* cu_q;        // packed varlen offsets (device), null for fixed length
@@ -34,6 +34,7 @@ struct FwdParams {
   int causal;
   float alpha;            // softmax scale
   float scale_log2;       // alpha * log2(e)
+  float tau;              // rescale threshold on the running-max jump, log2 units
 };
 
 struct BwdParams {

@@ -178,9 +178,15 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
  *                   MI355X so far), 0 = one phase per key tile (default);
  *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
  *                   (batch-head major, blocks ascending, no remap);
- *   "exp_emulation" 0 = every exp2 on v_exp_f32 (default), 2 = 2 of every 8
- *                   on the Cody-Waite + Horner FMA path (blog page, faster
- *                   exponential section);
+ *   "exp_emulation" -1 = automatic (default: 2 at head_dim 256, where it
+ *                   measured faster, 0 otherwise); 0 = every exp2 on
+ *                   v_exp_f32; 1, 2 or 4 = that many of every 8 on the
+ *                   Cody-Waite + Horner FMA path (blog page, faster exponential
+ *                   section);
+ *   "tau"           forward rescale threshold on the running-max jump, in
+ *                   log2 units, 0..64 (default 8 = log2 256: digest page item
+ *                   3; blog page, forward section). 0 rescales on every
+ *                   increase of the row max;
  *   "spin_limit"    bound on each wait of the deterministic chain (default
  *                   2^26 polls).
  * Returns ATTN_ERR_INVALID_ARGUMENT for unknown keys or values. */

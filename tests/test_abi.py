@@ -118,12 +118,19 @@ def test_workspace_sizes():
 def test_tuning_knobs():
     ea.set_tuning("tile_order", 1)
     ea.set_tuning("tile_order", 0)
-    ea.set_tuning("exp_emulation", 2)
-    ea.set_tuning("exp_emulation", 0)
+    for e in (1, 2, 4, 0, -1):
+        ea.set_tuning("exp_emulation", e)
+    for t in (0, 64, 8):
+        ea.set_tuning("tau", t)
     with pytest.raises(ea.AttnError):
         ea.set_tuning("no_such_knob", 1)
-    with pytest.raises(ea.AttnError):
-        ea.set_tuning("exp_emulation", 3)
+    for bad in (3, 5, 8, -2):
+        with pytest.raises(ea.AttnError):
+            ea.set_tuning("exp_emulation", bad)
+    for bad in (-1, 65):
+        with pytest.raises(ea.AttnError):
+            ea.set_tuning("tau", bad)
+    assert ea.get_tuning("tau") == 8 and ea.get_tuning("exp_emulation") == -1
 
 
 # ------------------------------------------------------------------ tile order

@@ -198,18 +198,26 @@ def test_forward_independent_of_tile_order(bwd_mode):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_exp_emulation_variant_matches_oracle(bwd_mode):
-    inp = make_inputs(1, 512, 512, 2, 2, 128, seed=81, scaled_heads=True, with_grad=False)
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("emu,tau", [(2, 8), (1, 8), (4, 8), (0, 0), (0, 16), (4, 0)])
+def test_tau_and_exp_emulation_variants_match_oracle(d, emu, tau):
+    """The forward's knobs (FMA-path exp2 on emu of every 8 elements; rescale
+    threshold tau in log2 units) all reach the definition: the conditional
+    rescale and the polynomial change rounding, not the result."""
+    inp = make_inputs(1, 700, 700, 2, 2, d, seed=81 + d, scaled_heads=True, with_grad=False)
     g = _dev(inp)
-    ea.set_tuning("exp_emulation", 2)
+    ea.set_tuning("exp_emulation", emu)
+    ea.set_tuning("tau", tau)
     try:
         o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
     finally:
-        ea.set_tuning("exp_emulation", 0)
+        ea.set_tuning("exp_emulation", -1)
+        ea.set_tuning("tau", 8)
     torch.cuda.synchronize()
-    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], 1 / math.sqrt(128), True)
-    check_o(o, o_ref, "emu")
-    check_lse(lse, lse_ref, "emu")
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], 1 / math.sqrt(d), True)
+    e = check_o(o, o_ref, f"emu{emu} tau{tau} d{d}")
+    el = check_lse(lse, lse_ref, f"emu{emu} tau{tau} d{d}")
+    print(f"[tau/exp accuracy] d={d} emu={emu} tau={tau} O {e} LSE max-abs {el:.3e}")
 
 
 def test_gqa_equals_repeated_kv_on_gpu():
