@@ -21,9 +21,13 @@ elementwise P and dS):
     dV_j  =         sum_{h in group} sum_i P_ij dO_i
 
 Visibility: non-causal, every key of the same sequence; causal (lower
-triangular, query i sees key j iff j <= i), only with equal query and key
-lengths. Grouped heads: query head h reads KV head h // (Hq / Hkv). A query row
-that sees no key (an empty key sequence) gets O = 0 and LSE = -inf.
+triangular, query i sees key j iff j <= i; the pages only use equal query and
+key lengths). With Sq != Sk the diagonal is aligned to the last query and the
+last key (bottom-right): query i sees key j iff j <= i + Sk - Sq, so the last
+query sees every key, and with Sq > Sk the first Sq - Sk queries see none.
+Grouped heads: query head h reads KV head h // (Hq / Hkv). A query row that
+sees no key (an empty key sequence, or a row above a bottom-right diagonal)
+gets O = 0 and LSE = -inf, and its gradients are 0.
 
 Layouts: fixed length BSHD [B, S, H, d], LSE [B, Hq, Sq]; packed variable
 length THD [T, H, d] with cu_seqlens [n + 1], LSE [Hq, T].
@@ -48,10 +52,13 @@ def _f64(x) -> np.ndarray:
     return x.detach().to("cpu", torch.float64).numpy()
 
 
-def _visible(rows: np.ndarray, nk: int, causal: bool) -> Optional[np.ndarray]:
+def _visible(rows: np.ndarray, nk: int, causal: bool, nq: int) -> Optional[np.ndarray]:
+    """Causal mask for query rows ``rows`` of a sequence of ``nq`` queries and
+    ``nk`` keys: key j is visible iff j <= i + (nk - nq) (bottom-right aligned;
+    plain lower triangular when nq == nk)."""
     if not causal:
         return None
-    return np.arange(nk)[None, :] <= rows[:, None]
+    return np.arange(nk)[None, :] <= rows[:, None] + (nk - nq)
 
 
 def head_forward(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, causal: bool,
@@ -63,8 +70,6 @@ def head_forward(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, c
     """
     sq, d = qh.shape
     sk = kh.shape[0]
-    if causal and sq != sk:
-        raise ValueError("causal attention needs equal query and key lengths")
     rows = np.arange(sq) if rows is None else np.asarray(rows)
     o = np.zeros((rows.size, vh.shape[1]), dtype=np.float64)
     lse = np.full(rows.size, -np.inf, dtype=np.float64)
@@ -73,14 +78,20 @@ def head_forward(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, c
     for c0 in range(0, rows.size, _CHUNK):
         r = rows[c0:c0 + _CHUNK]
         s = scale * (qh[r] @ kh.T)
-        vis = _visible(r, sk, causal)
+        vis = _visible(r, sk, causal, sq)
         if vis is not None:
             s = np.where(vis, s, -np.inf)
+        # rows that see no key keep O = 0 and LSE = -inf
+        seen = vis.any(axis=1) if vis is not None else np.ones(r.size, dtype=bool)
+        if not seen.any():
+            continue
+        idx = np.nonzero(seen)[0]
+        s = s[idx]
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         l = e.sum(axis=1, keepdims=True)
-        o[c0:c0 + r.size] = (e @ vh) / l
-        lse[c0:c0 + r.size] = (m + np.log(l))[:, 0]
+        o[c0 + idx] = (e @ vh) / l
+        lse[c0 + idx] = (m + np.log(l))[:, 0]
     return o, lse
 
 
@@ -89,8 +100,9 @@ def head_probs(qh, kh, scale, causal, lse, rows=None) -> np.ndarray:
     sq = qh.shape[0]
     rows = np.arange(sq) if rows is None else np.asarray(rows)
     s = scale * (qh[rows] @ kh.T)
-    vis = _visible(rows, kh.shape[0], causal)
-    p = np.exp(s - lse[:, None])
+    vis = _visible(rows, kh.shape[0], causal, sq)
+    with np.errstate(over="ignore"):   # rows with LSE = -inf see no key: P = 0
+        p = np.exp(s - lse[:, None])
     if vis is not None:
         p = np.where(vis, p, 0.0)
     return p
@@ -139,13 +151,14 @@ def head_dkdv_cols(qh, kh, vh, doh, scale, causal, cols):
     needs LSE_i and D_i of every query row, then dK_j = alpha sum_i dS_ij q_i,
     dV_j = sum_i P_ij dO_i."""
     cols = np.asarray(cols)
-    sq = qh.shape[0]
+    sq, sk = qh.shape[0], kh.shape[0]
     o, lse = head_forward(qh, kh, vh, scale, causal)
     dd = np.sum(doh * o, axis=1)
     s = scale * (qh @ kh[cols].T)                          # [Sq, n]
-    p = np.exp(s - lse[:, None])
+    with np.errstate(over="ignore"):
+        p = np.exp(s - lse[:, None])
     if causal:
-        p = np.where(cols[None, :] <= np.arange(sq)[:, None], p, 0.0)
+        p = np.where(cols[None, :] <= np.arange(sq)[:, None] + (sk - sq), p, 0.0)
     ds = p * (doh @ vh[cols].T - dd[:, None])
     return scale * (ds.T @ qh), p.T @ doh
 

@@ -42,27 +42,30 @@ from .attention import _f64
 LOG2E = 1.0 / math.log(2.0)
 
 
-def _group_forward(qg, kh, vh, rows, scale, causal, block_n, tau, exp2, dt, round_p, stats):
-    """One decision group of query rows (absolute indices ``rows``)."""
+def _group_forward(qg, kh, vh, rows, scale, causal, block_n, tau, exp2, dt, round_p, stats,
+                   off=0):
+    """One decision group of query rows (absolute indices ``rows``); under the
+    causal mask row i sees keys j <= i + ``off``."""
     n_rows = rows.size
     sk = kh.shape[0]
     m_ref = np.full(n_rows, -np.inf, dtype=dt)
     l = np.zeros(n_rows, dtype=dt)
     acc = np.zeros((n_rows, vh.shape[1]), dtype=dt)
-    last_key = int(rows.max()) + 1 if causal else sk
+    last_key = max(0, int(rows.max()) + 1 + off) if causal else sk
     n_tiles = -(-min(last_key, sk) // block_n)
     c = dt(scale * LOG2E)
     for t in range(n_tiles):
         cols = np.arange(t * block_n, min(sk, (t + 1) * block_n))
         s = (qg @ kh[cols].T).astype(dt) * c                     # S_j in log2 units
         if causal:
-            s = np.where(cols[None, :] <= rows[:, None], s, dt(-np.inf))
+            s = np.where(cols[None, :] <= rows[:, None] + off, s, dt(-np.inf))
         m_new = np.maximum(m_ref, s.max(axis=1))                   # m_j
         with np.errstate(invalid="ignore"):
             jump = m_new - m_ref
         if np.any(jump > tau):                                     # one decision per group
-            fac = np.where(np.isneginf(m_ref), dt(0.0),
-                           exp2((np.where(np.isneginf(m_ref), m_new, m_ref) - m_new).astype(dt)))
+            with np.errstate(invalid="ignore"):                    # rows that saw no key yet
+                fac = np.where(np.isneginf(m_ref), dt(0.0),
+                               exp2((np.where(np.isneginf(m_ref), m_new, m_ref) - m_new).astype(dt)))
             acc = acc * fac[:, None].astype(dt)
             l = l * fac.astype(dt)
             m_ref = m_new
@@ -103,7 +106,7 @@ def blockwise_forward(q, k, v, scale: float, causal: bool, block_m: int = 128,
     stats.setdefault("skipped", 0)
     stats.setdefault("max_p", 0.0)
     bsz, sq, hq, d = q.shape
-    hkv = k.shape[2]
+    hkv, sk = k.shape[2], k.shape[1]
     grp = hq // hkv
     o = np.zeros(q.shape[:-1] + (v.shape[-1],))
     lse = np.full((bsz, hq, sq), -np.inf)
@@ -116,7 +119,7 @@ def blockwise_forward(q, k, v, scale: float, causal: bool, block_m: int = 128,
                 for r0 in range(m0, min(sq, m0 + block_m), group_rows):
                     rows = np.arange(r0, min(sq, r0 + group_rows, m0 + block_m))
                     og, lg = _group_forward(qh[rows], kh, vh, rows, scale, causal, block_n,
-                                            tau, exp2, dt, round_p, stats)
+                                            tau, exp2, dt, round_p, stats, off=sk - sq)
                     o[b, rows, h] = og
                     lse[b, h, rows] = lg
     return o, lse
