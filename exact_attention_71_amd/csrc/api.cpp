@@ -46,12 +46,7 @@ attn_status check_params(const attn_params* p, bool varlen) {
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.0f)) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARGUMENT;
-  if (varlen) {
-    if (p->total_q < 0 || p->total_k < 0) return ATTN_ERR_INVALID_ARGUMENT;
-    if (p->causal && p->total_q != p->total_k) return ATTN_ERR_INVALID_ARGUMENT;
-  } else if (p->causal && p->seqlen_q != p->seqlen_k) {
-    return ATTN_ERR_INVALID_ARGUMENT;
-  }
+  if (varlen && (p->total_q < 0 || p->total_k < 0)) return ATTN_ERR_INVALID_ARGUMENT;
   // one (sequence, head) slab must stay within 32-bit byte offsets
   const int64_t d = p->head_dim;
   const int64_t ext_q = (int64_t)p->seqlen_q * p->num_heads_q * d * 4;  // fp32 dQ accumulator

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t n_pai
       off = (b * p.hq + h) * p.sv.seqlen_q + s;
     }
     p.dsum[off] = acc;
-    p.lse2[off] = p.lse[off] * 1.4426950408889634f;
+    p.lse2[off] = lse_log2(p.lse[off]);
   }
 }
 
@@ -185,7 +185,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const float sl2 = p.scale_log2;
   const int nm = cdiv(lq, BM);
-  const int m_first = causal ? (n0 / BM) : 0;
+  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
+  const int m_first = causal ? causal_row_begin(n0, shift) / BM : 0;
   const int nlast_all = cdiv(lk, BN) - 1;   // last key block of this sequence
 
   // ---- K, V of this wave's keys as B operands; K^T of the block in LDS
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       const int r = m * BM + tid;
       if (r < lq) {
         const int64_t so = stat_off(p.sv, p.hq, t.seq, qs, hq, r);
-        lreg = p.lse[so] * 1.4426950408889634f;
+        lreg = lse_log2(p.lse[so]);
         dreg = p.dsum[so];
       } else {
         lreg = __builtin_inff();   // padding rows: P = 0
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       }
 
     // P = 2^(S alpha log2e - LSE log2e), dS = P (dP - D)
-    const bool need_mask = (n0 + BN > lk) || (causal && n0 + BN - 1 > mq0);
+    const bool need_mask = (n0 + BN > lk) || (causal && n0 + BN - 1 > mq0 + shift);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
           float pv = fast_exp2(__builtin_fmaf(s[qb][i], sl2, -l4[r]));
           if (need_mask) {
             const int qrow = mq0 + q4 + r;
-            if (mykey >= lk || (causal && mykey > qrow)) pv = 0.0f;
+            if (mykey >= lk || (causal && mykey > qrow + shift)) pv = 0.0f;
           }
           s[qb][i] = pv;
           dp[qb][i] = pv * (dp[qb][i] - d4[r]);
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     if (det) {
       const int64_t mb = p.sv.cu_q ? (int64_t)p.mb_prefix[t.seq] + m : (int64_t)t.seq * p.nm + m;
       semp = p.sem + mb * p.hq + hq;
-      const int nlast = causal ? imin(nlast_all, (mq0 + BM - 1) / BN) : nlast_all;
+      const int nlast = causal ? imin(nlast_all, (mq0 + BM - 1 + shift) / BN) : nlast_all;
       const int turn = nlast - t.block;
       if (tid == 0) {
         // bounded wait: once any wait has expired (status set) nobody waits again

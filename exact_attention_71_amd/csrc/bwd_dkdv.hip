@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const float sl2 = p.scale_log2;
   const int nm = cdiv(lq, BM);
-  const int m_first = causal ? imin(n0 / BM, nm) : 0;
+  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
+  const int m_first = causal ? imin(causal_row_begin(n0, shift) / BM, nm) : 0;
   const int per_head = nm - m_first;
   const int n_steps = p.group * per_head;
   const int wk0 = n0 + KPW * w;         // first key of this wave
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // One step for query block mq0. Masking (causal diagonal, key tail) sets
   // S = -inf in a branch of its own on the steps that need it: register i of a
   // tile is query row mq0 + 32 qb + 8 (i / 4) + 4 g + i % 4, so with
-  // rel = key - mq0 - 4g the pair is hidden iff rel > 32 qb + 8 (i / 4) + i % 4
+  // rel = key - shift - mq0 - 4g the pair is hidden iff rel > 32 qb + 8 (i / 4) + i % 4
   // (rel = INT_MAX for keys past the sequence, -1 where nothing is hidden).
   // Only S crosses that branch; a second copy of the whole body would split
   // the AGPR accumulators over two paths (the allocator answers with spills).
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = wk0 + 32 * kb + c;
-      rel[kb] = key >= lk ? 0x7fffffff : (causal ? key - mq0 - 4 * g : -1);
+      rel[kb] = key >= lk ? 0x7fffffff : (causal ? key - shift - mq0 - 4 * g : -1);
     }
     // Hand schedule (one wave per SIMD: nothing else hides this wave's VALU
     // work, and issue is in order). The step reads one stream of LDS operand
@@ -339,8 +340,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int mq0 = c_m * BM;
     if (++c_m == nm) c_m = m_first;
     // whole wave above the diagonal: no visible pair in this step
-    const bool active = !(causal && wk0 > mq0 + BM - 1);
-    const bool need_mask = (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0);
+    const bool active = !(causal && wk0 > mq0 + BM - 1 + shift);
+    const bool need_mask = (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
     if (active) step_body(mq0, need_mask);
     advance_slot(st);
     if (step + 1 < n_steps) wait_next(step + NS - 1 < n_steps);

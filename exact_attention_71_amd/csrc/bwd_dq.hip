@@ -71,7 +71,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   const int h = t.head;
   const int kvh = h / p.group;
   const bool causal = p.causal != 0;
-  const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
+  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
+  const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -162,7 +163,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
   // One key tile. Register i of an S^T tile is key k0 + 32 kb + 8 (i / 4) +
-  // 4 g + i % 4, so with lim = min(q, lk - 1) - k0 - 4g (q only when causal)
+  // 4 g + i % 4, so with lim = min(q + shift, lk - 1) - k0 - 4g (q + shift only
+  // when causal)
   // the pair is hidden iff 32 kb + 8 (i / 4) + i % 4 > lim. The operands come
   // as one stream of fragments PF ahead of use: NG1 of K (S^T), NG1 of V
   // (dP^T), NG2 of K^T (dQ^T).
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
         if (x == NG1 - 1) {
           // ---- P^T = 2^(S^T scale log2 e - LSE log2 e), dS^T = P^T o (dP^T - D)
           if (need_mask) {
-            const int lim = imin(causal ? myq : 0x7fffffff, lk - 1) - k0 - 4 * g;
+            const int lim = imin(causal ? myq + shift : 0x7fffffff, lk - 1) - k0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -237,8 +239,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
     if (n + NS - 1 < n_tiles) issue(n + NS - 1);
     const int k0 = n * BN;
     // whole wave below the diagonal's start: no visible pair in this tile
-    const bool active = !(causal && k0 > qw0 + 31);
-    const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+    const bool active = !(causal && k0 > qw0 + 31 + shift);
+    const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
     if (active) tile_body(k0, need_mask);
     advance_slot(st);
     if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);

@@ -178,6 +178,13 @@ __device__ __forceinline__ float emu_exp2(float x) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// LSE in log2 units for the backward's P = 2^(S alpha log2 e - LSE log2 e).
+// A row that saw no key has LSE = -inf; it maps to +inf so that every P of
+// the row is 2^-inf = 0, masked (S = -inf) or not, and never -inf + inf.
+__device__ __forceinline__ float lse_log2(float lse) {
+  return lse == neg_inf() ? __builtin_inff() : lse * 1.4426950408889634f;
+}
+
 // ---------------------------------------------------------------------------
 // Buffer resources: raw buffer loads return zero past `bytes`, which handles
 // ragged sequence tails without branches. Offsets are 32-bit byte offsets.

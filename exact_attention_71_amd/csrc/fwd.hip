@@ -92,7 +92,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
   const int h = t.head;
   const int kvh = h / p.group;
   const bool causal = p.causal != 0;
-  const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
+  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
+  const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
     const int st = n % NS;
     if (n + NS - 1 < n_tiles) issue(n + NS - 1);
     const int k0 = n * BN;
-    const bool active = !(causal && k0 > qw0 + 32 * QB - 1);
+    const bool active = !(causal && k0 > qw0 + 32 * QB - 1 + shift);
     if (active) {
       // S^T = K Q^T for this tile
       f32x16 s[NKB][QB];
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
         }
       }
       // mask the ragged key tail and the causal diagonal
-      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = k0 + kb * 32 + c_row(i, g);
-              const bool hide = key >= lk || (causal && key > qrow);
+              const bool hide = key >= lk || (causal && key > qrow + shift);
               s[kb][qb][i] = hide ? neg_inf() : s[kb][qb][i];
             }
           }
@@ -371,7 +372,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
   const int h = t.head;
   const int kvh = h / p.group;
   const bool causal = p.causal != 0;
-  const int n_tiles = causal ? cdiv(imin(m0 + BM, lq), BN) : cdiv(lk, BN);
+  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
+  const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -464,8 +466,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
     // ---------------- MFMA phase
     const bool more = it + 1 < n_tiles;
     if (more) load_stage(it + 1);
-    const bool act = it < n_tiles && !(causal && it * BN > qw0 + 31);
-    const bool act_prev = it >= 1 && !(causal && (it - 1) * BN > qw0 + 31);
+    const bool act = it < n_tiles && !(causal && it * BN > qw0 + 31 + shift);
+    const bool act_prev = it >= 1 && !(causal && (it - 1) * BN > qw0 + 31 + shift);
     if (act) {
       const int buf = it & 1;
 #pragma unroll
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
     // ---------------- VALU phase
     if (act) {
       const int k0 = it * BN;
-      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
       if (need_mask) {
         const int qrow = qw0 + c;
 #pragma unroll
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + kb * 32 + c_row(i, g);
-            const bool hide = key >= lk || (causal && key > qrow);
+            const bool hide = key >= lk || (causal && key > qrow + shift);
             s[kb][i] = hide ? neg_inf() : s[kb][i];
           }
       }

@@ -35,7 +35,18 @@ struct Tile {
 };
 
 A71_HD int imin(int a, int b) { return a < b ? a : b; }
+A71_HD int imax(int a, int b) { return a > b ? a : b; }
 A71_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Causal mask with the diagonal aligned to the last query and the last key:
+// query i of a sequence with lq queries and lk keys sees key j iff
+// j <= i + shift, shift = lk - lq (equal lengths: lower triangular).
+// Keys visible to any of the rows below row_end: [0, causal_key_end).
+A71_HD int causal_key_end(int row_end, int shift, int lk) {
+  return imax(0, imin(row_end + shift, lk));
+}
+// First query row that sees key n0 (rows before it see no key >= n0).
+A71_HD int causal_row_begin(int n0, int shift) { return imax(0, n0 - shift); }
 
 // Position of workgroup i among the contiguous ranges given to each XCD.
 // XCD x (receiving workgroups x, x + nx, x + 2nx, ...) owns positions

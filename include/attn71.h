@@ -27,9 +27,13 @@
  *   - Grouped heads: num_heads_q % num_heads_kv == 0 and query head h reads
  *     KV head h / (num_heads_q / num_heads_kv) (MQA: Hkv = 1, MHA: Hkv = Hq).
  *     dK, dV are summed over the query heads of each group.
- *   - causal: key j is visible to query i iff j <= i (lower triangular). It
- *     requires equal query and key lengths (per sequence for varlen: the
- *     caller passes cu_seqlens_k equal in content to cu_seqlens_q).
+ *   - causal: key j is visible to query i iff j <= i (lower triangular:
+ *     the causal masking of the digest page's LPT scheduling item). With
+ *     unequal lengths (per sequence for varlen) the diagonal is aligned to
+ *     the last query and last key: j <= i + (Lk - Lq). The pages show only
+ *     the square case; this alignment is the reading taken (a query block
+ *     appended to a key cache). With Lq > Lk the first Lq - Lk queries see
+ *     no key: O = 0, LSE = -inf, dQ = 0.
  *   - softmax_scale (alpha) is finite and > 0, typically 1/sqrt(head_dim).
  *   - head_dim is 64, 128 or 256; the device must be gfx950.
  *

@@ -56,7 +56,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
     (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=32), UNSUPPORTED),
     (dict(heads_q=3, heads_kv=2), INVALID), (dict(heads_kv=0), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=-1.0), INVALID),
-    (dict(causal=True, seqlen_k=299), INVALID), (dict(batch=-1), INVALID),
+    (dict(seqlen_k=-1), INVALID), (dict(batch=-1), INVALID),
     (dict(seqlen_q=1 << 24, heads_q=64, heads_kv=64), UNSUPPORTED),
 ])
 def test_forward_rejects_bad_parameters(kw, status):
@@ -66,6 +66,17 @@ def test_forward_rejects_bad_parameters(kw, status):
     assert st == status
     st = lib.attn_bwd(ctypes.byref(p), *([FAKE] * 9), FAKE, 1 << 30, None)
     assert st == status
+
+
+def test_causal_with_unequal_lengths_passes_validation():
+    """Causal with Sq != Sk (bottom-right diagonal) is accepted: with a null
+    q pointer the call must fail on the pointer, not on the shape."""
+    lib = ea.load()
+    for sq, sk in ((300, 299), (17, 4096), (4096, 17)):
+        p = _p(causal=True, seqlen_q=sq, seqlen_k=sk)
+        assert lib.attn_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+        assert lib.attn_fwd_workspace_size(ctypes.byref(p), 0) == 0
+        assert 0 < lib.attn_bwd_workspace_size(ctypes.byref(p), 0) < (1 << 40)
 
 
 def test_forward_rejects_null_and_misaligned_pointers():
