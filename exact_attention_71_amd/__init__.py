@@ -13,8 +13,9 @@ Entry points mirror the C ABI in ``include/attn71.h``:
     bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
     bwd_phases(...)          the backward split into preprocess / main / postprocess
     tile_order(...)          the fixed-length tile schedule, evaluated on the host
-    set_tuning(key, value)   process-wide knobs ("tile_order", "exp_emulation", "tau", "spin_limit",
-                             "bwd_fused_dq"); get_tuning(key) reads back what was set
+    set_tuning(key, value)   process-wide knobs ("tile_order", "persistent", "exp_emulation",
+                             "tau", "spin_limit", "bwd_fused_dq", "fwd_pingpong");
+                             get_tuning(key) reads back what was set
 """
 from __future__ import annotations
 
@@ -54,6 +55,7 @@ _vp = ctypes.c_void_p
 EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
+           "attn_persistent_tile",
            "attn_set_tuning"]
 
 
@@ -79,6 +81,8 @@ def _lib():
     lib.attn_tile_order.argtypes = [_P, ctypes.c_int32, _vp, ctypes.c_int64,
                                     ctypes.POINTER(ctypes.c_int64)]
     lib.attn_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_int32]
+    lib.attn_persistent_tile.argtypes = [ctypes.c_int32] * 5
+    lib.attn_persistent_tile.restype = ctypes.c_int32
     for n in EXPORTS:
         if n not in ("attn_status_string", "attn_version", "attn_fwd_workspace_size",
                      "attn_bwd_workspace_size"):
@@ -248,8 +252,13 @@ def tile_order(p: AttnParams, which: int):
     return [tuple(buf[3 * i:3 * i + 3]) for i in range(count.value)]
 
 
-_TUNING = {"tile_order": 0, "exp_emulation": -1, "tau": 8, "spin_limit": 1 << 26, "bwd_fused_dq": 0,
-           "fwd_pingpong": 0}
+def persistent_tile(g: int, r: int, grid: int, ntiles: int, nx: int = 8) -> int:
+    """Tile position taken by persistent workgroup g in round r (-1: none)."""
+    return int(_lib().attn_persistent_tile(g, r, grid, ntiles, nx))
+
+
+_TUNING = {"tile_order": 0, "persistent": 1, "exp_emulation": -1, "tau": 8,
+           "spin_limit": 1 << 26, "bwd_fused_dq": 0, "fwd_pingpong": 0}
 
 
 def set_tuning(key: str, value: int) -> None:

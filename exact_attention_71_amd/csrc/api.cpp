@@ -29,6 +29,7 @@ struct Tuning {
   int spin_limit = 1 << 26;
   int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
   int fwd_pingpong = 0;   // 1: phase-offset wave groups (d <= 128); 0: one phase per tile
+  int persistent = 1;     // 1: resident workgroups loop over the tiles; 0: one per tile
 };
 Tuning g_tuning;
 
@@ -135,6 +136,7 @@ int bwd_grid(const attn_params* p, bool varlen, bool fused) {
 // ----------------------------------------------------------------- device
 std::mutex g_dev_mu;
 int g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[64]; // compute units per device
 
 attn_status check_device() {
   int dev = 0;
@@ -145,8 +147,19 @@ attn_status check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_HIP;
     g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev] = prop.multiProcessorCount;
   }
   return g_dev_ok[dev] == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+}
+
+// CU count for persistent launches of the current device (after
+// check_device), or 0 when the knob asks for one workgroup per tile.
+int launch_cus() {
+  if (!g_tuning.persistent) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  return g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 0;
 }
 
 SeqView make_sv(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k) {
@@ -188,6 +201,7 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   fp.sec = section_width(2ll * p->seqlen_k * d * 2);
   fp.nxcd = kNxcd;
   fp.natural = g_tuning.tile_order;
+  fp.ntiles = fwd_grid(p, varlen);
   fp.causal = p->causal;
   fp.alpha = p->softmax_scale;
   fp.scale_log2 = p->softmax_scale * 1.4426950408889634f;
@@ -205,8 +219,7 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   // the FMA-path exp2 pays off only where the forward runs one wave per SIMD
   // (head_dim 256: +8 % measured); elsewhere v_exp_f32 alone is faster
   const int emu = g_tuning.exp_emulation >= 0 ? g_tuning.exp_emulation : (d == 256 ? 2 : 0);
-  if (launch_fwd(fp, d, fwd_grid(p, varlen), emu, g_tuning.fwd_pingpong != 0,
-                 stream) != hipSuccess)
+  if (launch_fwd(fp, d, launch_cus(), emu, g_tuning.fwd_pingpong != 0, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -259,6 +272,8 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.sec = section_width(2ll * bp.group * p->seqlen_q * d * 2);
   bp.nxcd = kNxcd;
   bp.natural = g_tuning.tile_order;
+  bp.ntiles = bwd_grid(p, varlen, fused);
+  bp.ntiles_dq = dq_grid(p, varlen);
   bp.causal = p->causal;
   bp.deterministic = p->deterministic;
   bp.alpha = p->softmax_scale;
@@ -291,11 +306,11 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (main) {
-    const hipError_t e = fused ? launch_bwd_main(bp, d, bwd_grid(p, varlen, true), true, stream)
-                               : launch_bwd_dkdv(bp, d, bwd_grid(p, varlen, false), stream);
+    const hipError_t e = fused ? launch_bwd_main(bp, d, bp.ntiles, true, stream)
+                               : launch_bwd_dkdv(bp, d, launch_cus(), stream);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
-  if (dqk && launch_bwd_dq(bp, d, dq_grid(p, varlen), stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (dqk && launch_bwd_dq(bp, d, launch_cus(), stream) != hipSuccess) return ATTN_ERR_HIP;
   if (post && launch_bwd_post(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -411,11 +426,20 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
   return ATTN_OK;
 }
 
+int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles, int32_t nx) {
+  if (g < 0 || g >= grid || r < 0 || ntiles < 0 || nx < 1 || grid < (ntiles < nx ? ntiles : nx))
+    return -1;
+  return persistent_index(g, r, grid, ntiles, nx);
+}
+
 attn_status attn_set_tuning(const char* key, int32_t value) {
   if (!key) return ATTN_ERR_INVALID_ARGUMENT;
   if (!std::strcmp(key, "tile_order")) {
     if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.tile_order = value;
+  } else if (!std::strcmp(key, "persistent")) {
+    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
+    g_tuning.persistent = value;
   } else if (!std::strcmp(key, "exp_emulation")) {
     if (value != -1 && value != 0 && value != 1 && value != 2 && value != 4)
       return ATTN_ERR_INVALID_ARGUMENT;

@@ -28,8 +28,13 @@ namespace attn71 {
 
 namespace {
 
+// LDS of one workgroup: [NS] Q tiles | [NS] dO tiles | [NS][LSE BM | D BM] fp32
+template <int D, int BM>
+constexpr int dkdv_smem_bytes() { return 2 * 3 * BM * 2 * D + 3 * 2 * BM * 4; }
+
+// One tile: the keys of key block t.block of (sequence t.seq, KV head t.head).
 template <int D, int KB, int BM>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, char* smem) {
   constexpr int NW = 4, NT = NW * 64;
   constexpr int KPW = 32 * KB;          // keys per wave
   constexpr int BN = NW * KPW;          // keys per workgroup
@@ -46,21 +51,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   static_assert(TILE % (16 * NT) == 0 && NLD <= NW, "tile split over the workgroup");
   constexpr int OPS = 2 * CH;           // dma per step by waves >= NLD (one more below)
   static_assert(OPS + 1 < 64, "vmcnt range");
-  // [NS] Q tiles | [NS] dO tiles | [NS][LSE BM | D BM] fp32
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE + NS * 2 * BM * 4];
+  static_assert(dkdv_smem_bytes<D, BM>() == 2 * NS * TILE + NS * 2 * BM * 4, "LDS layout");
   char* const qtile = smem;
   char* const otile = smem + NS * TILE;
   float* const lsed = reinterpret_cast<float*>(smem + 2 * NS * TILE);
   static_assert(BN == DkdvCfg<D>::BN && BM == DkdvCfg<D>::BM, "host and kernel tiling agree");
 
-  Tile t;
-  if (p.sv.cu_q) {
-    t = varlen_tile(blockIdx.x, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/false);
-    if (t.seq < 0) return;
-  } else {
-    if ((int)blockIdx.x >= p.sv.batch * p.hkv * p.nn) return;
-    t = bwd_tile_fixed(blockIdx.x, p.sv.batch, p.hkv, p.nn, p.sec, false, p.nxcd, p.natural != 0);
-  }
   int64_t qs, ks0;
   int lq, lk;
   if (p.sv.cu_q) {
@@ -74,7 +70,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int n0 = t.block * BN;
   if (n0 >= lk) return;
 
-  const int tid = threadIdx.x;
+  const int tid = tile_tid();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const bool causal = p.causal != 0;
@@ -375,21 +371,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// Persistent workgroups walk the tiles (schedule.hpp: persistent_index); a
+// one-shot grid (gridDim.x == ntiles) gives each workgroup one tile.
+template <int D, int KB, int BM>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
+  __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM>()];
+  for (int r = 0;; ++r) {
+    const BwdParams& p = kernel_args<BwdParams>();
+    const int i = persistent_index(blockIdx.x, r, gridDim.x, p.ntiles, p.nxcd);
+    if (i < 0) break;
+    Tile t;
+    if (p.sv.cu_q) {
+      t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/false);
+      if (t.seq < 0) break;
+    } else {
+      t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, false, p.nxcd, p.natural != 0);
+    }
+    dkdv_tile<D, KB, BM>(p, t, smem);
+    __syncthreads();   // the next tile's loads reuse the ring slots
+  }
+}
+
 template <int D>
-hipError_t launch_dkdv_d(const BwdParams& p, int grid, hipStream_t stream) {
+hipError_t launch_dkdv_d(const BwdParams& p, int cus, hipStream_t stream) {
   using C = DkdvCfg<D>;
+  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM>, 256);
+  const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int grid, hipStream_t stream) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int cus, hipStream_t stream) {
+  if (p.ntiles <= 0) return hipSuccess;
   switch (d) {
-    case 64: return launch_dkdv_d<64>(p, grid, stream);
-    case 128: return launch_dkdv_d<128>(p, grid, stream);
-    case 256: return launch_dkdv_d<256>(p, grid, stream);
+    case 64: return launch_dkdv_d<64>(p, cus, stream);
+    case 128: return launch_dkdv_d<128>(p, cus, stream);
+    case 256: return launch_dkdv_d<256>(p, cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,8 +26,13 @@ namespace attn71 {
 
 namespace {
 
+// LDS of one workgroup: [NS] K tiles | [NS] V tiles
+template <int D, int BN>
+constexpr int dq_smem_bytes() { return 2 * 3 * BN * 2 * D; }
+
+// One tile: query block t.block of (sequence t.seq, query head t.head).
 template <int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char* smem) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;            // k-steps of S^T and dP^T
@@ -43,19 +48,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int OPS = 2 * CH;           // ring loads per thread per tile (K and V)
   static_assert(OPS < 64, "vmcnt range");
   static_assert(BM == DqCfg<D>::BM && BN == DqCfg<D>::BN, "host and kernel tiling agree");
-  // [NS] K tiles | [NS] V tiles
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];
+  static_assert(dq_smem_bytes<D, BN>() == 2 * NS * TILE, "LDS layout");
   const uint32_t lds_k = lds_addr(smem);
   constexpr int VT = NS * TILE;         // V tile offset from the K tile
 
-  Tile t;
-  if (p.sv.cu_q) {
-    t = varlen_tile(blockIdx.x, p.order_dq, p.tile_prefix_dq, p.sv.batch, p.hq, true);
-    if (t.seq < 0) return;
-  } else {
-    if ((int)blockIdx.x >= p.sv.batch * p.hq * p.nm_dq) return;
-    t = fwd_tile_fixed(blockIdx.x, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
-  }
   int64_t qs, ks0;
   int lq, lk;
   if (p.sv.cu_q) {
@@ -74,7 +70,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
   const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
 
-  const int tid = threadIdx.x;
+  const int tid = tile_tid();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int qw0 = m0 + w * 32;
@@ -261,21 +257,43 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// Persistent workgroups walk the query blocks (schedule.hpp: persistent_index).
+template <int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams) {
+  __shared__ __attribute__((aligned(1024))) char smem[dq_smem_bytes<D, BN>()];
+  for (int r = 0;; ++r) {
+    const BwdParams& p = kernel_args<BwdParams>();
+    const int i = persistent_index(blockIdx.x, r, gridDim.x, p.ntiles_dq, p.nxcd);
+    if (i < 0) break;
+    Tile t;
+    if (p.sv.cu_q) {
+      t = varlen_tile(i, p.order_dq, p.tile_prefix_dq, p.sv.batch, p.hq, true);
+      if (t.seq < 0) break;
+    } else {
+      t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
+    }
+    dq_tile<D, NW, BN>(p, t, smem);
+    __syncthreads();   // the next tile's loads reuse the ring slots
+  }
+}
+
 template <int D>
-hipError_t launch_dq_d(const BwdParams& p, int grid, hipStream_t stream) {
+hipError_t launch_dq_d(const BwdParams& p, int cus, hipStream_t stream) {
   using C = DqCfg<D>;
+  static const int occ = resident_per_cu(bwd_dq_kernel<D, C::NW, C::BN>, C::NW * 64);
+  const int grid = persistent_grid(p.ntiles_dq, cus * occ, p.nxcd);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C::NW, C::BN>), dim3(grid), dim3(C::NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dq(const BwdParams& p, int d, int grid, hipStream_t stream) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_bwd_dq(const BwdParams& p, int d, int cus, hipStream_t stream) {
+  if (p.ntiles_dq <= 0) return hipSuccess;
   switch (d) {
-    case 64: return launch_dq_d<64>(p, grid, stream);
-    case 128: return launch_dq_d<128>(p, grid, stream);
-    case 256: return launch_dq_d<256>(p, grid, stream);
+    case 64: return launch_dq_d<64>(p, cus, stream);
+    case 128: return launch_dq_d<128>(p, cus, stream);
+    case 256: return launch_dq_d<256>(p, cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

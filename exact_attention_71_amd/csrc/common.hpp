@@ -178,6 +178,32 @@ __device__ __forceinline__ float emu_exp2(float x) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// The kernel's argument block (the only explicit argument, at offset 0 of the
+// kernel argument segment), read through a pointer the compiler cannot see
+// through. Called once per iteration of a persistent loop, it keeps the
+// argument loads (scalar loads from constant memory) inside the iteration
+// instead of hoisting them all in front of the loop, where they would stay
+// live in SGPRs for the whole kernel and spill.
+template <typename P>
+__device__ __forceinline__ const P& kernel_args() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  auto a = __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(a));
+  return *(const P*)(const __attribute__((address_space(4))) P*)a;
+#else
+  return *static_cast<const P*>(nullptr);   // host pass: never executed
+#endif
+}
+
+// threadIdx.x through an opaque copy: values derived from it inside a
+// persistent loop's tile body are then recomputed per tile rather than
+// hoisted in front of the loop and kept live (in VGPRs) across all tiles.
+__device__ __forceinline__ int tile_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // LSE in log2 units for the backward's P = 2^(S alpha log2 e - LSE log2 e).
 // A row that saw no key has LSE = -inf; it maps to +inf so that every P of
 // the row is 2^-inf = 0, masked (S = -inf) or not, and never -inf + inf.

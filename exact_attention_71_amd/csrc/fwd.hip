@@ -55,8 +55,15 @@ __device__ __forceinline__ void seq_bounds(const SeqView& sv, int seq, int64_t* 
   }
 }
 
+// LDS of one workgroup: [NS] K tiles | [NS] V tiles (three-deep ring when it fits)
+template <int D, int BN>
+constexpr int fwd_ring_depth() { return (3 * 2 * BN * 2 * D <= 160 * 1024) ? 3 : 2; }
+template <int D, int BN>
+constexpr int fwd_smem_bytes() { return 2 * fwd_ring_depth<D, BN>() * BN * 2 * D; }
+
+// One tile: query block t.block of (sequence t.seq, query head t.head).
 template <int D, int NW, int QB, int BN, int EMU>
-__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char* smem) {
   constexpr int NT = NW * 64;           // threads
   constexpr int BM = NW * 32 * QB;
   constexpr int KS = D / 16;            // MFMA k-steps over the head dim
@@ -65,25 +72,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
   constexpr int RB = 2 * D;             // bytes per K / V row in LDS
   constexpr int SPR = D / 8;            // 16-byte slots per row
   constexpr int TILE = BN * RB;         // bytes of one K (or V) tile
-  constexpr int NS = (3 * 2 * TILE <= 160 * 1024) ? 3 : 2;   // ring depth
+  constexpr int NS = fwd_ring_depth<D, BN>();   // ring depth
   constexpr int CH = TILE / (16 * NT);  // dma16 per thread per tile
   static_assert(CH * 16 * NT == TILE, "tile split over the workgroup");
   constexpr int OPS = 2 * CH;           // ring loads per thread per tile (K and V)
   static_assert(OPS < 64, "vmcnt range");
-  // [NS] K tiles | [NS] V tiles
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];
+  static_assert(fwd_smem_bytes<D, BN>() == 2 * NS * TILE, "LDS layout");
   const uint32_t lds_k = lds_addr(smem);
   constexpr int VT = NS * TILE;         // V tile offset from the K tile
 
-  // ---- which tile
-  Tile t;
-  if (p.sv.cu_q) {
-    t = varlen_tile(blockIdx.x, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
-    if (t.seq < 0) return;
-  } else {
-    if ((int)blockIdx.x >= p.sv.batch * p.hq * p.nm) return;
-    t = fwd_tile_fixed(blockIdx.x, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
-  }
   int64_t qs, ks0;
   int lq, lk;
   seq_bounds(p.sv, t.seq, &qs, &lq, &ks0, &lk);
@@ -95,7 +92,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
   const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
   const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
 
-  const int tid = threadIdx.x;
+  const int tid = tile_tid();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int qw0 = m0 + w * 32 * QB;     // first query row of this wave
@@ -325,6 +322,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams p) {
         p.lse[off] = val;
       }
     }
+  }
+}
+
+// Persistent workgroups walk the query blocks (schedule.hpp: persistent_index).
+template <int D, int NW, int QB, int BN, int EMU>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
+  __shared__ __attribute__((aligned(1024))) char smem[fwd_smem_bytes<D, BN>()];
+  for (int r = 0;; ++r) {
+    const FwdParams& p = kernel_args<FwdParams>();
+    const int i = persistent_index(blockIdx.x, r, gridDim.x, p.ntiles, p.nxcd);
+    if (i < 0) break;
+    Tile t;
+    if (p.sv.cu_q) {
+      t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
+      if (t.seq < 0) break;
+    } else {
+      t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
+    }
+    fwd_tile<D, NW, QB, BN, EMU>(p, t, smem);
+    __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }
 
@@ -572,14 +589,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
 }
 
 template <int D, int EMU>
-hipError_t launch_d(const FwdParams& p, int grid, bool pingpong, hipStream_t stream) {
+hipError_t launch_d(const FwdParams& p, int cus, bool pingpong, hipStream_t stream) {
   using C = FwdCfg<D>;
   if constexpr (C::NW == 8 && C::QB == 1) {
-    if (pingpong) {
-      hipLaunchKernelGGL((fwd_pp_kernel<D, C::BN, EMU>), dim3(grid), dim3(512), 0, stream, p);
+    if (pingpong) {   // one workgroup per tile
+      hipLaunchKernelGGL((fwd_pp_kernel<D, C::BN, EMU>), dim3(p.ntiles), dim3(512), 0, stream, p);
       return hipGetLastError();
     }
   }
+  static const int occ = resident_per_cu(fwd_kernel<D, C::NW, C::QB, C::BN, EMU>, C::NW * 64);
+  const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
   hipLaunchKernelGGL((fwd_kernel<D, C::NW, C::QB, C::BN, EMU>), dim3(grid), dim3(C::NW * 64), 0,
                      stream, p);
   return hipGetLastError();
@@ -590,12 +609,12 @@ hipError_t launch_d(const FwdParams& p, int grid, bool pingpong, hipStream_t str
 // exp_emulation: 0 = all exp2 on v_exp_f32; E = 1, 2, 4: E of every 8 on the
 // FMA path. pingpong: use the two-group phase-offset kernel where it exists
 // (d <= 128).
-hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, bool pingpong,
+hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, bool pingpong,
                       hipStream_t stream) {
-  if (grid <= 0) return hipSuccess;
+  if (p.ntiles <= 0) return hipSuccess;
   switch (d * 8 + exp_emulation) {
 #define ATTN71_FWD_CASE(D, E) \
-    case D * 8 + E: return launch_d<D, E>(p, grid, pingpong, stream);
+    case D * 8 + E: return launch_d<D, E>(p, cus, pingpong, stream);
     ATTN71_FWD_CASE(64, 0) ATTN71_FWD_CASE(64, 1) ATTN71_FWD_CASE(64, 2) ATTN71_FWD_CASE(64, 4)
     ATTN71_FWD_CASE(128, 0) ATTN71_FWD_CASE(128, 1) ATTN71_FWD_CASE(128, 2) ATTN71_FWD_CASE(128, 4)
     ATTN71_FWD_CASE(256, 0) ATTN71_FWD_CASE(256, 1) ATTN71_FWD_CASE(256, 2) ATTN71_FWD_CASE(256, 4)

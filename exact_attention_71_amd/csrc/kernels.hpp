@@ -31,6 +31,7 @@ struct FwdParams {
   int nm;                 // fixed: query blocks per sequence
   int sec, nxcd;
   int natural;            // 1: plain tile order (tuning / ablation)
+  int ntiles;             // tiles of the launch (varlen: upper bound)
   int causal;
   float alpha;            // softmax scale
   float scale_log2;       // alpha * log2(e)
@@ -62,6 +63,8 @@ struct BwdParams {
   int nm;                 // fixed: query blocks per sequence
   int sec, nxcd;
   int natural;            // 1: plain tile order (non-deterministic only)
+  int ntiles;             // dK/dV (or fused) tiles of the launch (varlen: upper bound)
+  int ntiles_dq;          // dQ kernel tiles (varlen: upper bound)
   int causal, deterministic;
   float alpha;
   float scale_log2;
@@ -116,16 +119,35 @@ inline int fwd_block_m(int d) {
 inline int bwd_block_n(int) { return 128; }
 inline int bwd_block_m(int d) { return d <= 128 ? 64 : 32; }
 
-hipError_t launch_fwd(const FwdParams& p, int d, int grid, int exp_emulation, bool pingpong,
+// Workgroups of `kernel` (block of `threads`) that fit on one CU at once.
+template <typename K>
+int resident_per_cu(K kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+// Grid of a persistent launch over `ntiles` tiles: every resident slot
+// (resident <= 0: a one-shot grid of ntiles), never fewer than min(ntiles, nx)
+// so that every XCD residue class of tiles has a workgroup.
+inline int persistent_grid(int ntiles, int resident, int nx) {
+  if (resident <= 0 || resident >= ntiles) return ntiles;
+  const int lo = ntiles < nx ? ntiles : nx;
+  return resident < lo ? lo : resident;
+}
+
+// Launchers. `cus` is the device's CU count for persistent launches, or 0 for
+// a one-shot grid of one workgroup per tile (p.ntiles).
+hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, bool pingpong,
                       hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 // fused = true: dQ accumulated with fp32 atomics (or the deterministic
 // semaphore chain) inside the dK/dV kernel; false: dK/dV only.
 hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream);
 // dK, dV only: one workgroup per DkdvCfg<d>::BN keys (see bwd_dkdv.hip).
-hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int grid, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int cus, hipStream_t stream);
 // dQ without atomics: one workgroup per query block (see bwd_dq.hip).
-hipError_t launch_bwd_dq(const BwdParams& p, int d, int grid, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, int cus, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
 // Varlen pre-pass: order[] = sequences by decreasing length of key_cu (ties
 // by index), tile_prefix[vs] = first tile of virtual sequence vs with

@@ -58,6 +58,30 @@ A71_HD int xcd_remap(int i, int n, int nx) {
   return x * q + imin(x, r) + j;
 }
 
+// Persistent workgroups. Dispatch hands workgroups to the XCDs round-robin
+// and, inside an XCD, to its shader engines in turn. With a one-shot grid of
+// unequal causal tiles that leaves CUs idle: in a timeline of the dK/dV kernel
+// at B2 H16 S8192 (one workgroup per CU), later workgroups started in groups
+// of four, one per shader engine, each group only once every engine had a
+// free CU, so a CU sat idle ~20 us on average before each new tile. Instead G workgroups,
+// as many as can be resident, loop over the n tiles of the schedule order in
+// rounds. Workgroup g stays on XCD x = g % nx as the j-th of its J_x
+// workgroups; in round r it takes the tile that workgroup x + nx * p of a
+// one-shot grid would take, with p = r * J_x + j in even rounds and
+// r * J_x + (J_x - 1 - j) in odd rounds. Going back and forth pairs the
+// longest tiles of one round with the shortest of the next, and every tile
+// keeps the XCD (and L2) it has in the one-shot grid. With G = n this is
+// exactly the one-shot grid. Requires G >= min(n, nx) so that every residue
+// class of tiles has a workgroup. Returns -1 past the last tile.
+A71_HD int persistent_index(int g, int r, int G, int n, int nx) {
+  if (nx < 1) nx = 1;
+  const int x = g % nx, j = g / nx;
+  const int J = (G - x + nx - 1) / nx;
+  const int64_t pos = (int64_t)r * J + ((r & 1) ? (J - 1 - j) : j);
+  const int64_t i = x + (int64_t)nx * pos;
+  return i < n ? (int)i : -1;
+}
+
 // Section order over a regular grid of nbh batch-heads x nblk blocks:
 // sections of `sec` batch-heads; inside a section blocks are visited from
 // `first` in the direction given by `reverse`, batch-heads innermost.

@@ -174,6 +174,14 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* wo
 attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,
                             int64_t* count);
 
+/* Persistent launches (forward, dK/dV and dQ kernels): `grid` workgroups, as
+ * many as fit on the device at once, loop over the `ntiles` positions of the
+ * tile order above. Returns the position that workgroup g takes in round r,
+ * or -1 when it has no more (host evaluation of the kernels' arithmetic:
+ * workgroup g stays on XCD g % nx; rounds alternate direction). Requires
+ * grid >= min(ntiles, nx). No GPU is needed. */
+int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles, int32_t nx);
+
 /* Process-wide tuning knobs (not synchronised with launches in flight):
  *   "bwd_fused_dq"  0 = dK/dV kernel + dQ kernel (default), 1 = one kernel with
  *                   dQ atomics / semaphore-ordered adds (see attn_bwd);
@@ -182,6 +190,8 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
  *                   MI355X so far), 0 = one phase per key tile (default);
  *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
  *                   (batch-head major, blocks ascending, no remap);
+ *   "persistent"    1 = resident workgroups loop over the tiles (default),
+ *                   0 = one workgroup per tile;
  *   "exp_emulation" -1 = automatic (default: 2 at head_dim 256, where it
  *                   measured faster, 0 otherwise); 0 = every exp2 on
  *                   v_exp_f32; 1, 2 or 4 = that many of every 8 on the

@@ -202,3 +202,56 @@ def test_natural_tile_order_knob():
     finally:
         ea.set_tuning("tile_order", 0)
     assert nat == [(0, h, m) for h in range(2) for m in range(4)]
+
+
+@pytest.mark.parametrize("n,grid,nx", [(1024, 256, 8), (1000, 256, 8), (300, 256, 8), (7, 7, 8),
+                                       (5000, 250, 8), (64, 13, 8), (100, 8, 8), (9, 3, 1),
+                                       (2048, 512, 8), (33, 10, 4)])
+def test_persistent_schedule_covers_every_tile_once(n, grid, nx):
+    """Every tile position is taken by exactly one (workgroup, round), and a
+    workgroup only takes positions of its own XCD residue class."""
+    seen = []
+    for g in range(grid):
+        r = 0
+        while True:
+            i = ea.persistent_tile(g, r, grid, n, nx)
+            if i < 0:
+                break
+            assert i % nx == g % nx
+            seen.append(i)
+            r += 1
+    assert sorted(seen) == list(range(n))
+
+
+def test_persistent_schedule_with_one_workgroup_per_tile_is_the_one_shot_grid():
+    for n in (1, 8, 100, 1024):
+        for g in range(n):
+            assert ea.persistent_tile(g, 0, n, n, 8) == g
+            assert ea.persistent_tile(g, 1, n, n, 8) == -1
+    assert ea.persistent_tile(0, 0, 3, 100, 8) == -1      # fewer workgroups than XCDs: refused
+
+
+def test_persistent_schedule_balances_causal_key_blocks():
+    """B2 H16 S8192 d128 causal, dK/dV: key block n walks 256 - 8n query steps.
+    256 resident workgroups get equal totals (the one-shot grid of 1024 would
+    need every CU to pick the right successor at the right time)."""
+    p = _p(batch=2, seqlen_q=8192, seqlen_k=8192, heads_q=16, heads_kv=16, head_dim=128,
+           causal=True)
+    order = ea.tile_order(p, 1)
+    steps = [256 - 8 * blk for (_, _, blk) in order]
+    tot = []
+    for g in range(256):
+        s, r = 0, 0
+        while (i := ea.persistent_tile(g, r, 256, len(order), 8)) >= 0:
+            s += steps[i]
+            r += 1
+        tot.append(s)
+    assert max(tot) == min(tot) == sum(steps) // 256
+
+
+def test_persistent_knob():
+    for v in (0, 1):
+        ea.set_tuning("persistent", v)
+    with pytest.raises(ea.AttnError):
+        ea.set_tuning("persistent", 2)
+    ea.set_tuning("persistent", 1)

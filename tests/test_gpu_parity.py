@@ -260,3 +260,37 @@ def test_deterministic_main_without_preprocess_stays_in_bounds():
     assert ea.bwd_status(p, ws) == 0
     for a, b in zip(first, again):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_persistent_and_one_shot_launches_agree(varlen):
+    """Resident workgroups looping over tiles compute every tile exactly as a
+    one-workgroup-per-tile grid does: same bits for O, LSE, dQ, dK, dV."""
+    d = 128
+    if varlen:
+        inp = make_inputs(0, 0, 0, 4, 2, d, seed=121, lengths=[3000, 17, 1200, 640, 2500, 1])
+    else:
+        inp = make_inputs(2, 3000, 3000, 8, 4, d, seed=122)
+    g = _dev(inp)
+
+    def run():
+        if varlen:
+            mx = 3000
+            o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+                                   mx, mx, causal=True)
+            grads = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
+                                  g["cu_seqlens_k"], mx, mx, causal=True)
+        else:
+            o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
+            grads = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True)
+        torch.cuda.synchronize()
+        return (o, lse) + tuple(grads)
+
+    a = run()
+    ea.set_tuning("persistent", 0)
+    try:
+        b = run()
+    finally:
+        ea.set_tuning("persistent", 1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
