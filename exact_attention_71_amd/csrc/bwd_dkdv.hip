@@ -116,6 +116,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   const int64_t last_bytes = ((int64_t)(lq - (nm - 1) * BM - 1) * qstride + D) * 2;
   const int64_t lse_seq = p.sv.cu_q ? qs : (int64_t)t.seq * p.hq * p.sv.seqlen_q;
   const int64_t lse_head = p.sv.cu_q ? p.sv.total_q : p.sv.seqlen_q;
+  const bf16* const q_base = keep_sgpr(static_cast<const bf16*>(p.q));
+  const bf16* const do_base = keep_sgpr(static_cast<const bf16*>(p.dout));
+  const float* const lse2_base = keep_sgpr(static_cast<const float*>(p.lse2));
+  const float* const dsum_base = keep_sgpr(static_cast<const float*>(p.dsum));
   // Load the step at the issue cursor into ring slot st and advance the
   // cursor. Rows past the sequence read as zero (buffer range), so their P
   // never reaches dK or dV: both products multiply it by a zero row of Q or
@@ -123,8 +127,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   auto issue = [&](int st) {
     const int64_t row0 = (qs + (int64_t)i_m * BM) * qstride + (int64_t)i_hq * D;
     const int64_t bytes = i_m == nm - 1 ? last_bytes : full_bytes;
-    const rsrc_t qr = make_rsrc(static_cast<const bf16*>(p.q) + row0, bytes);
-    const rsrc_t orr = make_rsrc(static_cast<const bf16*>(p.dout) + row0, bytes);
+    const rsrc_t qr = make_rsrc(q_base + row0, bytes);
+    const rsrc_t orr = make_rsrc(do_base + row0, bytes);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int base = (i * NW + w) * 64;          // first slot of this wave's 1 KB
@@ -139,7 +143,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
       const bool is_l = idx < BM;
       const int r = imin(i_m * BM + (idx & (BM - 1)), lq - 1);
       const int64_t so = lse_seq + (int64_t)i_hq * lse_head + r;
-      dma4(is_l ? p.lse2 + so : p.dsum + so, lds_l + (st * 2 * BM + 64 * w) * 4);
+      dma4(is_l ? lse2_base + so : dsum_base + so, lds_l + (st * 2 * BM + 64 * w) * 4);
     }
     if (++i_m == nm) { i_m = m_first; ++i_hq; }
   };

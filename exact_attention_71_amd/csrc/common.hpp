@@ -195,6 +195,16 @@ __device__ __forceinline__ const P& kernel_args() {
 #endif
 }
 
+// A uniform value the compiler must keep in an SGPR from here on: without
+// this it may re-load an argument field (a scalar load from constant memory)
+// inside a hot loop instead of keeping it live, and the wait for that load
+// (lgkmcnt) also waits for every LDS read in flight.
+template <typename T>
+__device__ __forceinline__ T keep_sgpr(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 // threadIdx.x through an opaque copy: values derived from it inside a
 // persistent loop's tile body are then recomputed per tile rather than
 // hoisted in front of the loop and kept live (in VGPRs) across all tiles.

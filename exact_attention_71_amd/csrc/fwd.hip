@@ -97,6 +97,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int qw0 = m0 + w * 32 * QB;     // first query row of this wave
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
+  const float tau = keep_sgpr(p.tau);
   const bf16* __restrict__ qp = static_cast<const bf16*>(p.q);
   const bf16* __restrict__ kp = static_cast<const bf16*>(p.k);
   const bf16* __restrict__ vp = static_cast<const bf16*>(p.v);
@@ -248,7 +249,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
           for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kb][qb][i], s[kb][qb][i + 1]);
         mx = fmaxf(mx, xor32(mx));
         mnew[qb] = fmaxf(mref[qb], mx);
-        big = big || ((mnew[qb] - mref[qb]) * sl2 > p.tau);
+        big = big || ((mnew[qb] - mref[qb]) * sl2 > tau);
       }
       if (wave_any(big)) {
 #pragma unroll
