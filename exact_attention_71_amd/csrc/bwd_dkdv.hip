@@ -110,25 +110,38 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // Steps walk (query head of the group, query block) with the block fastest.
   // Cursors replace a division per step: the issue cursor runs NS - 1 steps
   // ahead of the compute cursor (which only needs the block).
-  int i_hq = kvh * p.group, i_m = m_first;   // next step to load
+  int i_m = m_first;                          // next step to load (block of the issue cursor)
   int c_m = m_first;                          // step being computed
-  const int64_t full_bytes = ((int64_t)(BM - 1) * qstride + D) * 2;
-  const int64_t last_bytes = ((int64_t)(lq - (nm - 1) * BM - 1) * qstride + D) * 2;
   const int64_t lse_seq = p.sv.cu_q ? qs : (int64_t)t.seq * p.hq * p.sv.seqlen_q;
   const int64_t lse_head = p.sv.cu_q ? p.sv.total_q : p.sv.seqlen_q;
-  const bf16* const q_base = keep_sgpr(static_cast<const bf16*>(p.q));
-  const bf16* const do_base = keep_sgpr(static_cast<const bf16*>(p.dout));
-  const float* const lse2_base = keep_sgpr(static_cast<const float*>(p.lse2));
-  const float* const dsum_base = keep_sgpr(static_cast<const float*>(p.dsum));
+  // Addresses of the issue cursor (query block i_m of head kvh0 + i_h) as
+  // 32-bit offsets from per-tile bases: a step's loads then cost a few scalar
+  // operations (one wave per SIMD issues every instruction of the step
+  // itself). Within one sequence the Q / dO byte offsets stay below 2^31.
+  const int kvh0 = kvh * p.group;
+  int i_h = 0;
+  const int64_t q_tile = (qs * qstride + (int64_t)kvh0 * D) * 2;
+  const char* const q_seq = keep_sgpr(static_cast<const char*>(p.q) + q_tile);
+  const char* const do_seq = keep_sgpr(static_cast<const char*>(p.dout) + q_tile);
+  const int blk_bytes = BM * (int)qstride * 2;
+  const int l_step = (int)lse_head;
+  const int n_full = clamp_range(((int64_t)(BM - 1) * qstride + D) * 2);
+  const int n_last = clamp_range(((int64_t)(lq - (nm - 1) * BM - 1) * qstride + D) * 2);
+  // LSE * log2 e rows then D rows: lane idx of the waves below NLD loads row
+  // idx % BM of the block from the array its half names
+  const int l_idx = 64 * w + lane;
+  const float* const l_src = (l_idx < BM ? static_cast<const float*>(p.lse2)
+                                         : static_cast<const float*>(p.dsum)) +
+                             lse_seq + (int64_t)kvh0 * lse_head;
   // Load the step at the issue cursor into ring slot st and advance the
   // cursor. Rows past the sequence read as zero (buffer range), so their P
   // never reaches dK or dV: both products multiply it by a zero row of Q or
   // dO. Their LSE and D are clamped to the last row to stay finite.
   auto issue = [&](int st) {
-    const int64_t row0 = (qs + (int64_t)i_m * BM) * qstride + (int64_t)i_hq * D;
-    const int64_t bytes = i_m == nm - 1 ? last_bytes : full_bytes;
-    const rsrc_t qr = make_rsrc(q_base + row0, bytes);
-    const rsrc_t orr = make_rsrc(do_base + row0, bytes);
+    const int n = i_m == nm - 1 ? n_last : n_full;
+    const int q_rel = i_m * blk_bytes + i_h * (2 * D);
+    const rsrc_t qr = raw_rsrc(q_seq + q_rel, n);
+    const rsrc_t orr = raw_rsrc(do_seq + q_rel, n);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int base = (i * NW + w) * 64;          // first slot of this wave's 1 KB
@@ -139,13 +152,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
       dma16(orr, lds_q + (NS + st) * TILE + base * 16, voff);
     }
     if (w < NLD) {
-      const int idx = 64 * w + lane;                // [LSE * log2 e rows | D rows]
-      const bool is_l = idx < BM;
-      const int r = imin(i_m * BM + (idx & (BM - 1)), lq - 1);
-      const int64_t so = lse_seq + (int64_t)i_hq * lse_head + r;
-      dma4(is_l ? lse2_base + so : dsum_base + so, lds_l + (st * 2 * BM + 64 * w) * 4);
+      const int r = imin(i_m * BM + (l_idx & (BM - 1)), lq - 1);
+      dma4(l_src + (i_h * l_step + r), lds_l + (st * 2 * BM + 64 * w) * 4);
     }
-    if (++i_m == nm) { i_m = m_first; ++i_hq; }
+    if (++i_m == nm) { i_m = m_first; ++i_h; }
   };
   // wait until the loads of the next step are in LDS (those of later steps may
   // still be in flight), then make them visible to the workgroup
@@ -334,9 +344,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
 
+  int st = 0;   // ring slot of the step being computed (step % NS)
   for (int step = 0; step < n_steps; ++step) {
-    const int st = step % NS;
-    if (step + NS - 1 < n_steps) issue((step + NS - 1) % NS);
+    if (step + NS - 1 < n_steps) issue(st == 0 ? NS - 1 : st - 1);   // (step + NS - 1) % NS
     const int mq0 = c_m * BM;
     if (++c_m == nm) c_m = m_first;
     // whole wave above the diagonal: no visible pair in this step
@@ -344,6 +354,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     const bool need_mask = (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
     if (active) step_body(mq0, need_mask);
     advance_slot(st);
+    st = st == NS - 1 ? 0 : st + 1;
     if (step + 1 < n_steps) wait_next(step + NS - 1 < n_steps);
   }
 

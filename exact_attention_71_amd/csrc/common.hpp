@@ -232,6 +232,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
+// Byte range of a buffer resource clamped to [0, 2^31 - 1].
+__device__ __forceinline__ int clamp_range(int64_t bytes) {
+  return bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes));
+}
+// Resource for a range already clamped by clamp_range (no per-call checks).
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* base, int range) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, range, 0x00020000);
+}
+
 __device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, int voff, int soff) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return __builtin_bit_cast(bf16x8, x);
