@@ -45,7 +45,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   constexpr int SPR = D / 8;            // 16-byte slots per row
   constexpr int TILE = BM * RB;         // bytes of one Q (or dO) tile
   constexpr int NS = 3;                 // ring depth
-  static_assert(NS == 3, "wait_next() counts at most one later step in flight");
+  static_assert(NS == 3, "loads run two steps ahead: slot (s + 2) % NS == (s - 1) % NS");
   constexpr int CH = TILE / (16 * NT);  // dma16 per thread per tile
   constexpr int NLD = 2 * BM / 64;      // dma4 (LSE and D) per step, waves 0 .. NLD-1
   static_assert(TILE % (16 * NT) == 0 && NLD <= NW, "tile split over the workgroup");
@@ -157,14 +157,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     }
     if (++i_m == nm) { i_m = m_first; ++i_h; }
   };
-  // wait until the loads of the next step are in LDS (those of later steps may
-  // still be in flight), then make them visible to the workgroup
-  auto wait_next = [&](bool later_issued) {
-    if (later_issued) {
-      if (w < NLD) wait_vm<OPS + 1>(); else wait_vm<OPS>();
-    } else {
-      wait_vm<0>();
-    }
+  // Ring order. Step s reads slot s % NS. Between its dV^T and dK^T phases
+  // every wave waits for its own loads of step s + 1 (the only ones in flight
+  // then) and meets the others at a barrier: after it, slot (s + 1) % NS is
+  // complete, and every wave is past step s - 1, so the loads of step s + 2
+  // may overwrite slot (s - 1) % NS; they go out during the dK^T phase. The
+  // barrier sits under a queue of dK^T MFMAs instead of in front of the next
+  // step, and the next step's first fragments are read before that step begins.
+  auto mid = [&]() {
+    wait_vm<0>();
     __builtin_amdgcn_s_barrier();
   };
 
@@ -203,6 +204,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   };
   static_assert(TILE % 8192 == 0 || TILE >= 2 * RB * 32, "slot offsets clear the XOR bits");
 
+  // Fragment j (0 or 1) of a step, the Q operands of its first S MFMAs, from
+  // the slot at byte offset nxt from the current one.
+  auto fetch_first = [&](int j, int nxt) -> bf16x8 {
+    const int kk = j / NQB, qb = j % NQB;
+    return lds_ld16(ar[kk] + nxt + qb * 32 * RB);
+  };
+
   // One step for query block mq0. Masking (causal diagonal, key tail) sets
   // S = -inf in a branch of its own on the steps that need it: register i of a
   // tile is query row mq0 + 32 qb + 8 (i / 4) + 4 g + i % 4, so with
@@ -210,7 +218,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // (rel = INT_MAX for keys past the sequence, -1 where nothing is hidden).
   // Only S crosses that branch; a second copy of the whole body would split
   // the AGPR accumulators over two paths (the allocator answers with spills).
-  auto step_body = [&](int mq0, bool need_mask) {
+  // f0, f1: the first two operand fragments of this step on entry (read by
+  // the previous step), of the next step (slot offset nxt) on return.
+  // has_next: a later step exists (mid-step sync); iss >= 0: the ring slot the
+  // loads of step + 2 go to.
+  auto step_body = [&](int mq0, bool need_mask, bf16x8& f0, bf16x8& f1, bool has_next, int iss,
+                       int nxt) {
     constexpr int OT = NS * TILE;   // dO tile offset from the Q tile
     int rel[KB];
 #pragma unroll
@@ -283,12 +296,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
         for (int k2 = 0; k2 < KB; ++k2) sb[qb][k2][j >> 1] = pack_half(dp[qb][k2], j >> 1);
       }
     };
-    bf16x8 f0 = fetch(0), f1 = fetch(1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
+      if (f == 2 * NG1 + NG2) {                       // dV^T done: sync for step + 1
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const bf16x8 cur = f0;
       f0 = f1;
-      if (f + 2 < NF) f1 = fetch(f + 2);
+      f1 = f + 2 < NF ? fetch(f + 2) : fetch_first(f + 2 - NF, nxt);
       if (f < NG1) {                                  // S = Q K^T
         const int kk = f / NQB, qb = f % NQB;
 #pragma unroll
@@ -330,6 +346,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mfma32_agpr(dk[kb][db], cur, sb[qb][kb][tt]);
         __builtin_amdgcn_sched_barrier(0);
+        if (x == 1 && iss >= 0) {
+          issue(__builtin_amdgcn_readfirstlane(iss));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
@@ -345,17 +365,21 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   __builtin_amdgcn_s_barrier();
 
   int st = 0;   // ring slot of the step being computed (step % NS)
+  bf16x8 f0 = fetch_first(0, 0), f1 = fetch_first(1, 0);
   for (int step = 0; step < n_steps; ++step) {
-    if (step + NS - 1 < n_steps) issue(st == 0 ? NS - 1 : st - 1);   // (step + NS - 1) % NS
     const int mq0 = c_m * BM;
     if (++c_m == nm) c_m = m_first;
-    // whole wave above the diagonal: no visible pair in this step
-    const bool active = !(causal && wk0 > mq0 + BM - 1 + shift);
+    const bool has_next = step + 1 < n_steps;
+    const int iss = step + NS - 1 < n_steps ? (st == 0 ? NS - 1 : st - 1) : -1;  // (step + 2) % NS
+    const int nxt = st == NS - 1 ? -(NS - 1) * TILE : TILE;                      // next slot
+    // A wave whose keys all lie above this block's rows computes the step
+    // anyway (masked to zero): skipping it would need a second path around
+    // the mid-step barrier, and the register allocator answers such a split
+    // of the AGPR accumulators with spills.
     const bool need_mask = (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
-    if (active) step_body(mq0, need_mask);
+    step_body(mq0, need_mask, f0, f1, has_next, iss, nxt);
     advance_slot(st);
     st = st == NS - 1 ? 0 : st + 1;
-    if (step + 1 < n_steps) wait_next(step + NS - 1 < n_steps);
   }
 
   // ---- dK = alpha dK^T, dV = dV^T for this wave's keys
