@@ -180,6 +180,27 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
     f32x16 s[NKB], dp[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+    // Hand schedule (as in the dK/dV kernel): after each dP^T MFMA its slice
+    // of P = 2^(S scale log2 e - LSE log2 e); the dS^T = P o (dP^T - D) work in
+    // groups of 8 elements (one 16-key half of a 32-key block: the B operand of
+    // NDB dQ^T MFMAs), group q + 1 computed between the MFMAs of group q.
+    constexpr int PPM = NKB * 16 / NG1;       // P elements per dP^T MFMA
+    constexpr int NQG = 2 * NKB;              // dS groups
+    constexpr int SPM = 8 / NDB;              // dS elements per dQ^T MFMA
+    static_assert(PPM * NG1 == NKB * 16 && SPM * NDB == 8, "even slices");
+    auto p_elem = [&](int e) {
+      const int kb = e / 16, i = e % 16;
+      float pv = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -lse2));
+      pin(pv);
+      s[kb][i] = pv;
+    };
+    auto ds_elem = [&](int q, int j) {
+      const int kb = q / 2, i = 8 * (q % 2) + j;
+      float d = s[kb][i] * (dp[kb][i] - dsum);
+      pin(d);
+      dp[kb][i] = d;
+    };
+    bf16x8 dsb = {};
     bf16x8 fq[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) fq[i] = fetch(i);
@@ -192,31 +213,39 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
       if (f < NG1) {                                  // S^T = K Q^T
         const int kk = f / NKB, kb = f % NKB;
         s[kb] = mfma32(cur, qf[kk], s[kb]);
-      } else if (f < 2 * NG1) {                       // dP^T = V dO^T
+        __builtin_amdgcn_sched_barrier(0);
+        if (f == NG1 - 1 && need_mask) {
+          const int lim = imin(causal ? myq + shift : 0x7fffffff, lk - 1) - k0 - 4 * g;
+#pragma unroll
+          for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              s[kb2][i] = 32 * kb2 + 8 * (i >> 2) + (i & 3) > lim ? neg_inf() : s[kb2][i];
+        }
+      } else if (f < 2 * NG1) {                       // dP^T = V dO^T, with P
         const int x = f - NG1, kk = x / NKB, kb = x % NKB;
         dp[kb] = mfma32(cur, df[kk], dp[kb]);
-        if (x == NG1 - 1) {
-          // ---- P^T = 2^(S^T scale log2 e - LSE log2 e), dS^T = P^T o (dP^T - D)
-          if (need_mask) {
-            const int lim = imin(causal ? myq + shift : 0x7fffffff, lk - 1) - k0 - 4 * g;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+        for (int e = 0; e < PPM; ++e) p_elem(x * PPM + e);
+        __builtin_amdgcn_sched_barrier(0);
+        if (x == NG1 - 1) {                           // dS group 0 before its MFMAs
 #pragma unroll
-              for (int i = 0; i < 16; ++i)
-                s[kb][i] = 32 * kb + 8 * (i >> 2) + (i & 3) > lim ? neg_inf() : s[kb][i];
-          }
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float pv = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -lse2));
-              dp[kb][i] = pv * (dp[kb][i] - dsum);
-            }
+          for (int j = 0; j < 8; ++j) ds_elem(0, j);
+          dsb = pack_half(dp[0], 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      } else {                                        // dQ^T += K^T dS^T
+      } else {                                        // dQ^T += K^T dS^T, with dS
         const int x = f - 2 * NG1;
-        const int kb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
-        dqacc[db] = mfma32(cur, pack_half(dp[kb], tt), dqacc[db]);
+        const int q = x / NDB, db = x % NDB;
+        dqacc[db] = mfma32(cur, dsb, dqacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + 1 < NQG) {
+#pragma unroll
+          for (int j = 0; j < SPM; ++j) ds_elem(q + 1, db * SPM + j);
+          if (db == NDB - 1) dsb = pack_half(dp[(q + 1) / 2], (q + 1) % 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
