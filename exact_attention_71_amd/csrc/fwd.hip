@@ -261,38 +261,66 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
           mref[qb] = mnew[qb];
         }
       }
-      // P = 2^(s*alpha*log2e - m_ref*alpha*log2e), row sums from fp32 p
+      // P = 2^(s*alpha*log2e - m_ref*alpha*log2e), row sums from fp32 p, and
+      // O^T += V^T P^T (A of the PV product by transposing reads of V). Hand
+      // schedule: the P work of each 16-key half (8 elements) runs between
+      // the NDB MFMAs of the previous half, whose V^T fragments stream two
+      // ahead; only half 0 is computed up front.
+      float nb[QB], acc[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float nb = (mref[qb] == neg_inf()) ? 0.0f : -mref[qb] * sl2;
-        float acc = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = __builtin_fmaf(s[kb][qb][i], sl2, nb);
-            const float e = ((i & 7) < EMU) ? emu_exp2(x) : fast_exp2(x);
-            s[kb][qb][i] = e;
-            acc += e;
-          }
-        lsum[qb] += acc;
+        nb[qb] = (mref[qb] == neg_inf()) ? 0.0f : -mref[qb] * sl2;
+        acc[qb] = 0.0f;
       }
-      // O^T += V^T P^T (A of the PV product by transposing reads of V)
+      auto p_half = [&](int h, int j0, int nj) {   // elements j0 .. j0+nj-1 of half h
+        const int kb = h / 2;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int j = j0; j < j0 + nj; ++j) {
+          const int i = 8 * (h % 2) + j;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          bf16x8 pb[QB];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_half(s[kb][qb], tt);
-          const int off = (kb * 32 + 16 * tt) * RB;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(a, pb[qb], oacc[qb][db]);
+          for (int qb = 0; qb < QB; ++qb) {
+            const float x = __builtin_fmaf(s[kb][qb][i], sl2, nb[qb]);
+            float e = ((i & 7) < EMU) ? emu_exp2(x) : fast_exp2(x);
+            pin(e);
+            s[kb][qb][i] = e;
+            acc[qb] += e;
           }
         }
+      };
+      constexpr int NH = 2 * NKB, NPV = NH * NDB;   // halves, PV MFMAs
+      constexpr int PE = 8 / NDB;                   // P elements per PV MFMA
+      static_assert(PE * NDB == 8, "even P slices");
+      auto fetch_pv = [&](int x) -> bf16x8 {
+        const int h = x / NDB, db = x % NDB;
+        const int off = (h / 2 * 32 + 16 * (h % 2)) * RB;
+        return cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
+      };
+      bf16x8 v0 = fetch_pv(0), v1 = fetch_pv(1);
+      p_half(0, 0, 8);
+      bf16x8 pb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_half(s[0][qb], 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < NPV; ++x) {
+        const int h = x / NDB, db = x % NDB;
+        const bf16x8 a = v0;
+        v0 = v1;
+        if (x + 2 < NPV) v1 = fetch_pv(x + 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(a, pb[qb], oacc[qb][db]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (h + 1 < NH) {
+          p_half(h + 1, db * PE, PE);
+          if (db == NDB - 1) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_half(s[(h + 1) / 2][qb], (h + 1) % 2);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb];
     }
     advance_slot(st);
     if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
