@@ -206,26 +206,20 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
     const int k0 = n * BN;
     const bool active = !(causal && k0 > qw0 + 32 * QB - 1 + shift);
     if (active) {
-      // S^T = K Q^T for this tile
+      // S^T = K Q^T for this tile, key block by key block; the mask and the
+      // row-max work of block kb run between the MFMAs of block kb + 1
+      // (operand fragments streamed two ahead)
       f32x16 s[NKB][QB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 a = lds_ld16(ar[kk] + kb * 32 * RB);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(a, qf[qb][kk], s[kb][qb]);
-        }
-      }
-      // mask the ragged key tail and the causal diagonal
       const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
-      if (need_mask) {
+      float mx[QB];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = neg_inf();
+      auto kb_max = [&](int kb) {
+        if (need_mask) {   // the ragged key tail and the causal diagonal
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const int qrow = qw0 + qb * 32 + c;
@@ -236,19 +230,40 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
               s[kb][qb][i] = hide ? neg_inf() : s[kb][qb][i];
             }
           }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mx[qb] = max3f(mx[qb], s[kb][qb][i], s[kb][qb][i + 1]);
+      };
+      constexpr int NSF = NKB * KS;                 // S^T MFMA fragments
+      auto fetch_s = [&](int y) -> bf16x8 {
+        const int kb = y / KS, kk = y % KS;
+        return lds_ld16(ar[kk] + kb * 32 * RB);
+      };
+      bf16x8 k0f = fetch_s(0), k1f = fetch_s(1);
+#pragma unroll
+      for (int y = 0; y < NSF; ++y) {
+        const int kb = y / KS, kk = y % KS;
+        const bf16x8 a = k0f;
+        k0f = k1f;
+        if (y + 2 < NSF) k1f = fetch_s(y + 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(a, qf[qb][kk], s[kb][qb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb > 0 && kk == 1) {
+          kb_max(kb - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      kb_max(NKB - 1);
       // running max and the per-wavefront rescale decision
       float mnew[QB];
       bool big = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = neg_inf();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kb][qb][i], s[kb][qb][i + 1]);
-        mx = fmaxf(mx, xor32(mx));
-        mnew[qb] = fmaxf(mref[qb], mx);
+        const float m = fmaxf(mx[qb], xor32(mx[qb]));
+        mnew[qb] = fmaxf(mref[qb], m);
         big = big || ((mnew[qb] - mref[qb]) * sl2 > tau);
       }
       if (wave_any(big)) {
