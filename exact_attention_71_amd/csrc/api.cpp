@@ -66,7 +66,7 @@ int64_t rows_q_of(const attn_params* p, bool varlen) {
 
 // ------------------------------------------------------------ workspace maps
 struct FwdWs {
-  size_t order = 0, tile_prefix = 0, total = 0;
+  size_t order = 0, tile_prefix = 0, queue = 0, total = 0;
 };
 FwdWs fwd_ws(const attn_params* p, bool varlen) {
   FwdWs w;
@@ -74,6 +74,7 @@ FwdWs fwd_ws(const attn_params* p, bool varlen) {
   size_t off = 0;
   w.order = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
   w.tile_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
+  w.queue = off; off = align_up(off + sizeof(unsigned));
   w.total = off;
   return w;
 }
@@ -194,7 +195,7 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   FwdParams fp;
   fp.q = q; fp.k = k; fp.v = v; fp.o = o; fp.lse = lse;
   fp.sv = make_sv(p, cu_q, cu_k);
-  fp.order = nullptr; fp.tile_prefix = nullptr;
+  fp.order = nullptr; fp.tile_prefix = nullptr; fp.queue = nullptr;
   fp.hq = p->num_heads_q; fp.hkv = p->num_heads_kv; fp.group = p->num_heads_q / p->num_heads_kv;
   const int bm = fwd_block_m(d);
   fp.nm = cdiv(p->seqlen_q, bm);
@@ -210,18 +211,18 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     char* base = static_cast<char*>(ws);
     int* order = reinterpret_cast<int*>(base + wl.order);
     int* tp = reinterpret_cast<int*>(base + wl.tile_prefix);
+    unsigned* queue = launch_cus() ? reinterpret_cast<unsigned*>(base + wl.queue) : nullptr;
     if (launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bm, order, tp, nullptr,
-                               1, stream) != hipSuccess)
+                               1, queue, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     fp.order = order;
     fp.tile_prefix = tp;
+    fp.queue = queue;
   }
   // the FMA-path exp2 pays off only where the forward runs one wave per SIMD
   // (head_dim 256: +8 % measured); elsewhere v_exp_f32 alone is faster
   const int emu = g_tuning.exp_emulation >= 0 ? g_tuning.exp_emulation : (d == 256 ? 2 : 0);
-  // persistent workgroups for fixed lengths only (see bwd_impl)
-  if (launch_fwd(fp, d, varlen ? 0 : launch_cus(), emu, g_tuning.fwd_pingpong != 0, stream) !=
-      hipSuccess)
+  if (launch_fwd(fp, d, launch_cus(), emu, g_tuning.fwd_pingpong != 0, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -296,18 +297,24 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   }
   // Packed sequences of very different lengths make tiles too unequal for a
   // static walk (measured 19 % slower dK/dV on 16 sequences of 512..8192):
-  // there the dispatcher's one workgroup per tile balances better.
-  const int pcus = varlen ? 0 : launch_cus();
+  // there the persistent workgroups draw tiles from device counters, which
+  // the varlen schedule pass clears.
+  const int pcus = launch_cus();
+  if (varlen && pcus) {
+    bp.queue = reinterpret_cast<unsigned*>(base + wl.misc + 8);
+    bp.queue_dq = reinterpret_cast<unsigned*>(base + wl.misc + 12);
+  }
   if (pre) {
     if (varlen && launch_varlen_schedule(cu_q, cu_k, cu_q, p->batch, p->num_heads_kv, bn,
                                          const_cast<int*>(bp.order),
                                          const_cast<int*>(bp.tile_prefix),
-                                         const_cast<int*>(bp.mb_prefix), bm, stream) != hipSuccess)
+                                         const_cast<int*>(bp.mb_prefix), bm, bp.queue,
+                                         stream) != hipSuccess)
       return ATTN_ERR_HIP;
     if (varlen && !fused &&
         launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bmq,
                                const_cast<int*>(bp.order_dq), const_cast<int*>(bp.tile_prefix_dq),
-                               nullptr, 1, stream) != hipSuccess)
+                               nullptr, 1, bp.queue_dq, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }

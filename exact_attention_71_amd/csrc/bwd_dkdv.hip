@@ -415,14 +415,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 template <int D, int KB, int BM>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM>()];
+  __shared__ int ticket;
   for (int r = 0;; ++r) {
     const BwdParams& p = kernel_args<BwdParams>();
-    const int i = persistent_index(blockIdx.x, r, gridDim.x, p.ntiles, p.nxcd);
+    const int i = next_tile(r, p.ntiles, p.nxcd, p.queue, &ticket);
     if (i < 0) break;
     Tile t;
     if (p.sv.cu_q) {
       t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/false);
-      if (t.seq < 0) break;
+      if (t.seq < 0) {
+        if (p.queue) continue;   // a ticket past the last real tile
+        break;
+      }
     } else {
       t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, false, p.nxcd, p.natural != 0);
     }

@@ -290,14 +290,18 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
 template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_smem_bytes<D, BN>()];
+  __shared__ int ticket;
   for (int r = 0;; ++r) {
     const BwdParams& p = kernel_args<BwdParams>();
-    const int i = persistent_index(blockIdx.x, r, gridDim.x, p.ntiles_dq, p.nxcd);
+    const int i = next_tile(r, p.ntiles_dq, p.nxcd, p.queue_dq, &ticket);
     if (i < 0) break;
     Tile t;
     if (p.sv.cu_q) {
       t = varlen_tile(i, p.order_dq, p.tile_prefix_dq, p.sv.batch, p.hq, true);
-      if (t.seq < 0) break;
+      if (t.seq < 0) {
+        if (p.queue_dq) continue;   // a ticket past the last real tile
+        break;
+      }
     } else {
       t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
     }

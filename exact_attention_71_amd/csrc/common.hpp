@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "schedule.hpp"
 #include <stdint.h>
 
 namespace attn71 {
@@ -203,6 +205,24 @@ template <typename T>
 __device__ __forceinline__ T keep_sgpr(T x) {
   asm volatile("" : "+s"(x));
   return x;
+}
+
+// Next tile position of a persistent workgroup in round r. queue == null:
+// the static walk (schedule.hpp: persistent_index). Otherwise a ticket from a
+// device counter, in the schedule's longest-first order — for packed variable
+// lengths, whose tiles are too unequal for a static walk. A launch draws
+// exactly ntiles + gridDim.x tickets (one past the end per workgroup), so
+// counting modulo that keeps a counter cleared once (by the varlen schedule
+// pass) valid for repeated launches of the same problem. Returns -1 when the
+// workgroup is done; every thread of the workgroup calls it (barriers).
+__device__ __forceinline__ int next_tile(int r, int ntiles, int nx, unsigned* queue, int* slot) {
+  if (!queue) return persistent_index(blockIdx.x, r, gridDim.x, ntiles, nx);
+  if (threadIdx.x == 0)
+    *slot = static_cast<int>(atomicAdd(queue, 1u) % static_cast<unsigned>(ntiles + gridDim.x));
+  __syncthreads();
+  const int i = *slot;
+  __syncthreads();   // every thread has read the ticket before the next draw
+  return i < ntiles ? i : -1;
 }
 
 // threadIdx.x through an opaque copy: values derived from it inside a

@@ -373,14 +373,18 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
 template <int D, int NW, int QB, int BN, int EMU>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[fwd_smem_bytes<D, BN>()];
+  __shared__ int ticket;
   for (int r = 0;; ++r) {
     const FwdParams& p = kernel_args<FwdParams>();
-    const int i = persistent_index(blockIdx.x, r, gridDim.x, p.ntiles, p.nxcd);
+    const int i = next_tile(r, p.ntiles, p.nxcd, p.queue, &ticket);
     if (i < 0) break;
     Tile t;
     if (p.sv.cu_q) {
       t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
-      if (t.seq < 0) break;
+      if (t.seq < 0) {
+        if (p.queue) continue;   // a ticket past the last real tile
+        break;
+      }
     } else {
       t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
     }

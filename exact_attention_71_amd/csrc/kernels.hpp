@@ -32,6 +32,7 @@ struct FwdParams {
   int sec, nxcd;
   int natural;            // 1: plain tile order (tuning / ablation)
   int ntiles;             // tiles of the launch (varlen: upper bound)
+  unsigned* queue;        // varlen: tile ticket counter (null: static walk)
   int causal;
   float alpha;            // softmax scale
   float scale_log2;       // alpha * log2(e)
@@ -65,6 +66,8 @@ struct BwdParams {
   int natural;            // 1: plain tile order (non-deterministic only)
   int ntiles;             // dK/dV (or fused) tiles of the launch (varlen: upper bound)
   int ntiles_dq;          // dQ kernel tiles (varlen: upper bound)
+  unsigned* queue;        // varlen: dK/dV tile ticket counter (null: static walk)
+  unsigned* queue_dq;     // varlen: dQ tile ticket counter
   int causal, deterministic;
   float alpha;
   float scale_log2;
@@ -152,9 +155,11 @@ hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
 // Varlen pre-pass: order[] = sequences by decreasing length of key_cu (ties
 // by index), tile_prefix[vs] = first tile of virtual sequence vs with
 // cdiv(len of count_cu, blk) * heads tiles each, and (optional) mb_prefix[s]
-// = first query block of actual sequence s with cdiv(len of q_cu, mb_blk).
+// = first query block of actual sequence s with cdiv(len of q_cu, mb_blk);
+// clears *queue (optional) for the tile tickets of the launch that follows.
 hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
                                   int nseq, int heads, int blk, int* order, int* tile_prefix,
-                                  int* mb_prefix, int mb_blk, hipStream_t stream);
+                                  int* mb_prefix, int mb_blk, unsigned* queue,
+                                  hipStream_t stream);
 
 }  // namespace attn71

@@ -17,8 +17,10 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(const int* __restr
                                                               const int* __restrict__ q_cu,
                                                               int nseq, int heads, int blk,
                                                               int* order, int* tile_prefix,
-                                                              int* mb_prefix, int mb_blk) {
+                                                              int* mb_prefix, int mb_blk,
+                                                              unsigned* queue) {
   for (int s = threadIdx.x; s < nseq; s += blockDim.x) order[varlen_rank(key_cu, nseq, s)] = s;
+  if (queue && threadIdx.x == 128) *queue = 0u;   // tile tickets of the launch that follows
   __syncthreads();
   if (threadIdx.x == 0) {
     int acc = 0;
@@ -42,9 +44,10 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(const int* __restr
 
 hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
                                   int nseq, int heads, int blk, int* order, int* tile_prefix,
-                                  int* mb_prefix, int mb_blk, hipStream_t stream) {
+                                  int* mb_prefix, int mb_blk, unsigned* queue,
+                                  hipStream_t stream) {
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(256), 0, stream, key_cu, count_cu,
-                     q_cu, nseq, heads, blk, order, tile_prefix, mb_prefix, mb_blk);
+                     q_cu, nseq, heads, blk, order, tile_prefix, mb_prefix, mb_blk, queue);
   return hipGetLastError();
 }
 

@@ -190,9 +190,10 @@ int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles,
  *                   MI355X so far), 0 = one phase per key tile (default);
  *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
  *                   (batch-head major, blocks ascending, no remap);
- *   "persistent"    1 = for fixed-length calls, resident workgroups loop over
- *                   the tiles (default); 0 = one workgroup per tile (always
- *                   the case for packed variable lengths);
+ *   "persistent"    1 = resident workgroups loop over the tiles (default: a
+ *                   static walk for fixed lengths, tickets from a workspace
+ *                   counter for packed variable lengths); 0 = one workgroup
+ *                   per tile;
  *   "exp_emulation" -1 = automatic (default: 2 at head_dim 256, where it
  *                   measured faster, 0 otherwise); 0 = every exp2 on
  *                   v_exp_f32; 1, 2 or 4 = that many of every 8 on the
