@@ -24,7 +24,7 @@ constexpr size_t kAlign = 256;
 
 struct Tuning {
   int tile_order = 0;
-  int exp_emulation = -1; // -1: automatic (2 of 8 at head_dim 256, else none; measured)
+  int exp_emulation = -1; // -1: automatic (none: v_exp_f32 measured fastest at every head_dim)
   int tau = 8;            // rescale threshold (log2 units); the pages' log2(256)
   int spin_limit = 1 << 26;
   int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
@@ -219,9 +219,10 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     fp.tile_prefix = tp;
     fp.queue = queue;
   }
-  // the FMA-path exp2 pays off only where the forward runs one wave per SIMD
-  // (head_dim 256: +8 % measured); elsewhere v_exp_f32 alone is faster
-  const int emu = g_tuning.exp_emulation >= 0 ? g_tuning.exp_emulation : (d == 256 ? 2 : 0);
+  // the FMA-path exp2 issues from the same VALU port as v_exp_f32 here, and
+  // with the hand-scheduled forward step every share E > 0 measured slower at
+  // head_dim 64, 128 and 256, so the automatic choice is none
+  const int emu = g_tuning.exp_emulation >= 0 ? g_tuning.exp_emulation : 0;
   if (launch_fwd(fp, d, launch_cus(), emu, g_tuning.fwd_pingpong != 0, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;

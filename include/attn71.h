@@ -194,8 +194,8 @@ int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles,
  *                   static walk for fixed lengths, tickets from a workspace
  *                   counter for packed variable lengths); 0 = one workgroup
  *                   per tile;
- *   "exp_emulation" -1 = automatic (default: 2 at head_dim 256, where it
- *                   measured faster, 0 otherwise); 0 = every exp2 on
+ *   "exp_emulation" -1 = automatic (default: 0, the fastest measured at
+ *                   every head_dim); 0 = every exp2 on
  *                   v_exp_f32; 1, 2 or 4 = that many of every 8 on the
  *                   Cody-Waite + Horner FMA path (blog page, faster exponential
  *                   section);
