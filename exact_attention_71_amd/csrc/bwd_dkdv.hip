@@ -334,7 +334,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
         const int qb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          mfma32_agpr(dv[kb][db], cur, pb[qb][kb][tt]);
+          mfma32_agpr<false>(dv[kb][db], cur, pb[qb][kb][tt]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int e = 0; e < SPM; ++e) s_elem((x * KB + kb) * SPM + e);
@@ -344,7 +344,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
         const int x = f - 2 * NG1 - NG2;
         const int qb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mfma32_agpr(dk[kb][db], cur, sb[qb][kb][tt]);
+        for (int kb = 0; kb < KB; ++kb) mfma32_agpr<false>(dk[kb][db], cur, sb[qb][kb][tt]);
         __builtin_amdgcn_sched_barrier(0);
         if (x == 1 && iss >= 0) {
           issue(__builtin_amdgcn_readfirstlane(iss));

@@ -39,12 +39,20 @@ __device__ __forceinline__ int c_row(int i, int g) { return 8 * (i >> 2) + 4 * g
 // accumulators in kernels whose VGPRs are full (the compiler's VGPR/AGPR form
 // choice is all-or-nothing per function). The compiler does not see hazards
 // inside inline asm, so the two cases that apply here are covered by hand:
-// s_nop 1 gives the 2 wait states a VALU-written A/B operand needs before an
-// MFMA reads it, and agpr_fence() must separate the last accumulation from
-// any non-MFMA read of the accumulator. Back-to-back accumulation into the
-// same registers needs no wait states.
+// an A/B operand written by a VALU instruction needs 2 wait states before an
+// MFMA reads it, which WAIT = true provides with s_nop 1, and agpr_fence()
+// must separate the last accumulation from any non-MFMA read of the
+// accumulator. Back-to-back accumulation into the same registers needs no
+// wait states. WAIT = false is for hand-scheduled call sites whose operands
+// come from LDS reads or from VALU work issued well before; the
+// tests/test_isa_hazards.py scan of the compiled code checks every such MFMA
+// for a VALU write of its operands in the 2 wait states before it.
+template <bool WAIT = true>
 __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (WAIT)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Keeps a value's computation where it stands in the source: sched_barrier
