@@ -82,9 +82,12 @@ typedef struct attn_params {
   int32_t head_dim;      /* 64, 128 or 256 */
   float softmax_scale;   /* alpha */
   int32_t causal;        /* 0 or 1 */
-  int32_t deterministic; /* backward only: 0 = fp32 atomics for dQ; 1 = fixed
-                            accumulation order, bit-identical dQ/dK/dV across runs
-                            (blog page, deterministic-mode section) */
+  int32_t deterministic; /* backward only, 0 or 1. The default split backward
+                            writes every output once and is bit-identical across
+                            runs either way; with bwd_fused_dq = 1, 0 = fp32
+                            atomics for dQ, 1 = fixed accumulation order,
+                            bit-identical dQ/dK/dV across runs (blog page,
+                            deterministic-mode section) */
 } attn_params;
 
 /* "OK", "invalid argument", ... ; never NULL. */
