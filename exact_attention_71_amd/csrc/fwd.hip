@@ -23,6 +23,8 @@
 //  * the rescale decision is one ballot per wavefront (any row over tau);
 //  * exp2 runs on v_exp_f32; EMU > 0 moves EMU of every 8 elements to the
 //    Cody-Waite + Horner polynomial on the FMA path.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "schedule.hpp"
@@ -62,8 +64,23 @@ template <int D, int BN>
 constexpr int fwd_smem_bytes() { return 2 * fwd_ring_depth<D, BN>() * BN * 2 * D; }
 
 // One tile: query block t.block of (sequence t.seq, query head t.head).
+// Tiles follow each other on a workgroup: the K / V ring continues across them
+// (key tile n of this tile sits in slot (s0 + n) % NS; s0 is advanced for the
+// next tile), and during its last key tile a tile loads the first key tile
+// and the Q fragments of `nxt` (when has_nxt), so that the next tile starts
+// without waiting for them. `pre` says the previous tile did so for this one;
+// the return value says whether this one did for `nxt`.
 template <int D, int NW, int QB, int BN, int EMU>
-__device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char* smem) {
+__device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char* smem,
+                                         bf16x8 (&qf)[QB][D / 16], int& s0, bool pre,
+                                         Tile nxt, bool has_nxt) {
+  // not at head_dim 256, whose scalar registers are already short: there every
+  // tile starts its ring at slot 0 and loads its own first tiles
+  constexpr bool XT = D <= 128;
+  if constexpr (!XT) {
+    s0 = 0;
+    has_nxt = false;
+  }
   constexpr int NT = NW * 64;           // threads
   constexpr int BM = NW * 32 * QB;
   constexpr int KS = D / 16;            // MFMA k-steps over the head dim
@@ -83,10 +100,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
 
   int64_t qs, ks0;
   int lq, lk;
-  seq_bounds(p.sv, t.seq, &qs, &lq, &ks0, &lk);
-  const int m0 = t.block * BM;
-  if (m0 >= lq) return;
-  const int h = t.head;
+  // the tile is wave-uniform (the previous tile carried it); its fields stay in
+  // scalar registers for the loads' buffer resources
+  seq_bounds(p.sv, __builtin_amdgcn_readfirstlane(t.seq), &qs, &lq, &ks0, &lk);
+  const int m0 = __builtin_amdgcn_readfirstlane(t.block) * BM;
+  if (m0 >= lq) return false;   // never with pre: the prefetch checks the same bound
+  const int h = __builtin_amdgcn_readfirstlane(t.head);
   const int kvh = h / p.group;
   const bool causal = p.causal != 0;
   const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
@@ -102,17 +121,19 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
   const bf16* __restrict__ kp = static_cast<const bf16*>(p.k);
   const bf16* __restrict__ vp = static_cast<const bf16*>(p.v);
 
-  // ---- Q^T operands: lane holds query row (qb*32 + c), dims 16ks + 8g .. +7
-  const rsrc_t qr = make_rsrc(qp + qs * qstride + (int64_t)h * D,
-                              ((int64_t)(lq - 1) * qstride + D) * 2);
-  bf16x8 qf[QB][KS];
+  // ---- Q^T operands: lane holds query row (qb*32 + c), dims 16ks + 8g .. +7,
+  // of the query block at row q0_ of head hh_ in the sequence at packed row qs_
+  auto load_q = [&](int64_t qs_, int lq_, int hh_, int q0_) {
+    const rsrc_t qr = make_rsrc(qp + qs_ * qstride + (int64_t)hh_ * D,
+                                ((int64_t)(lq_ - 1) * qstride + D) * 2);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + c;
-    const int voff = (row * (int)qstride + 8 * g) * 2;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = q0_ + w * 32 * QB + qb * 32 + c;
+      const int voff = (row * (int)qstride + 8 * g) * 2;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = buf_load16(qr, voff + 32 * kk, 0);
-  }
+      for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = buf_load16(qr, voff + 32 * kk, 0);
+    }
+  };
 
   // ---- K / V ring: tile n into slot n % NS, loaded NS - 1 tiles ahead by
   // direct global->LDS loads (row-major, XOR row swizzle dma_swz). Buffers
@@ -128,18 +149,41 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
     const int r = slot / SPR, pos = slot % SPR;
     voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
   }
-  auto issue = [&](int n) {
+  // key tile n of the K / V rows at kb_ / vb_ (kvb_ bytes each) into slot st
+  auto issue_at = [&](const bf16* kb_, const bf16* vb_, int64_t kvb_, int n, int st) {
     // one resource per tile (scalar math): the range check covers the tail
     const int64_t t0 = (int64_t)n * BN * kstride;
-    const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
-    const rsrc_t vr = make_rsrc(vbase + t0, kv_bytes - 2 * t0);
-    const int st = n % NS;
+    const rsrc_t kr = make_rsrc(kb_ + t0, kvb_ - 2 * t0);
+    const rsrc_t vr = make_rsrc(vb_ + t0, kvb_ - 2 * t0);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const uint32_t dst = lds_k + st * TILE + (i * NW + w) * 1024;
       dma16(kr, dst, voffs[i]);
       dma16(vr, dst + VT, voffs[i]);
     }
+  };
+  auto issue = [&](int n) { issue_at(kbase, vbase, kv_bytes, n, (s0 + n) % NS); };
+  // The next tile: its first key tile goes to slot (s0 + n_tiles) % NS, whose
+  // last reader (this tile's key tile n_tiles - NS, or an earlier tile) has
+  // passed a workgroup barrier by the start of this tile's last key tile; its
+  // Q fragments load into qf after this tile's last S^T product.
+  bool nxt_ok = false;
+  int nn = 0, nlq = 0, nlk = 0, nm0 = 0, nh = 0;
+  int64_t nqs = 0, nks = 0;
+  if (has_nxt) {
+    // wave-uniform by construction; kept in scalar registers for the loads'
+    // buffer resources
+    const int nseq = __builtin_amdgcn_readfirstlane(nxt.seq);
+    seq_bounds(p.sv, nseq, &nqs, &nlq, &nks, &nlk);
+    nm0 = __builtin_amdgcn_readfirstlane(nxt.block) * BM;
+    nh = __builtin_amdgcn_readfirstlane(nxt.head);
+    nxt_ok = nm0 < nlq;
+    if (nxt_ok) nn = cdiv(causal ? causal_key_end(nm0 + BM, nlk - nlq, nlk) : nlk, BN);
+  }
+  auto prefetch_kv = [&]() {
+    if (!nxt_ok || nn == 0) return;
+    const int64_t off = nks * kstride + (int64_t)(nh / p.group) * D;
+    issue_at(kp + off, vp + off, ((int64_t)(nlk - 1) * kstride + D) * 2, 0, (s0 + n_tiles) % NS);
   };
   // wait until the next tile is in LDS (with NS = 3 the tile after it may
   // still be in flight), then make it visible to the workgroup
@@ -165,12 +209,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
   const int cl = 2 * dh + ((s16 & 3) >> 1);
   const int a_t = rq * RB + 16 * (cl ^ dma_swz<D>(rq)) + 8 * (s16 & 1);
   uint32_t ar[KS], at[NDB][2];
+  const uint32_t lds_s0 = lds_k + s0 * TILE;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_k + (a_rm ^ (32 * kk));
+  for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_s0 + (a_rm ^ (32 * kk));
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    at[db][0] = lds_k + VT + (a_t ^ (64 * db));
-    at[db][1] = lds_k + VT + (a_t ^ (64 * db + 32)) + 8 * RB;
+    at[db][0] = lds_s0 + VT + (a_t ^ (64 * db));
+    at[db][1] = lds_s0 + VT + (a_t ^ (64 * db + 32)) + 8 * RB;
   }
   auto advance_slot = [&](int st) {
     const int dq = st == NS - 1 ? -(NS - 1) * TILE : TILE;
@@ -191,25 +236,42 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
   }
   const float sl2 = p.scale_log2;
 
-  // ---- prologue: fill NS - 1 slots. The full wait also retires the Q loads,
-  // so the compiler places no wait of its own in the loop (where the ring
-  // loads, which it cannot see, would make it stall).
+  // ---- prologue: Q fragments and NS - 1 ring slots. The full wait also
+  // retires the Q loads, so the compiler places no wait of its own in the loop
+  // (where the ring loads, which it cannot see, would make it stall). After a
+  // prefetch, Q and key tile 0 have landed already (waited for by the previous
+  // tile, on every path that issued them).
+  if (!pre) {
+    load_q(qs, lq, h, m0);
 #pragma unroll
-  for (int n = 0; n < NS - 1; ++n)
-    if (n < n_tiles) issue(n);
-  wait_vm<0>();
+    for (int n = 0; n < NS - 1; ++n)
+      if (n < n_tiles) issue(n);
+    wait_vm<0>();
+  } else {
+#pragma unroll
+    for (int n = 1; n < NS - 1; ++n)
+      if (n < n_tiles) issue(n);
+  }
   __builtin_amdgcn_s_barrier();
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int st = n % NS;
-    if (n + NS - 1 < n_tiles) issue(n + NS - 1);
+  // key tile n; the last one is a separate copy (LAST) that also loads the
+  // next tile's first key tile and Q fragments, so that those loads sit
+  // outside the loop and the compiler tracks no loop-carried load
+  auto k_tile = [&](int n, auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value;
+    const int st = (s0 + n) % NS;
+    if constexpr (LAST) {
+      prefetch_kv();
+    } else {
+      if (n + NS - 1 < n_tiles) issue(n + NS - 1);
+    }
     const int k0 = n * BN;
     const bool active = !(causal && k0 > qw0 + 32 * QB - 1 + shift);
+    f32x16 s[NKB][QB];   // S^T, then P^T in place
     if (active) {
       // S^T = K Q^T for this tile, key block by key block; the mask and the
       // row-max work of block kb run between the MFMAs of block kb + 1
       // (operand fragments streamed two ahead)
-      f32x16 s[NKB][QB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -276,6 +338,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
           mref[qb] = mnew[qb];
         }
       }
+    }
+    // the last key tile's S^T products were the last reads of qf: the next
+    // tile's Q fragments load now, under this tile's PV products
+    if constexpr (LAST) {
+      if (nxt_ok) load_q(nqs, nlq, nh, nm0);
+    }
+    if (active) {
       // P = 2^(s*alpha*log2e - m_ref*alpha*log2e), row sums from fp32 p, and
       // O^T += V^T P^T (A of the PV product by transposing reads of V). Hand
       // schedule: the P work of each 16-key half (8 elements) runs between
@@ -338,8 +407,19 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
       for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb];
     }
     advance_slot(st);
-    if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
+    if constexpr (!LAST) wait_next(n + NS - 1 < n_tiles);
+  };
+  for (int n = 0; n + 1 < n_tiles; ++n) k_tile(n, std::false_type{});
+  if (n_tiles > 0) k_tile(n_tiles - 1, std::true_type{});
+  if (n_tiles == 0) {
+    prefetch_kv();
+    if (nxt_ok) load_q(nqs, nlq, nh, nm0);
   }
+  // the next tile's loads land before this tile's stores queue behind them
+  // (the vector memory counter also counts stores), so the next tile's
+  // prologue need not wait for either; unconditional, so the compiler sees
+  // the Q loads retired on every path
+  wait_vm<0>();
 
   // ---- epilogue: O = O_acc / l (true statistics), LSE = alpha*m + ln(l)
   bf16* __restrict__ op = static_cast<bf16*>(p.o);
@@ -367,29 +447,45 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, const Tile& t, char
       }
     }
   }
+  s0 = XT ? (s0 + n_tiles) % NS : 0;
+  return nxt_ok;
 }
 
 // Persistent workgroups walk the query blocks (schedule.hpp: persistent_index).
+// The next tile is drawn before the current one runs, so that its first loads
+// can go out during the current tile's last key tile.
 template <int D, int NW, int QB, int BN, int EMU>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[fwd_smem_bytes<D, BN>()];
   __shared__ int ticket;
-  for (int r = 0;; ++r) {
-    const FwdParams& p = kernel_args<FwdParams>();
-    const int i = next_tile(r, p.ntiles, p.nxcd, p.queue, &ticket);
-    if (i < 0) break;
-    Tile t;
-    if (p.sv.cu_q) {
-      t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
-      if (t.seq < 0) {
-        if (p.queue) continue;   // a ticket past the last real tile
-        break;
+  auto draw = [&](int& r, Tile& t) -> bool {   // every thread calls it (barriers)
+    for (;;) {
+      const FwdParams& p = kernel_args<FwdParams>();
+      const int i = next_tile(r++, p.ntiles, p.nxcd, p.queue, &ticket);
+      if (i < 0) return false;
+      if (p.sv.cu_q) {
+        t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
+        if (t.seq < 0) {
+          if (p.queue) continue;   // a ticket past the last real tile
+          return false;
+        }
+      } else {
+        t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
       }
-    } else {
-      t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
+      return true;
     }
-    fwd_tile<D, NW, QB, BN, EMU>(p, t, smem);
+  };
+  bf16x8 qf[QB][D / 16];
+  int r = 0, s0 = 0;
+  Tile cur, nxt;
+  bool have = draw(r, cur), pre = false;
+  while (have) {
+    const bool have_next = draw(r, nxt);
+    const FwdParams& p = kernel_args<FwdParams>();
+    pre = fwd_tile<D, NW, QB, BN, EMU>(p, cur, smem, qf, s0, pre, nxt, have_next);
     __syncthreads();   // the next tile's loads reuse the ring slots
+    cur = nxt;
+    have = have_next;
   }
 }
 
