@@ -188,6 +188,11 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--bwd-fused-dq", action="store_true",
                     help="time the fused backward (dQ atomics) instead of dK/dV + dQ kernels")
+    ap.add_argument("--bwd-recompute-dq", action="store_true",
+                    help="dQ kernel recomputing S and dP instead of reading the dS the dK/dV "
+                         "kernel stores")
+    ap.add_argument("--bwd-store-ds", action="store_true",
+                    help="dQ from the dS the dK/dV kernel stores (fixed length)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: forward throughput over tau in {0,4,8,16} x "
                          "exp_emulation in {0,1,2,4} x d in {64,128,256} (B1 H8 S16384 causal, "
@@ -244,6 +249,15 @@ def main() -> int:
     varlen = w.varlen
     lib = ea.load()
     import ctypes
+    if args.bwd_fused_dq:
+        ea.set_tuning("bwd_fused_dq", 1)
+    if args.bwd_store_ds:
+        ea.set_tuning("bwd_store_ds", 1)
+    if args.bwd_recompute_dq:
+        ea.set_tuning("bwd_store_ds", 0)
+    fused = ea.get_tuning("bwd_fused_dq")
+    # the workspace size depends on the backward design (the stored dS lives there)
+    stored_ds = ea.bwd_stores_ds(p, varlen) == 1
     fws = torch.empty(max(1, ea.fwd_workspace_size(p, varlen)), dtype=torch.uint8, device=dev)
     bws = torch.empty(max(1, ea.bwd_workspace_size(p, varlen)), dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -283,10 +297,6 @@ def main() -> int:
         fn()
         b.record()
         marks.setdefault(name, []).append((a, b))
-
-    if args.bwd_fused_dq:
-        ea.set_tuning("bwd_fused_dq", 1)
-    fused = ea.get_tuning("bwd_fused_dq")
 
     def step(on: bool):
         timed("fwd", run_fwd, on)
@@ -356,7 +366,7 @@ def main() -> int:
               "bwd_dq": 1 * half}
     names = {"fwd": f"fwd_kernel<{w.head_dim}>",
              "bwd_main": f"{'bwd_main' if fused else 'bwd_dkdv'}_kernel<{w.head_dim}>",
-             "bwd_dq": f"bwd_dq_kernel<{w.head_dim}>"}
+             "bwd_dq": f"bwd_dq_{'ds_' if stored_ds else ''}kernel<{w.head_dim}>"}
     dom = max((n for n in kms if n in kflops), key=lambda n: kms[n])
     dom_ms = kms[dom]
     dom_name = names[dom]
@@ -378,7 +388,9 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
         "config": {"workload": _describe(w), "pass": w.passes,
-                   "bwd_design": "fused dQ atomics" if fused else "dK/dV kernel + dQ kernel",
+                   "bwd_design": "fused dQ atomics" if fused else
+                                 ("dK/dV kernel storing dS + dQ = dS K kernel" if stored_ds
+                                  else "dK/dV kernel + dQ kernel recomputing S, dP"),
                    "kernels": kernels, "abi_ms": abi, "device": device_info(torch),
                    "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": dom_name,

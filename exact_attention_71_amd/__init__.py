@@ -14,7 +14,8 @@ Entry points mirror the C ABI in ``include/attn71.h``:
     bwd_phases(...)          the backward split into preprocess / main / postprocess
     tile_order(...)          the fixed-length tile schedule, evaluated on the host
     set_tuning(key, value)   process-wide knobs ("tile_order", "persistent", "exp_emulation",
-                             "tau", "spin_limit", "bwd_fused_dq", "fwd_pingpong");
+                             "tau", "spin_limit", "bwd_fused_dq", "fwd_pingpong",
+                             "bwd_store_ds");
                              get_tuning(key) reads back what was set
 """
 from __future__ import annotations
@@ -55,7 +56,7 @@ _vp = ctypes.c_void_p
 EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
-           "attn_persistent_tile",
+           "attn_persistent_tile", "attn_bwd_stores_ds",
            "attn_set_tuning"]
 
 
@@ -83,6 +84,7 @@ def _lib():
     lib.attn_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_int32]
     lib.attn_persistent_tile.argtypes = [ctypes.c_int32] * 5
     lib.attn_persistent_tile.restype = ctypes.c_int32
+    lib.attn_bwd_stores_ds.argtypes = [_P, ctypes.c_int32]
     for n in EXPORTS:
         if n not in ("attn_status_string", "attn_version", "attn_fwd_workspace_size",
                      "attn_bwd_workspace_size"):
@@ -137,6 +139,12 @@ def fwd_workspace_size(p: AttnParams, varlen: bool = False) -> int:
 
 def bwd_workspace_size(p: AttnParams, varlen: bool = False) -> int:
     return _lib().attn_bwd_workspace_size(ctypes.byref(p), int(varlen))
+
+
+def bwd_stores_ds(p: AttnParams, varlen: bool = False) -> int:
+    """1: the backward stores dS and its dQ kernel runs dQ = alpha dS K; 0: dQ
+    recomputes S and dP (or is fused); -1: parameters the calls would reject."""
+    return _lib().attn_bwd_stores_ds(ctypes.byref(p), int(varlen))
 
 
 # --------------------------------------------------------------------- forward
@@ -258,7 +266,7 @@ def persistent_tile(g: int, r: int, grid: int, ntiles: int, nx: int = 8) -> int:
 
 
 _TUNING = {"tile_order": 0, "persistent": 1, "exp_emulation": -1, "tau": 8,
-           "spin_limit": 1 << 26, "bwd_fused_dq": 0, "fwd_pingpong": 0}
+           "spin_limit": 1 << 26, "bwd_fused_dq": 0, "fwd_pingpong": 0, "bwd_store_ds": -1}
 
 
 def set_tuning(key: str, value: int) -> None:

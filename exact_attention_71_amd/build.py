@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libattn71.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip", "varlen.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd_dq_ds.hip", "varlen.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -30,6 +30,8 @@ struct Tuning {
   int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
   int fwd_pingpong = 0;   // 1: phase-offset wave groups (d <= 128); 0: one phase per tile
   int persistent = 1;     // 1: resident workgroups loop over the tiles; 0: one per tile
+  int bwd_store_ds = -1;  // 1: dK/dV kernel stores dS, dQ = dS K (fixed length, split design);
+                          // 0: dQ kernel recomputes S, dP; -1: stored at head_dim 256 only
 };
 Tuning g_tuning;
 
@@ -81,10 +83,21 @@ FwdWs fwd_ws(const attn_params* p, bool varlen) {
 
 struct BwdWs {
   size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, order = 0, tile_prefix = 0, mb_prefix = 0;
-  size_t order_dq = 0, tile_prefix_dq = 0;
+  size_t order_dq = 0, tile_prefix_dq = 0, ds = 0;
   size_t total = 0;
   int64_t n_sem = 0;
+  bool use_ds = false;
+  int ds_nq32 = 0, ds_nk32 = 0;
 };
+// Stored-dS backward: fixed length, split design, and one head's sub-tiles
+// (plus the rows a last query block may address past them) within 32-bit
+// buffer offsets. Otherwise the dQ kernel recomputes S and dP.
+bool bwd_uses_ds(const attn_params* p, bool varlen) {
+  const bool on = g_tuning.bwd_store_ds < 0 ? p->head_dim == 256 : g_tuning.bwd_store_ds != 0;
+  if (!on || g_tuning.bwd_fused_dq || varlen) return false;
+  const int64_t ext = ((int64_t)ds_nq32_of(p->seqlen_q) + 8) * ds_nk32_of(p->seqlen_k) * 2048;
+  return ext <= kMaxExtent;
+}
 int64_t bwd_mblocks(const attn_params* p, bool varlen) {
   const int bm = bwd_block_m(p->head_dim);
   return varlen ? (int64_t)cdiv(p->total_q, bm) + p->batch
@@ -106,6 +119,13 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
     w.mb_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
     w.order_dq = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
     w.tile_prefix_dq = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
+  }
+  if (bwd_uses_ds(p, varlen)) {
+    w.use_ds = true;
+    w.ds_nq32 = ds_nq32_of(p->seqlen_q);
+    w.ds_nk32 = ds_nk32_of(p->seqlen_k);
+    w.ds = off;
+    off = align_up(off + (size_t)p->batch * p->num_heads_q * w.ds_nq32 * w.ds_nk32 * 2048);
   }
   w.total = off;
   return w;
@@ -286,8 +306,14 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.n_sem = fused ? wl.n_sem : 0;
   bp.zero_acc = fused ? 1 : 0;
   bp.spin_limit = g_tuning.spin_limit;
-  const int bmq = dq_block_m(d);
+  const int bmq = wl.use_ds ? DqDsCfg<128>::BM : dq_block_m(d);
   bp.nm_dq = cdiv(p->seqlen_q, bmq);
+  if (wl.use_ds) {
+    bp.ds = base + wl.ds;
+    bp.ds_nq32 = wl.ds_nq32;
+    bp.ds_nk32 = wl.ds_nk32;
+    bp.ntiles_dq = p->batch * p->num_heads_q * bp.nm_dq;
+  }
   bp.sec_dq = section_width(2ll * p->seqlen_k * d * 2);
   if (varlen) {
     bp.order = reinterpret_cast<int*>(base + wl.order);
@@ -324,7 +350,11 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
                                : launch_bwd_dkdv(bp, d, pcus, stream);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
-  if (dqk && launch_bwd_dq(bp, d, pcus, stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (dqk) {
+    const hipError_t e = wl.use_ds ? launch_bwd_dq_ds(bp, d, pcus, stream)
+                                   : launch_bwd_dq(bp, d, pcus, stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
   if (post && launch_bwd_post(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -354,6 +384,11 @@ size_t attn_fwd_workspace_size(const attn_params* p, int32_t varlen) {
 size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen) {
   if (check_params(p, varlen != 0) != ATTN_OK) return (size_t)-1;
   return bwd_ws(p, varlen != 0).total;
+}
+
+int32_t attn_bwd_stores_ds(const attn_params* p, int32_t varlen) {
+  if (check_params(p, varlen != 0) != ATTN_OK) return -1;
+  return bwd_ws(p, varlen != 0).use_ds ? 1 : 0;
 }
 
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o,
@@ -467,6 +502,9 @@ attn_status attn_set_tuning(const char* key, int32_t value) {
   } else if (!std::strcmp(key, "bwd_fused_dq")) {
     if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.bwd_fused_dq = value;
+  } else if (!std::strcmp(key, "bwd_store_ds")) {
+    if (value != -1 && value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
+    g_tuning.bwd_store_ds = value;
   } else if (!std::strcmp(key, "spin_limit")) {
     if (value < 1) return ATTN_ERR_INVALID_ARGUMENT;
     g_tuning.spin_limit = value;

@@ -20,6 +20,10 @@
 // and dP come out with the key on the lane and the query on the register,
 // which is the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS, so P and
 // dS never leave the registers. Each LDS operand fragment feeds KB MFMAs.
+//
+// With DS set the kernel also stores every dS it forms (bf16, the values its
+// dK^T product uses) for the dQ kernel of bwd_dq_ds.hip, which then runs
+// dQ = alpha dS K as its only GEMM instead of recomputing S and dP.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "schedule.hpp"
@@ -33,7 +37,7 @@ template <int D, int BM>
 constexpr int dkdv_smem_bytes() { return 2 * 3 * BM * 2 * D + 3 * 2 * BM * 4; }
 
 // One tile: the keys of key block t.block of (sequence t.seq, KV head t.head).
-template <int D, int KB, int BM>
+template <int D, int KB, int BM, bool DS>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, char* smem) {
   constexpr int NW = 4, NT = NW * 64;
   constexpr int KPW = 32 * KB;          // keys per wave
@@ -120,6 +124,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // itself). Within one sequence the Q / dO byte offsets stay below 2^31.
   const int kvh0 = kvh * p.group;
   int i_h = 0;
+  // Stored dS (DS): sub-tiles of 32 queries x 32 keys per (sequence, query
+  // head), [q32][k32], 2 KiB each: two 1 KiB fragments (16-row halves tt of
+  // the sub-tile), each the 64 lanes' packed B operands of dK^T in lane order,
+  // except that lanes 32..63 swap 64-byte halves (slot L ^ 4), which makes the
+  // dQ kernel's transposing reads conflict-free. ds_cur: the head of the
+  // compute cursor.
+  const int ds_nk32 = p.ds_nk32;
+  const int ds_bh = p.ds_nq32 * ds_nk32 * 2048;
+  const char* ds_cur = nullptr;
+  if constexpr (DS) ds_cur = keep_sgpr(p.ds + ((int64_t)t.seq * p.hq + kvh0) * ds_bh);
   const int64_t q_tile = (qs * qstride + (int64_t)kvh0 * D) * 2;
   const char* const q_seq = keep_sgpr(static_cast<const char*>(p.q) + q_tile);
   const char* const do_seq = keep_sgpr(static_cast<const char*>(p.dout) + q_tile);
@@ -346,6 +360,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mfma32_agpr<false>(dk[kb][db], cur, sb[qb][kb][tt]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DS) {
+          if (db == NDB - 1) {   // last read of sb[qb][*][tt]: store it (waited for a step later)
+            const rsrc_t dr = raw_rsrc(ds_cur, ds_bh);
+            const int so = ((mq0 >> 5) * ds_nk32 + (wk0 >> 5)) * 2048;
+            // lane offset recomputed here from an opaque lane id: kept live
+            // across the step it costs a VGPR
+            const int ln = opaque_lane_id();
+            const int ds_voff = (ln ^ ((ln >> 5) << 2)) << 4;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              buf_store16_nt(dr, ds_voff, so + (qb * ds_nk32 + kb) * 2048 + tt * 1024, sb[qb][kb][tt]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
         if (x == 1 && iss >= 0) {
           issue(__builtin_amdgcn_readfirstlane(iss));
           __builtin_amdgcn_sched_barrier(0);
@@ -368,7 +396,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   bf16x8 f0 = fetch_first(0, 0), f1 = fetch_first(1, 0);
   for (int step = 0; step < n_steps; ++step) {
     const int mq0 = c_m * BM;
-    if (++c_m == nm) c_m = m_first;
+    const bool wrap = ++c_m == nm;
+    if (wrap) c_m = m_first;
     const bool has_next = step + 1 < n_steps;
     const int iss = step + NS - 1 < n_steps ? (st == 0 ? NS - 1 : st - 1) : -1;  // (step + 2) % NS
     const int nxt = st == NS - 1 ? -(NS - 1) * TILE : TILE;                      // next slot
@@ -378,6 +407,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     // of the AGPR accumulators with spills.
     const bool need_mask = (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
     step_body(mq0, need_mask, f0, f1, has_next, iss, nxt);
+    if constexpr (DS) {
+      if (wrap) ds_cur = keep_sgpr(ds_cur + ds_bh);
+    }
     advance_slot(st);
     st = st == NS - 1 ? 0 : st + 1;
   }
@@ -412,7 +444,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 
 // Persistent workgroups walk the tiles (schedule.hpp: persistent_index); a
 // one-shot grid (gridDim.x == ntiles) gives each workgroup one tile.
-template <int D, int KB, int BM>
+template <int D, int KB, int BM, bool DS>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM>()];
   __shared__ int ticket;
@@ -430,18 +462,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
     } else {
       t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, false, p.nxcd, p.natural != 0);
     }
-    dkdv_tile<D, KB, BM>(p, t, smem);
+    dkdv_tile<D, KB, BM, DS>(p, t, smem);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }
 
+template <int D, bool DS>
+hipError_t launch_dkdv_t(const BwdParams& p, int cus, hipStream_t stream) {
+  using C = DkdvCfg<D>;
+  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM, DS>, 256);
+  const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM, DS>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 template <int D>
 hipError_t launch_dkdv_d(const BwdParams& p, int cus, hipStream_t stream) {
-  using C = DkdvCfg<D>;
-  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM>, 256);
-  const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM>), dim3(grid), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return p.ds ? launch_dkdv_t<D, true>(p, cus, stream) : launch_dkdv_t<D, false>(p, cus, stream);
 }
 
 }  // namespace

@@ -1,0 +1,229 @@
+// dQ of the attention backward from the dS the dK/dV kernel stored.
+//
+// dQ_i = alpha * sum_j dS_ij k_j (FlashAttention-4 blog page, backward
+// section: dQ is the product of dS with the key block). The dK/dV kernel
+// already forms every dS_ij in bf16 for its dK product; with the stored-dS
+// option it writes them out (2 bytes per visible pair), and this kernel runs
+// dQ as a single GEMM over them instead of recomputing S, P and dP (two more
+// GEMMs and the exponentials). It is bound by the dS stream from HBM: 2 bytes
+// per pair against 2 d flops.
+//
+// Per workgroup: NW wavefronts x 32 query rows of one (sequence, query head).
+// Per key tile of BN keys, the K tile (row-major, XOR row swizzle dma_swz) and
+// each wave's own BN x 32 block of dS stream into a three-deep LDS ring by
+// direct global->LDS loads issued two tiles ahead. Both MFMA operands of
+// dQ^T += K^T dS^T come from transposing LDS reads (ds_read_b64_tr_b16): K^T
+// from the K tile as in bwd_dq.hip, dS^T from the stored sub-tiles, whose
+// 8-byte chunks hold four queries of one key. dQ is written once, in bf16, so
+// the result is bit-reproducible.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "schedule.hpp"
+
+namespace attn71 {
+
+namespace {
+
+// LDS of one workgroup: [NS] K tiles | [NS][NW] per-wave dS blocks
+template <int D>
+constexpr int dqds_smem_bytes() {
+  using C = DqDsCfg<D>;
+  return 3 * C::BN * 2 * D + 3 * C::NW * C::BN * 64;
+}
+
+// One tile: query block t.block of (sequence t.seq, query head t.head).
+template <int D>
+__device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, char* smem) {
+  using C = DqDsCfg<D>;
+  constexpr int NW = C::NW, NT = NW * 64, BM = C::BM, BN = C::BN;
+  constexpr int NKB = BN / 32;          // 32-key sub-tiles per key tile
+  constexpr int NDB = D / 32;           // 32-dim blocks of dQ^T
+  constexpr int RB = 2 * D;             // bytes per K row
+  constexpr int SPR = D / 8;            // 16-byte slots per K row
+  constexpr int TILE = BN * RB;         // bytes of one K tile
+  constexpr int DSW = BN * 64;          // bytes of one wave's dS block (32 queries x BN keys)
+  constexpr int NS = 3;                 // ring depth
+  static_assert(NS == 3, "loads run two tiles ahead");
+  constexpr int CH = TILE / (16 * NT);  // K dma16 per thread per tile
+  constexpr int CD = DSW / 1024;        // dS dma16 per wave per tile
+  static_assert(CH * 16 * NT == TILE && CD * 1024 == DSW, "tile split over the workgroup");
+  constexpr int OPS = CH + CD;          // ring loads per thread per tile
+  static_assert(OPS < 64, "vmcnt range");
+  static_assert(dqds_smem_bytes<D>() == NS * TILE + NS * NW * DSW, "LDS layout");
+  const uint32_t lds_k = lds_addr(smem);
+  const uint32_t lds_s = lds_k + NS * TILE;
+
+  const int lq = p.sv.seqlen_q, lk = p.sv.seqlen_k;
+  const int64_t qs = (int64_t)t.seq * lq, ks0 = (int64_t)t.seq * lk;
+  const int m0 = t.block * BM;
+  if (m0 >= lq) return;
+  const int h = t.head;
+  const int kvh = h / p.group;
+  const bool causal = p.causal != 0;
+  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
+  const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
+
+  const int tid = tile_tid();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int qw0 = m0 + w * 32;
+  const int myq = qw0 + c;
+  const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
+
+  // ---- K ring (as in bwd_dq.hip): keys past the sequence read as zero
+  const int64_t kv_bytes = ((int64_t)(lk - 1) * kstride + D) * 2;
+  const bf16* kbase = static_cast<const bf16*>(p.k) + ks0 * kstride + (int64_t)kvh * D;
+  int voffs[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int slot = (i * NW + w) * 64 + lane;
+    const int r = slot / SPR, pos = slot % SPR;
+    voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
+  }
+  // ---- this wave's dS: sub-tile row qw0 / 32 of the head, NKB sub-tiles
+  // (contiguous, 2 KiB each) per key tile. Reads past the head's range give
+  // zero; a wave whose rows all lie past the sequence skips its MFMAs.
+  const int nk32 = p.ds_nk32;
+  const int ds_bh = p.ds_nq32 * nk32 * 2048;
+  const rsrc_t dsr = raw_rsrc(p.ds + ((int64_t)t.seq * p.hq + h) * ds_bh, ds_bh);
+  const int ds_row = (qw0 >> 5) * nk32 * 2048 + lane * 16;
+  auto issue = [&](int n) {
+    const int64_t t0 = (int64_t)n * BN * kstride;
+    const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
+    const int st = n % NS;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(kr, lds_k + st * TILE + (i * NW + w) * 1024, voffs[i]);
+#pragma unroll
+    for (int i = 0; i < CD; ++i)
+      dma16_nt(dsr, lds_s + (st * NW + w) * DSW + i * 1024, ds_row + n * NKB * 2048 + i * 1024);
+  };
+
+  // K^T by transposing reads (see bwd_dq.hip): 16-lane group (g, dh), lane
+  // s16 reads key row 4g + s16/4 (+8 for k slots 4..7), dims 32db + 16dh +
+  // 4(s16%4).
+  const int s16 = lane & 15, dh = (lane >> 4) & 1;
+  const int rq = 4 * g + (s16 >> 2);
+  const int cl = 2 * dh + ((s16 & 3) >> 1);
+  const int a_t = rq * RB + 16 * (cl ^ dma_swz<D>(rq)) + 8 * (s16 & 1);
+  uint32_t at[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    at[db][0] = lds_k + (a_t ^ (64 * db));
+    at[db][1] = lds_k + (a_t ^ (64 * db + 32)) + 8 * RB;
+  }
+  // dS^T by transposing reads. In a stored sub-tile, 16-row half tt' holds at
+  // 16-byte slot L ^ (4 (L >= 32)) the chunks (queries 16tt' + 4g' + 0..3,
+  // then + 8) of key c' for lane L = c' + 32g'. The B operand wants, in lane
+  // (query 16dh + s16, g), keys 16tt + 4g + j (slots 0..3) and 16tt + 8 + 4g + j
+  // (slots 4..7), the k order of K^T above. So lane s16 of the group points at
+  // the chunk of key 16tt + 8hh + 4g + s16/4 and queries 16dh + 4(s16%4) .. +3:
+  // tt' = dh, chunk (s16 >> 1) & 1, g' = s16 & 1. Per 16-lane group the 16
+  // chunks cover one 128-byte bank window.
+  const int sl = s16 & 1;
+  const int b_t = dh * 1024 + (32 * sl + ((4 * g + (s16 >> 2)) ^ (4 * sl))) * 16 + ((s16 >> 1) & 1) * 8;
+  const uint32_t bt = lds_s + w * DSW + b_t;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  // Key tile in ring slot st, its first NV sub-tiles (the visible ones).
+  auto body = [&](int st, auto nv) {
+    constexpr int NV = decltype(nv)::value;
+    const uint32_t ko = st * TILE, so = st * NW * DSW;
+#pragma unroll
+    for (int kb = 0; kb < NV; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t bo = so + kb * 2048 + 256 * tt;
+        const bf16x8 b = cat8(ds_read_tr(bt + bo), ds_read_tr(bt + bo + 128));
+        const uint32_t off = ko + (kb * 32 + 16 * tt) * RB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 a = cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
+          acc[db] = mfma32(a, b, acc[db]);
+        }
+      }
+  };
+  auto wait_next = [&](bool later_issued) {
+    if (later_issued) wait_vm<OPS>(); else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, wait for tile 0
+#pragma unroll
+  for (int n = 0; n < NS - 1; ++n)
+    if (n < n_tiles) issue(n);
+  wait_next(n_tiles > 1);
+
+  const bool rows_live = qw0 < lq;
+  for (int n = 0; n < n_tiles; ++n) {
+    const int st = n % NS;
+    if (n + NS - 1 < n_tiles) issue(n + NS - 1);
+    const int k0 = n * BN;
+    // sub-tiles with a visible pair for some row of this wave (the dK/dV
+    // kernel wrote exactly those; the rest of the tile is never read)
+    const int lim = causal ? qw0 + 31 + shift - k0 : BN - 1;
+    const int nv = !rows_live || lim < 0 ? 0 : imin(lim / 32 + 1, NKB);
+    if (nv == NKB) body(st, std::integral_constant<int, NKB>{});
+    else if constexpr (NKB > 1) {
+      if (nv == 1) body(st, std::integral_constant<int, 1>{});
+    }
+    if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
+  }
+
+  // ---- dQ = alpha * dQ^T, bf16, this lane's query row
+  if (myq < lq) {
+    bf16* dst = static_cast<bf16*>(p.dq) + (qs + myq) * qstride + (int64_t)h * D + 4 * g;
+    const float a = p.alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& x = acc[db];
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * j) =
+            pack4(x[4 * j] * a, x[4 * j + 1] * a, x[4 * j + 2] * a, x[4 * j + 3] * a);
+      }
+  }
+}
+
+// Persistent workgroups walk the query blocks (schedule.hpp: persistent_index).
+template <int D>
+__global__ __launch_bounds__(DqDsCfg<D>::NW * 64, 1) void bwd_dq_ds_kernel(BwdParams) {
+  __shared__ __attribute__((aligned(1024))) char smem[dqds_smem_bytes<D>()];
+  __shared__ int ticket;
+  for (int r = 0;; ++r) {
+    const BwdParams& p = kernel_args<BwdParams>();
+    const int i = next_tile(r, p.ntiles_dq, p.nxcd, nullptr, &ticket);
+    if (i < 0) break;
+    const Tile t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
+    dqds_tile<D>(p, t, smem);
+    __syncthreads();   // the next tile's loads reuse the ring slots
+  }
+}
+
+template <int D>
+hipError_t launch_dq_ds_d(const BwdParams& p, int cus, hipStream_t stream) {
+  using C = DqDsCfg<D>;
+  static const int occ = resident_per_cu(bwd_dq_ds_kernel<D>, C::NW * 64);
+  const int grid = persistent_grid(p.ntiles_dq, cus * occ, p.nxcd);
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<D>), dim3(grid), dim3(C::NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_ds(const BwdParams& p, int d, int cus, hipStream_t stream) {
+  if (!p.ds || p.sv.cu_q) return hipErrorInvalidValue;
+  if (p.ntiles_dq <= 0) return hipSuccess;
+  switch (d) {
+    case 64: return launch_dq_ds_d<64>(p, cus, stream);
+    case 128: return launch_dq_ds_d<128>(p, cus, stream);
+    case 256: return launch_dq_ds_d<256>(p, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn71

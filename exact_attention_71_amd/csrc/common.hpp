@@ -233,6 +233,14 @@ __device__ __forceinline__ int next_tile(int r, int ntiles, int nx, unsigned* qu
   return i < ntiles ? i : -1;
 }
 
+// Lane id (0..63) read where it is used: the asm cannot be hoisted out of a
+// loop, so no register holds it across the loop body.
+__device__ __forceinline__ int opaque_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // threadIdx.x through an opaque copy: values derived from it inside a
 // persistent loop's tile body are then recomputed per tile rather than
 // hoisted in front of the loop and kept live (in VGPRs) across all tiles.
@@ -274,6 +282,12 @@ __device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(bf16x8, x);
 }
 
+// Streaming store (cache policy nt: data written once and read back much
+// later by another kernel, kept from displacing reused lines in L2).
+__device__ __forceinline__ void buf_store16_nt(rsrc_t r, int voff, int soff, const bf16x8& x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 2);
+}
+
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
@@ -294,6 +308,12 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, int voff, int soff) {
 // and an LDS-DMA read of it. Nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_byte, int voff) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(lds_byte), "s"(r) : "memory", "m0");
+}
+
+// dma16 with cache policy nt (a stream read once).
+__device__ __forceinline__ void dma16_nt(rsrc_t r, uint32_t lds_byte, int voff) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
                :: "v"(voff), "s"(lds_byte), "s"(r) : "memory", "m0");
 }
 

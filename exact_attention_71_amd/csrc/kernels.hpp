@@ -79,7 +79,19 @@ struct BwdParams {
   int64_t rows_q;         // total query rows (B*Sq or total_q)
   int64_t n_sem;          // semaphore words to clear (deterministic)
   int spin_limit;         // bounded wait for the deterministic chain
+  // Stored dS (fixed length only; null: the dQ kernel recomputes S and dP).
+  // Per (sequence, query head): ds_nq32 x ds_nk32 sub-tiles of 32 queries x
+  // 32 keys, bf16, 2 KiB each, in the register order of the dK/dV kernel
+  // (ds_subtile_offset).
+  char* ds;
+  int ds_nq32, ds_nk32;
 };
+
+// Stored-dS geometry: query blocks of 32 rounded to the dK/dV step (64 rows
+// at most), key blocks of 32 rounded to the dK/dV workgroup (256 keys at
+// most), so every sub-tile the dK/dV kernel writes lies inside its head.
+inline int ds_nq32_of(int seqlen_q) { return (seqlen_q + 63) / 64 * 2; }
+inline int ds_nk32_of(int seqlen_k) { return (seqlen_k + 255) / 256 * 8; }
 
 // Tile sizes (rows of the query block and keys of the key block) per head dim.
 #ifndef ATTN71_FWD_NW
@@ -108,6 +120,12 @@ template <int D> struct DqCfg {
   static constexpr int BN = (D <= 128) ? 64 : 32; // keys per tile
 };
 inline int dq_block_m(int d) { return d <= 128 ? DqCfg<128>::BM : DqCfg<256>::BM; }
+
+template <int D> struct DqDsCfg {
+  static constexpr int NW = 8;                    // wavefronts, 32 query rows each
+  static constexpr int BM = NW * 32;
+  static constexpr int BN = (D <= 128) ? 64 : 32; // keys per tile
+};
 
 template <int D> struct DkdvCfg {
   static constexpr int KB = (D <= 128) ? 2 : 1;   // 32-key blocks per wavefront
@@ -151,6 +169,8 @@ hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipS
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int cus, hipStream_t stream);
 // dQ without atomics: one workgroup per query block (see bwd_dq.hip).
 hipError_t launch_bwd_dq(const BwdParams& p, int d, int cus, hipStream_t stream);
+// dQ = alpha dS K from the dS the dK/dV kernel stored (p.ds; see bwd_dq_ds.hip).
+hipError_t launch_bwd_dq_ds(const BwdParams& p, int d, int cus, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
 // Varlen pre-pass: order[] = sequences by decreasing length of key_cu (ties
 // by index), tile_prefix[vs] = first tile of virtual sequence vs with

@@ -101,6 +101,14 @@ int attn_version(void);
 size_t attn_fwd_workspace_size(const attn_params* p, int32_t varlen);
 size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen);
 
+/* 1 if a backward call with these parameters, under the current tuning
+ * (attn_set_tuning "bwd_store_ds", "bwd_fused_dq"), has its dK/dV kernel store
+ * dS into the workspace and computes dQ = alpha dS K from it; 0 if its dQ
+ * kernel recomputes S and dP (or dQ is fused); -1 for parameters the calls
+ * would reject. The stored dS takes B * Hq * ceil(Sq/64)*2 * ceil(Sk/256)*8
+ * * 2 KiB of the workspace (about 2 bytes per query-key pair). */
+int32_t attn_bwd_stores_ds(const attn_params* p, int32_t varlen);
+
 /* Forward, fixed length. lse may be NULL (the LSE is optional on the pages:
  * blog page, correction-warpgroup list, "optionally compute and store LSE"). */
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o,
@@ -124,7 +132,12 @@ attn_status attn_fwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  *   1 main = one kernel that also adds each tile's dQ into an fp32 buffer with
  *     atomics (blog page, 2-CTA backward, dQ atomic accumulation), or, with
  *     deterministic = 1, in a fixed order behind per-block semaphores (blog
- *     page, deterministic mode); postprocess converts dQ to bf16. */
+ *     page, deterministic mode); postprocess converts dQ to bf16.
+ * In the split design the dQ kernel either recomputes S and dP from q, k, v,
+ * dout and lse, or (fixed length, attn_bwd_stores_ds = 1) reads the dS that
+ * the dK/dV kernel wrote into the workspace and runs dQ = alpha dS K, its
+ * only GEMM (blog page, backward section: dQ is dS times the key block).
+ * Both write dQ once: bit-reproducible either way. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -146,7 +159,9 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  * PREPROCESS phase of the same workspace before it: it clears the dQ
  * accumulator and, in deterministic mode, the ordering state. A MAIN phase
  * run without it still terminates and stays in bounds, but dQ accumulates on
- * the previous values and the deterministic order is not guaranteed. */
+ * the previous values and the deterministic order is not guaranteed. When
+ * the call stores dS (attn_bwd_stores_ds), the DQ phase reads what the MAIN
+ * phase of the same workspace wrote: run MAIN before DQ. */
 #define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); fused design: clear dQ accumulator, semaphores */
 #define ATTN_BWD_MAIN 2        /* key-block kernel: dK, dV (fused design: + dQ accumulation) */
 #define ATTN_BWD_POSTPROCESS 4 /* fused design: dQ = bf16(alpha * accumulator); else nothing */
@@ -207,7 +222,15 @@ int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles,
  *                   3; blog page, forward section). 0 rescales on every
  *                   increase of the row max;
  *   "spin_limit"    bound on each wait of the deterministic chain (default
- *                   2^26 polls).
+ *                   2^26 polls);
+ *   "bwd_store_ds"  split backward, fixed length: -1 = automatic (default:
+ *                   stored dS at head_dim 256, where it measured 12 % faster
+ *                   per fwd+bwd step; recomputation at 64 and 128, where the
+ *                   dK/dV kernel's extra writes cost more than the dQ kernel
+ *                   saves), 1 = the dK/dV kernel stores dS and dQ = alpha dS K,
+ *                   0 = the dQ kernel recomputes S and dP. Packed variable
+ *                   lengths always recompute; so do heads whose stored dS
+ *                   would exceed 2 GiB.
  * Returns ATTN_ERR_INVALID_ARGUMENT for unknown keys or values. */
 attn_status attn_set_tuning(const char* key, int32_t value);
 

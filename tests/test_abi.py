@@ -255,3 +255,36 @@ def test_persistent_knob():
     with pytest.raises(ea.AttnError):
         ea.set_tuning("persistent", 2)
     ea.set_tuning("persistent", 1)
+
+
+def test_stored_ds_selection_and_workspace():
+    """Stored dS: automatic at head_dim 256 only, never for packed variable
+    lengths or the fused design; its workspace holds 2 KiB per 32 x 32
+    sub-tile of every (sequence, query head)."""
+    try:
+        for d, auto in ((64, 0), (128, 0), (256, 1)):
+            p = ea.make_params(2, 300, 700, 4, 2, d, 0.1, True, False)
+            base_ws = None
+            for mode, want in ((-1, auto), (0, 0), (1, 1)):
+                ea.set_tuning("bwd_store_ds", mode)
+                assert ea.bwd_stores_ds(p) == want, (d, mode)
+                assert ea.bwd_stores_ds(p, varlen=True) == 0
+                ws = ea.bwd_workspace_size(p)
+                if mode == 0:
+                    base_ws = ws
+            ea.set_tuning("bwd_store_ds", 1)
+            nq32, nk32 = -(-300 // 64) * 2, -(-700 // 256) * 8
+            extra = 2 * 4 * nq32 * nk32 * 2048
+            assert ea.bwd_workspace_size(p) - base_ws >= extra
+            assert ea.bwd_workspace_size(p) - base_ws < extra + 256
+            ea.set_tuning("bwd_fused_dq", 1)
+            assert ea.bwd_stores_ds(p) == 0
+            ea.set_tuning("bwd_fused_dq", 0)
+        # one head's sub-tiles beyond 32-bit buffer offsets: recomputation
+        big = ea.make_params(1, 40000, 40000, 1, 1, 256, 0.1, True, False)
+        assert ea.bwd_stores_ds(big) == 0
+        with pytest.raises(ea.AttnError):
+            ea.set_tuning("bwd_store_ds", 2)
+    finally:
+        ea.set_tuning("bwd_store_ds", -1)
+        ea.set_tuning("bwd_fused_dq", 0)

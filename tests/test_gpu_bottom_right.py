@@ -20,15 +20,17 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(params=[(0, 0), (1, 0), (1, 1)],
-                ids=["plainfwd-splitdq", "pingpong-splitdq", "pingpong-fuseddq"])
+@pytest.fixture(params=[(0, 0, 0), (1, 0, 0), (1, 1, 0), (0, 0, 1)],
+                ids=["plainfwd-splitdq", "pingpong-splitdq", "pingpong-fuseddq", "plainfwd-storedds"])
 def design(request):
-    pp, fused = request.param
+    pp, fused, ds = request.param
     ea.set_tuning("fwd_pingpong", pp)
     ea.set_tuning("bwd_fused_dq", fused)
+    ea.set_tuning("bwd_store_ds", ds)
     yield request.param
     ea.set_tuning("fwd_pingpong", 0)
     ea.set_tuning("bwd_fused_dq", 0)
+    ea.set_tuning("bwd_store_ds", -1)
 
 
 def _dev(inp):

@@ -107,6 +107,18 @@ def test_causal8k_full_size_fwd_bwd():
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)   # same dK/dV arithmetic
     _check_grads_sampled(dq2, dk2, dv2, q, k, v, do, 0, 1, 1, w.scale, True, rows, cols,
                          "causal8k fused bwd")
+    del dq2, dk2, dv2
+    # dQ from the dS the dK/dV kernel stores (4 GiB of workspace at this size)
+    ea.set_tuning("bwd_store_ds", 1)
+    try:
+        dq3, dk3, dv3 = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale)
+        torch.cuda.synchronize()
+    finally:
+        ea.set_tuning("bwd_store_ds", -1)
+    assert torch.equal(dk, dk3) and torch.equal(dv, dv3)   # same dK/dV arithmetic
+    for b, h in ((0, 1), (1, 9)):
+        _check_grads_sampled(dq3, dk3, dv3, q, k, v, do, b, h, 1, w.scale, True, rows, cols,
+                             f"causal8k stored-dS bwd b{b} h{h}")
 
 
 def test_varlen_gqa_full_size_fwd_bwd():
@@ -146,21 +158,22 @@ def test_varlen_gqa_full_size_fwd_bwd():
 
 @pytest.mark.parametrize("name", ["det16k_d64", "det16k_d128", "det16k_d256"])
 def test_det16k_full_size_bit_identical_and_parity(name):
-    """Both backward designs: the split one (no atomics) and the fused one with
-    its semaphore-ordered dQ; each bit-identical over 3 runs and within the
-    parity bar."""
+    """Every backward design: the split one (no atomics, dQ recomputing S and
+    dP or reading the stored dS) and the fused one with its semaphore-ordered
+    dQ; each bit-identical over 3 runs and within the parity bar."""
     w = WORKLOADS[name]
     inp = workload_inputs(w, device=DEV)
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
     o, lse = ea.fwd(q, k, v, causal=True, softmax_scale=w.scale)
     p = ea.make_params(1, w.seqlen, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, w.scale, True, True)
-    ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
     rows = _rows(w.seqlen, extra=16, seed=7)
     cols = _rows(w.seqlen, extra=4, seed=8)
     _check_rows(o, lse, q, k, v, 0, 5, 5, w.scale, True, rows, name)
-    for fused in (0, 1):
+    for fused, stored in ((0, 0), (1, 0), (0, 1)):
         ea.set_tuning("bwd_fused_dq", fused)
+        ea.set_tuning("bwd_store_ds", stored)
         try:
+            ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
             runs = []
             for _ in range(3):
                 runs.append(ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale,
@@ -169,10 +182,12 @@ def test_det16k_full_size_bit_identical_and_parity(name):
                 assert ea.bwd_status(p, ws) == 0
         finally:
             ea.set_tuning("bwd_fused_dq", 0)
+            ea.set_tuning("bwd_store_ds", -1)
+        del ws
         for r in runs[1:]:
             for a, b in zip(runs[0], r):
-                assert torch.equal(a, b), (name, fused)
+                assert torch.equal(a, b), (name, fused, stored)
         dq, dk, dv = runs[0]
-        what = f"{name} fused={fused}"
+        what = f"{name} fused={fused} stored_ds={stored}"
         _check_grads_sampled(dq, dk, dv, q, k, v, do, 0, 2, 1, w.scale, True, rows, cols, what)
         _identities(dk, dv, do, 1, what)

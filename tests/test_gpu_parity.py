@@ -19,17 +19,20 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(params=[(1, 0), (0, 0), (1, 1)],
-                ids=["pingpong-splitdq", "plainfwd-splitdq", "pingpong-fuseddq"])
+@pytest.fixture(params=[(1, 0, 0), (0, 0, 0), (1, 1, 0), (0, 0, 1)],
+                ids=["pingpong-splitdq", "plainfwd-splitdq", "pingpong-fuseddq", "plainfwd-storedds"])
 def bwd_mode(request):
     """Kernel designs under test: forward ping-pong on/off, backward with the
-    separate dQ kernel or with fused dQ atomics."""
-    pp, fused = request.param
+    separate dQ kernel (recomputing S and dP, or from the dS the dK/dV kernel
+    stored; packed variable lengths always recompute) or with fused dQ atomics."""
+    pp, fused, ds = request.param
     ea.set_tuning("fwd_pingpong", pp)
     ea.set_tuning("bwd_fused_dq", fused)
+    ea.set_tuning("bwd_store_ds", ds)
     yield request.param
     ea.set_tuning("fwd_pingpong", 0)
     ea.set_tuning("bwd_fused_dq", 0)
+    ea.set_tuning("bwd_store_ds", -1)
 
 
 def _dev(inp):
