@@ -31,7 +31,7 @@ struct Tuning {
   int fwd_pingpong = 0;   // 1: phase-offset wave groups (d <= 128); 0: one phase per tile
   int persistent = 1;     // 1: resident workgroups loop over the tiles; 0: one per tile
   int bwd_store_ds = -1;  // 1: dK/dV kernel stores dS, dQ = dS K (fixed length, split design);
-                          // 0: dQ kernel recomputes S, dP; -1: stored at head_dim 256 only
+                          // 0: dQ kernel recomputes S, dP; -1: stored at head_dim >= 128
 };
 Tuning g_tuning;
 
@@ -93,7 +93,7 @@ struct BwdWs {
 // (plus the rows a last query block may address past them) within 32-bit
 // buffer offsets. Otherwise the dQ kernel recomputes S and dP.
 bool bwd_uses_ds(const attn_params* p, bool varlen) {
-  const bool on = g_tuning.bwd_store_ds < 0 ? p->head_dim == 256 : g_tuning.bwd_store_ds != 0;
+  const bool on = g_tuning.bwd_store_ds < 0 ? p->head_dim >= 128 : g_tuning.bwd_store_ds != 0;
   if (!on || g_tuning.bwd_fused_dq || varlen) return false;
   const int64_t ext = ((int64_t)ds_nq32_of(p->seqlen_q) + 8) * ds_nk32_of(p->seqlen_k) * 2048;
   return ext <= kMaxExtent;

@@ -9,9 +9,11 @@
 // per pair against 2 d flops.
 //
 // Per workgroup: NW wavefronts x 32 query rows of one (sequence, query head).
-// Per key tile of BN keys, the K tile (row-major, XOR row swizzle dma_swz) and
-// each wave's own BN x 32 block of dS stream into a three-deep LDS ring by
-// direct global->LDS loads issued two tiles ahead. Both MFMA operands of
+// Per key tile of BN keys, the K tile (row-major, XOR row swizzle dma_swz)
+// streams into a three-deep LDS ring and each wave's own BN x 32 block of dS
+// into an NSD-deep one, both by direct global->LDS loads (dS NSD - 1 tiles
+// ahead: the HBM latency needs ~100 KiB of it in flight per CU, K comes from
+// L2 and needs only two tiles). Both MFMA operands of
 // dQ^T += K^T dS^T come from transposing LDS reads (ds_read_b64_tr_b16): K^T
 // from the K tile as in bwd_dq.hip, dS^T from the stored sub-tiles, whose
 // 8-byte chunks hold four queries of one key. dQ is written once, in bf16, so
@@ -26,11 +28,11 @@ namespace attn71 {
 
 namespace {
 
-// LDS of one workgroup: [NS] K tiles | [NS][NW] per-wave dS blocks
+// LDS of one workgroup: [3] K tiles | [NSD][NW] per-wave dS blocks
 template <int D>
 constexpr int dqds_smem_bytes() {
   using C = DqDsCfg<D>;
-  return 3 * C::BN * 2 * D + 3 * C::NW * C::BN * 64;
+  return 3 * C::BN * 2 * D + C::NSD * C::NW * C::BN * 64;
 }
 
 // One tile: query block t.block of (sequence t.seq, query head t.head).
@@ -44,14 +46,15 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
   constexpr int SPR = D / 8;            // 16-byte slots per K row
   constexpr int TILE = BN * RB;         // bytes of one K tile
   constexpr int DSW = BN * 64;          // bytes of one wave's dS block (32 queries x BN keys)
-  constexpr int NS = 3;                 // ring depth
-  static_assert(NS == 3, "loads run two tiles ahead");
+  constexpr int NS = 3;                 // K ring depth
+  static_assert(NS == 3, "K loads run two tiles ahead");
+  constexpr int NSD = C::NSD;           // dS ring depth
+  static_assert(NSD >= 4, "dS loads run at least as far ahead as the K loads");
   constexpr int CH = TILE / (16 * NT);  // K dma16 per thread per tile
   constexpr int CD = DSW / 1024;        // dS dma16 per wave per tile
   static_assert(CH * 16 * NT == TILE && CD * 1024 == DSW, "tile split over the workgroup");
-  constexpr int OPS = CH + CD;          // ring loads per thread per tile
-  static_assert(OPS < 64, "vmcnt range");
-  static_assert(dqds_smem_bytes<D>() == NS * TILE + NS * NW * DSW, "LDS layout");
+  static_assert(2 * CD + CH < 64 && (NSD - 1) * CD + 2 * CH < 64, "vmcnt range");
+  static_assert(dqds_smem_bytes<D>() == NS * TILE + NSD * NW * DSW, "LDS layout");
   const uint32_t lds_k = lds_addr(smem);
   const uint32_t lds_s = lds_k + NS * TILE;
 
@@ -89,15 +92,18 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
   const int ds_bh = p.ds_nq32 * nk32 * 2048;
   const rsrc_t dsr = raw_rsrc(p.ds + ((int64_t)t.seq * p.hq + h) * ds_bh, ds_bh);
   const int ds_row = (qw0 >> 5) * nk32 * 2048 + lane * 16;
-  auto issue = [&](int n) {
+  auto issue_k = [&](int n) {
     const int64_t t0 = (int64_t)n * BN * kstride;
     const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
     const int st = n % NS;
 #pragma unroll
     for (int i = 0; i < CH; ++i) dma16(kr, lds_k + st * TILE + (i * NW + w) * 1024, voffs[i]);
+  };
+  auto issue_ds = [&](int n) {
+    const int sd = n % NSD;
 #pragma unroll
     for (int i = 0; i < CD; ++i)
-      dma16_nt(dsr, lds_s + (st * NW + w) * DSW + i * 1024, ds_row + n * NKB * 2048 + i * 1024);
+      dma16_nt(dsr, lds_s + (sd * NW + w) * DSW + i * 1024, ds_row + n * NKB * 2048 + i * 1024);
   };
 
   // K^T by transposing reads (see bwd_dq.hip): 16-lane group (g, dh), lane
@@ -129,10 +135,11 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  // Key tile in ring slot st, its first NV sub-tiles (the visible ones).
-  auto body = [&](int st, auto nv) {
+  // Key tile in K ring slot st and dS ring slot sd, its first NV sub-tiles
+  // (the visible ones).
+  auto body = [&](int st, int sd, auto nv) {
     constexpr int NV = decltype(nv)::value;
-    const uint32_t ko = st * TILE, so = st * NW * DSW;
+    const uint32_t ko = st * TILE, so = sd * NW * DSW;
 #pragma unroll
     for (int kb = 0; kb < NV; ++kb)
 #pragma unroll
@@ -147,31 +154,47 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
         }
       }
   };
-  auto wait_next = [&](bool later_issued) {
-    if (later_issued) wait_vm<OPS>(); else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-  };
-
-  // ---- prologue: tiles 0 and 1 in flight, wait for tile 0
+  // ---- prologue, in issue order: dS of tiles 0 .. NSD - 2, K of tiles 0
+  // and 1; wait for K of tile 0 (and so for everything issued before it).
+  // Loads complete in order, so "K of tile n + 1 done" also covers its dS,
+  // which went out earlier.
+#pragma unroll
+  for (int n = 0; n < NSD - 1; ++n)
+    if (n < n_tiles) issue_ds(n);
 #pragma unroll
   for (int n = 0; n < NS - 1; ++n)
-    if (n < n_tiles) issue(n);
-  wait_next(n_tiles > 1);
+    if (n < n_tiles) issue_k(n);
+  if (n_tiles > 1) wait_vm<CH>(); else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
 
   const bool rows_live = qw0 < lq;
   for (int n = 0; n < n_tiles; ++n) {
-    const int st = n % NS;
-    if (n + NS - 1 < n_tiles) issue(n + NS - 1);
+    const int st = n % NS, sd = n % NSD;
+    // K of tile n + 2 into the slot of tile n - 1, dS of n + NSD - 1 likewise
+    // (every wave is past tile n - 1: the barrier that ended it)
+    const bool more_k = n + NS - 1 < n_tiles, more_ds = n + NSD - 1 < n_tiles;
+    if (more_k) issue_k(n + NS - 1);
+    if (more_ds) issue_ds(n + NSD - 1);
     const int k0 = n * BN;
     // sub-tiles with a visible pair for some row of this wave (the dK/dV
     // kernel wrote exactly those; the rest of the tile is never read)
     const int lim = causal ? qw0 + 31 + shift - k0 : BN - 1;
     const int nv = !rows_live || lim < 0 ? 0 : imin(lim / 32 + 1, NKB);
-    if (nv == NKB) body(st, std::integral_constant<int, NKB>{});
+    if (nv == NKB) body(st, sd, std::integral_constant<int, NKB>{});
     else if constexpr (NKB > 1) {
-      if (nv == 1) body(st, std::integral_constant<int, 1>{});
+      if (nv == 1) body(st, sd, std::integral_constant<int, 1>{});
     }
-    if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
+    // K (and dS) of tile n + 1 complete in every wave before any reads them.
+    // Issued after K of tile n + 1: at n = 0 only this tile's loads; later
+    // also the dS load of the previous tile (its K load came first).
+    if (n + 1 < n_tiles) {
+      if (more_ds) {
+        if (n == 0) wait_vm<CH + CD>(); else wait_vm<CH + 2 * CD>();
+      } else {
+        wait_vm<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+    }
   }
 
   // ---- dQ = alpha * dQ^T, bf16, this lane's query row

@@ -288,6 +288,12 @@ __device__ __forceinline__ void buf_store16_nt(rsrc_t r, int voff, int soff, con
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 2);
 }
 
+// Streaming load (cache policy nt: data read once).
+__device__ __forceinline__ bf16x8 buf_load16_nt(rsrc_t r, int voff, int soff) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+  return __builtin_bit_cast(bf16x8, x);
+}
+
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }

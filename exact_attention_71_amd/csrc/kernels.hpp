@@ -124,7 +124,8 @@ inline int dq_block_m(int d) { return d <= 128 ? DqCfg<128>::BM : DqCfg<256>::BM
 template <int D> struct DqDsCfg {
   static constexpr int NW = 8;                    // wavefronts, 32 query rows each
   static constexpr int BM = NW * 32;
-  static constexpr int BN = (D <= 128) ? 64 : 32; // keys per tile
+  static constexpr int BN = (D == 64) ? 64 : 32;  // keys per tile (a K tile covers 8 KiB at least)
+  static constexpr int NSD = (D == 64) ? 4 : (D == 128 ? 8 : 6);  // dS ring depth (K ring: 3)
 };
 
 template <int D> struct DkdvCfg {

@@ -224,10 +224,10 @@ int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles,
  *   "spin_limit"    bound on each wait of the deterministic chain (default
  *                   2^26 polls);
  *   "bwd_store_ds"  split backward, fixed length: -1 = automatic (default:
- *                   stored dS at head_dim 256, where it measured 12 % faster
- *                   per fwd+bwd step; recomputation at 64 and 128, where the
- *                   dK/dV kernel's extra writes cost more than the dQ kernel
- *                   saves), 1 = the dK/dV kernel stores dS and dQ = alpha dS K,
+ *                   stored dS at head_dim 128 and 256, where it measured 5 %
+ *                   and 11 % faster per fwd+bwd step; recomputation at 64,
+ *                   where the dK/dV kernel's extra writes cost more than the
+ *                   dQ kernel saves), 1 = the dK/dV kernel stores dS and dQ = alpha dS K,
  *                   0 = the dQ kernel recomputes S and dP. Packed variable
  *                   lengths always recompute; so do heads whose stored dS
  *                   would exceed 2 GiB.

@@ -258,11 +258,11 @@ def test_persistent_knob():
 
 
 def test_stored_ds_selection_and_workspace():
-    """Stored dS: automatic at head_dim 256 only, never for packed variable
+    """Stored dS: automatic at head_dim 128 and 256, never for packed variable
     lengths or the fused design; its workspace holds 2 KiB per 32 x 32
     sub-tile of every (sequence, query head)."""
     try:
-        for d, auto in ((64, 0), (128, 0), (256, 1)):
+        for d, auto in ((64, 0), (128, 1), (256, 1)):
             p = ea.make_params(2, 300, 700, 4, 2, d, 0.1, True, False)
             base_ws = None
             for mode, want in ((-1, auto), (0, 0), (1, 1)):

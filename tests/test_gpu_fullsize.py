@@ -108,8 +108,12 @@ def test_causal8k_full_size_fwd_bwd():
     _check_grads_sampled(dq2, dk2, dv2, q, k, v, do, 0, 1, 1, w.scale, True, rows, cols,
                          "causal8k fused bwd")
     del dq2, dk2, dv2
-    # dQ from the dS the dK/dV kernel stores (4 GiB of workspace at this size)
-    ea.set_tuning("bwd_store_ds", 1)
+    # the other split design: dQ recomputing S and dP (the default at this size
+    # reads the dS the dK/dV kernel stores)
+    p = ea.make_params(w.batch, w.seqlen, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, w.scale,
+                       True, False)
+    assert ea.bwd_stores_ds(p) == 1
+    ea.set_tuning("bwd_store_ds", 0)
     try:
         dq3, dk3, dv3 = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale)
         torch.cuda.synchronize()
@@ -118,7 +122,7 @@ def test_causal8k_full_size_fwd_bwd():
     assert torch.equal(dk, dk3) and torch.equal(dv, dv3)   # same dK/dV arithmetic
     for b, h in ((0, 1), (1, 9)):
         _check_grads_sampled(dq3, dk3, dv3, q, k, v, do, b, h, 1, w.scale, True, rows, cols,
-                             f"causal8k stored-dS bwd b{b} h{h}")
+                             f"causal8k recomputed-dQ bwd b{b} h{h}")
 
 
 def test_varlen_gqa_full_size_fwd_bwd():
