@@ -83,18 +83,18 @@ FwdWs fwd_ws(const attn_params* p, bool varlen) {
 
 struct BwdWs {
   size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, order = 0, tile_prefix = 0, mb_prefix = 0;
-  size_t order_dq = 0, tile_prefix_dq = 0, ds = 0;
+  size_t order_dq = 0, tile_prefix_dq = 0, ds = 0, ds_prefix = 0;
   size_t total = 0;
   int64_t n_sem = 0;
   bool use_ds = false;
-  int ds_nq32 = 0, ds_nk32 = 0;
 };
-// Stored-dS backward: fixed length, split design, and one head's sub-tiles
+// Stored-dS backward: split design, and one (sequence, head)'s sub-tiles
 // (plus the rows a last query block may address past them) within 32-bit
-// buffer offsets. Otherwise the dQ kernel recomputes S and dP.
-bool bwd_uses_ds(const attn_params* p, bool varlen) {
+// buffer offsets (for packed sequences: at the longest lengths). Otherwise
+// the dQ kernel recomputes S and dP.
+bool bwd_uses_ds(const attn_params* p, bool) {
   const bool on = g_tuning.bwd_store_ds < 0 ? p->head_dim >= 128 : g_tuning.bwd_store_ds != 0;
-  if (!on || g_tuning.bwd_fused_dq || varlen) return false;
+  if (!on || g_tuning.bwd_fused_dq) return false;
   const int64_t ext = ((int64_t)ds_nq32_of(p->seqlen_q) + 8) * ds_nk32_of(p->seqlen_k) * 2048;
   return ext <= kMaxExtent;
 }
@@ -122,10 +122,16 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
   }
   if (bwd_uses_ds(p, varlen)) {
     w.use_ds = true;
-    w.ds_nq32 = ds_nq32_of(p->seqlen_q);
-    w.ds_nk32 = ds_nk32_of(p->seqlen_k);
+    // packed sequences: sum over s of ds_nq32(Lq_s) <= 2 (cdiv(total_q, 64) + batch) and
+    // ds_nk32(Lk_s) <= ds_nk32(longest); the exact prefix is computed on the device
+    const int64_t nq_total = varlen ? 2 * ((int64_t)cdiv(p->total_q, 64) + p->batch)
+                                    : (int64_t)p->batch * ds_nq32_of(p->seqlen_q);
+    if (varlen) {
+      w.ds_prefix = off;
+      off = align_up(off + sizeof(int64_t) * ((size_t)p->batch + 1));
+    }
     w.ds = off;
-    off = align_up(off + (size_t)p->batch * p->num_heads_q * w.ds_nq32 * w.ds_nk32 * 2048);
+    off = align_up(off + (size_t)nq_total * p->num_heads_q * ds_nk32_of(p->seqlen_k) * 2048);
   }
   w.total = off;
   return w;
@@ -233,7 +239,7 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     int* tp = reinterpret_cast<int*>(base + wl.tile_prefix);
     unsigned* queue = launch_cus() ? reinterpret_cast<unsigned*>(base + wl.queue) : nullptr;
     if (launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bm, order, tp, nullptr,
-                               1, queue, stream) != hipSuccess)
+                               1, queue, nullptr, 0, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     fp.order = order;
     fp.tile_prefix = tp;
@@ -310,9 +316,10 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.nm_dq = cdiv(p->seqlen_q, bmq);
   if (wl.use_ds) {
     bp.ds = base + wl.ds;
-    bp.ds_nq32 = wl.ds_nq32;
-    bp.ds_nk32 = wl.ds_nk32;
-    bp.ntiles_dq = p->batch * p->num_heads_q * bp.nm_dq;
+    bp.ds_bytes = static_cast<int64_t>(wl.total - wl.ds);
+    bp.ds_prefix = varlen ? reinterpret_cast<const int64_t*>(base + wl.ds_prefix) : nullptr;
+    bp.ntiles_dq = varlen ? (cdiv(p->total_q, bmq) + p->batch) * p->num_heads_q
+                          : p->batch * p->num_heads_q * bp.nm_dq;
   }
   bp.sec_dq = section_width(2ll * p->seqlen_k * d * 2);
   if (varlen) {
@@ -336,12 +343,13 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
                                          const_cast<int*>(bp.order),
                                          const_cast<int*>(bp.tile_prefix),
                                          const_cast<int*>(bp.mb_prefix), bm, bp.queue,
+                                         const_cast<int64_t*>(bp.ds_prefix), p->num_heads_q,
                                          stream) != hipSuccess)
       return ATTN_ERR_HIP;
     if (varlen && !fused &&
         launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bmq,
                                const_cast<int*>(bp.order_dq), const_cast<int*>(bp.tile_prefix_dq),
-                               nullptr, 1, bp.queue_dq, stream) != hipSuccess)
+                               nullptr, 1, bp.queue_dq, nullptr, 0, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }

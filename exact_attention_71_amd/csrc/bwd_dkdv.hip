@@ -130,10 +130,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // except that lanes 32..63 swap 64-byte halves (slot L ^ 4), which makes the
   // dQ kernel's transposing reads conflict-free. ds_cur: the head of the
   // compute cursor.
-  const int ds_nk32 = p.ds_nk32;
-  const int ds_bh = p.ds_nq32 * ds_nk32 * 2048;
+  const int ds_nk32 = ds_nk32_of(lk);
+  int ds_bh = 0;
   const char* ds_cur = nullptr;
-  if constexpr (DS) ds_cur = keep_sgpr(p.ds + ((int64_t)t.seq * p.hq + kvh0) * ds_bh);
+  if constexpr (DS) ds_cur = keep_sgpr(p.ds + ds_region(p, t.seq, kvh0, lq, lk, &ds_bh));
   const int64_t q_tile = (qs * qstride + (int64_t)kvh0 * D) * 2;
   const char* const q_seq = keep_sgpr(static_cast<const char*>(p.q) + q_tile);
   const char* const do_seq = keep_sgpr(static_cast<const char*>(p.dout) + q_tile);

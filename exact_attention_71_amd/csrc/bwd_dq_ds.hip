@@ -58,8 +58,16 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
   const uint32_t lds_k = lds_addr(smem);
   const uint32_t lds_s = lds_k + NS * TILE;
 
-  const int lq = p.sv.seqlen_q, lk = p.sv.seqlen_k;
-  const int64_t qs = (int64_t)t.seq * lq, ks0 = (int64_t)t.seq * lk;
+  int64_t qs, ks0;
+  int lq, lk;
+  if (p.sv.cu_q) {
+    const int a = p.sv.cu_q[t.seq], b = p.sv.cu_q[t.seq + 1];
+    const int c0 = p.sv.cu_k[t.seq], d0 = p.sv.cu_k[t.seq + 1];
+    qs = a; lq = b - a; ks0 = c0; lk = d0 - c0;
+  } else {
+    qs = (int64_t)t.seq * p.sv.seqlen_q; lq = p.sv.seqlen_q;
+    ks0 = (int64_t)t.seq * p.sv.seqlen_k; lk = p.sv.seqlen_k;
+  }
   const int m0 = t.block * BM;
   if (m0 >= lq) return;
   const int h = t.head;
@@ -88,9 +96,10 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
   // ---- this wave's dS: sub-tile row qw0 / 32 of the head, NKB sub-tiles
   // (contiguous, 2 KiB each) per key tile. Reads past the head's range give
   // zero; a wave whose rows all lie past the sequence skips its MFMAs.
-  const int nk32 = p.ds_nk32;
-  const int ds_bh = p.ds_nq32 * nk32 * 2048;
-  const rsrc_t dsr = raw_rsrc(p.ds + ((int64_t)t.seq * p.hq + h) * ds_bh, ds_bh);
+  const int nk32 = ds_nk32_of(lk);
+  int ds_bh;
+  const int64_t ds_off = ds_region(p, t.seq, h, lq, lk, &ds_bh);
+  const rsrc_t dsr = raw_rsrc(p.ds + ds_off, ds_bh);
   const int ds_row = (qw0 >> 5) * nk32 * 2048 + lane * 16;
   auto issue_k = [&](int n) {
     const int64_t t0 = (int64_t)n * BN * kstride;
@@ -219,9 +228,18 @@ __global__ __launch_bounds__(DqDsCfg<D>::NW * 64, 1) void bwd_dq_ds_kernel(BwdPa
   __shared__ int ticket;
   for (int r = 0;; ++r) {
     const BwdParams& p = kernel_args<BwdParams>();
-    const int i = next_tile(r, p.ntiles_dq, p.nxcd, nullptr, &ticket);
+    const int i = next_tile(r, p.ntiles_dq, p.nxcd, p.queue_dq, &ticket);
     if (i < 0) break;
-    const Tile t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
+    Tile t;
+    if (p.sv.cu_q) {
+      t = varlen_tile(i, p.order_dq, p.tile_prefix_dq, p.sv.batch, p.hq, true);
+      if (t.seq < 0) {
+        if (p.queue_dq) continue;   // a ticket past the last real tile
+        break;
+      }
+    } else {
+      t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
+    }
     dqds_tile<D>(p, t, smem);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
@@ -239,7 +257,7 @@ hipError_t launch_dq_ds_d(const BwdParams& p, int cus, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_dq_ds(const BwdParams& p, int d, int cus, hipStream_t stream) {
-  if (!p.ds || p.sv.cu_q) return hipErrorInvalidValue;
+  if (!p.ds || (p.sv.cu_q && !p.ds_prefix)) return hipErrorInvalidValue;
   if (p.ntiles_dq <= 0) return hipSuccess;
   switch (d) {
     case 64: return launch_dq_ds_d<64>(p, cus, stream);

@@ -79,19 +79,39 @@ struct BwdParams {
   int64_t rows_q;         // total query rows (B*Sq or total_q)
   int64_t n_sem;          // semaphore words to clear (deterministic)
   int spin_limit;         // bounded wait for the deterministic chain
-  // Stored dS (fixed length only; null: the dQ kernel recomputes S and dP).
-  // Per (sequence, query head): ds_nq32 x ds_nk32 sub-tiles of 32 queries x
-  // 32 keys, bf16, 2 KiB each, in the register order of the dK/dV kernel
-  // (ds_subtile_offset).
+  // Stored dS (null: the dQ kernel recomputes S and dP). Per (sequence,
+  // query head): ds_nq32_of(Lq) x ds_nk32_of(Lk) sub-tiles of 32 queries x 32
+  // keys, bf16, 2 KiB each, in the register order of the dK/dV kernel; the
+  // regions of the heads of a sequence follow each other, sequences in order.
   char* ds;
-  int ds_nq32, ds_nk32;
+  const int64_t* ds_prefix;  // varlen: first sub-tile of each sequence (null: fixed length)
+  int64_t ds_bytes;          // size of the dS area (regions are clamped to it)
 };
 
 // Stored-dS geometry: query blocks of 32 rounded to the dK/dV step (64 rows
 // at most), key blocks of 32 rounded to the dK/dV workgroup (256 keys at
 // most), so every sub-tile the dK/dV kernel writes lies inside its head.
-inline int ds_nq32_of(int seqlen_q) { return (seqlen_q + 63) / 64 * 2; }
-inline int ds_nk32_of(int seqlen_k) { return (seqlen_k + 255) / 256 * 8; }
+__host__ __device__ inline int ds_nq32_of(int seqlen_q) { return (seqlen_q + 63) / 64 * 2; }
+__host__ __device__ inline int ds_nk32_of(int seqlen_k) { return (seqlen_k + 255) / 256 * 8; }
+
+// Byte offset from p.ds of the stored-dS region of (sequence s, query head h)
+// with lq queries and lk keys; *bh_bytes = the region's size, clamped to the
+// dS area (packed lengths beyond the maximum the caller declared would
+// otherwise place a region past it; the buffer range then drops the stores).
+__device__ inline int64_t ds_region(const BwdParams& p, int s, int h, int lq, int lk,
+                                    int* bh_bytes) {
+  const int nq = ds_nq32_of(lq), nk = ds_nk32_of(lk);
+  const int64_t first = p.ds_prefix ? p.ds_prefix[s] : (int64_t)s * p.hq * nq * nk;
+  const int64_t off = (first + (int64_t)h * nq * nk) * 2048;
+  const int64_t room = p.ds_bytes - off;
+  const int64_t size = (int64_t)nq * nk * 2048;
+  // wave-uniform by construction (the tile is); made explicit for SGPRs
+  *bh_bytes = __builtin_amdgcn_readfirstlane(room <= 0 ? 0 : static_cast<int>(size < room ? size : room));
+  const int64_t r = room <= 0 ? 0 : off;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 // Tile sizes (rows of the query block and keys of the key block) per head dim.
 #ifndef ATTN71_FWD_NW
@@ -178,9 +198,11 @@ hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
 // cdiv(len of count_cu, blk) * heads tiles each, and (optional) mb_prefix[s]
 // = first query block of actual sequence s with cdiv(len of q_cu, mb_blk);
 // clears *queue (optional) for the tile tickets of the launch that follows.
+// Optional ds_prefix[s] = first stored-dS sub-tile of sequence s (lengths
+// from q_cu and count_cu, ds_heads query heads each; see ds_region).
 hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
                                   int nseq, int heads, int blk, int* order, int* tile_prefix,
                                   int* mb_prefix, int mb_blk, unsigned* queue,
-                                  hipStream_t stream);
+                                  int64_t* ds_prefix, int ds_heads, hipStream_t stream);
 
 }  // namespace attn71

@@ -106,7 +106,10 @@ size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen);
  * dS into the workspace and computes dQ = alpha dS K from it; 0 if its dQ
  * kernel recomputes S and dP (or dQ is fused); -1 for parameters the calls
  * would reject. The stored dS takes B * Hq * ceil(Sq/64)*2 * ceil(Sk/256)*8
- * * 2 KiB of the workspace (about 2 bytes per query-key pair). */
+ * * 2 KiB of the workspace (about 2 bytes per query-key pair); for packed
+ * lengths the workspace holds Hq * 2 (ceil(total_q/64) + batch) *
+ * ceil(seqlen_k/256)*8 * 2 KiB, a bound from the total and the longest key
+ * length (seqlen_k must bound every sequence's key length). */
 int32_t attn_bwd_stores_ds(const attn_params* p, int32_t varlen);
 
 /* Forward, fixed length. lse may be NULL (the LSE is optional on the pages:
@@ -134,7 +137,7 @@ attn_status attn_fwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  *     deterministic = 1, in a fixed order behind per-block semaphores (blog
  *     page, deterministic mode); postprocess converts dQ to bf16.
  * In the split design the dQ kernel either recomputes S and dP from q, k, v,
- * dout and lse, or (fixed length, attn_bwd_stores_ds = 1) reads the dS that
+ * dout and lse, or (attn_bwd_stores_ds = 1) reads the dS that
  * the dK/dV kernel wrote into the workspace and runs dQ = alpha dS K, its
  * only GEMM (blog page, backward section: dQ is dS times the key block).
  * Both write dQ once: bit-reproducible either way. */
@@ -152,8 +155,8 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
 /* The backward split into its phases, for callers that schedule or time them
  * separately. `phases` is a mask of ATTN_BWD_*; running the masks in the
  * order PREPROCESS, MAIN, DQ, POSTPROCESS on one stream with the same
- * workspace equals attn_bwd(_varlen) (MAIN and DQ are independent of each
- * other and may also run in either order).
+ * workspace equals attn_bwd(_varlen) (with the recomputing dQ kernel MAIN and
+ * DQ are independent of each other and may also run in either order).
  * cu_seqlens_q/k NULL = fixed length. Arguments a phase does not read may
  * be NULL only if no selected phase reads them. Every MAIN phase needs a
  * PREPROCESS phase of the same workspace before it: it clears the dQ
@@ -223,14 +226,14 @@ int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles,
  *                   increase of the row max;
  *   "spin_limit"    bound on each wait of the deterministic chain (default
  *                   2^26 polls);
- *   "bwd_store_ds"  split backward, fixed length: -1 = automatic (default:
+ *   "bwd_store_ds"  split backward: -1 = automatic (default:
  *                   stored dS at head_dim 128 and 256, where it measured 5 %
  *                   and 11 % faster per fwd+bwd step; recomputation at 64,
  *                   where the dK/dV kernel's extra writes cost more than the
  *                   dQ kernel saves), 1 = the dK/dV kernel stores dS and dQ = alpha dS K,
- *                   0 = the dQ kernel recomputes S and dP. Packed variable
- *                   lengths always recompute; so do heads whose stored dS
- *                   would exceed 2 GiB.
+ *                   0 = the dQ kernel recomputes S and dP. Heads whose
+ *                   stored dS would exceed 2 GiB (at the longest lengths)
+ *                   always recompute.
  * Returns ATTN_ERR_INVALID_ARGUMENT for unknown keys or values. */
 attn_status attn_set_tuning(const char* key, int32_t value);
 

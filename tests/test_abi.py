@@ -258,25 +258,31 @@ def test_persistent_knob():
 
 
 def test_stored_ds_selection_and_workspace():
-    """Stored dS: automatic at head_dim 128 and 256, never for packed variable
-    lengths or the fused design; its workspace holds 2 KiB per 32 x 32
-    sub-tile of every (sequence, query head)."""
+    """Stored dS: automatic at head_dim 128 and 256, never with the fused
+    design; its workspace holds 2 KiB per 32 x 32 sub-tile of every (sequence,
+    query head) (packed lengths: a bound from the total and the longest, plus
+    the per-sequence offsets)."""
     try:
         for d, auto in ((64, 0), (128, 1), (256, 1)):
             p = ea.make_params(2, 300, 700, 4, 2, d, 0.1, True, False)
-            base_ws = None
+            pv = ea.make_params(3, 300, 700, 4, 2, d, 0.1, True, False, total_q=500, total_k=1200)
+            base_ws = base_vws = None
             for mode, want in ((-1, auto), (0, 0), (1, 1)):
                 ea.set_tuning("bwd_store_ds", mode)
                 assert ea.bwd_stores_ds(p) == want, (d, mode)
-                assert ea.bwd_stores_ds(p, varlen=True) == 0
-                ws = ea.bwd_workspace_size(p)
+                assert ea.bwd_stores_ds(pv, varlen=True) == want, (d, mode)
                 if mode == 0:
-                    base_ws = ws
+                    base_ws = ea.bwd_workspace_size(p)
+                    base_vws = ea.bwd_workspace_size(pv, varlen=True)
             ea.set_tuning("bwd_store_ds", 1)
             nq32, nk32 = -(-300 // 64) * 2, -(-700 // 256) * 8
             extra = 2 * 4 * nq32 * nk32 * 2048
             assert ea.bwd_workspace_size(p) - base_ws >= extra
             assert ea.bwd_workspace_size(p) - base_ws < extra + 256
+            # packed: 2 (cdiv(500, 64) + 3) 32-row blocks bound sum_s ds_nq32(Lq_s)
+            vextra = 4 * 2 * (-(-500 // 64) + 3) * nk32 * 2048
+            assert ea.bwd_workspace_size(pv, varlen=True) - base_vws >= vextra + 8 * 4
+            assert ea.bwd_workspace_size(pv, varlen=True) - base_vws < vextra + 512
             ea.set_tuning("bwd_fused_dq", 1)
             assert ea.bwd_stores_ds(p) == 0
             ea.set_tuning("bwd_fused_dq", 0)

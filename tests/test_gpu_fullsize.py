@@ -158,6 +158,29 @@ def test_varlen_gqa_full_size_fwd_bwd():
         sl = slice(cuh[s], cuh[s + 1])
         _identities(dk[sl].unsqueeze(0), dv[sl].unsqueeze(0), do[sl].unsqueeze(0), group,
                     f"varlen identities seq{s}")
+    # the default here stores dS; the recomputing dQ kernel gives the same dK, dV
+    # bits and dQ within the bar on the shortest and the longest sequence
+    p = ea.make_params(w.num_seqs, mx, mx, w.heads_q, w.heads_kv, w.head_dim, w.scale, True,
+                       False, total_q=q.shape[0], total_k=k.shape[0])
+    assert ea.bwd_stores_ds(p, varlen=True) == 1
+    ea.set_tuning("bwd_store_ds", 0)
+    try:
+        dq2, dk2, dv2 = ea.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, causal=True,
+                                      softmax_scale=w.scale)
+        torch.cuda.synchronize()
+    finally:
+        ea.set_tuning("bwd_store_ds", -1)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    for s in (int(order[0]), int(order[-1])):
+        sl = slice(cuh[s], cuh[s + 1])
+        n = lengths[s]
+        qs, ks, vs, dos = (x[sl].unsqueeze(0) for x in (q, k, v, do))
+        rows = _rows(n, extra=12, seed=s + 7)
+        for h in (2, 29):
+            dq_ref = oracle.head_dq_rows(_h(qs, 0, h), _h(ks, 0, h // group), _h(vs, 0, h // group),
+                                         _h(dos, 0, h), w.scale, True, rows)
+            for x, tag in ((dq, "stored dS"), (dq2, "recomputed")):
+                assert rel_l2(x[sl][rows, h], dq_ref) <= GRAD_REL, (s, h, tag)
 
 
 @pytest.mark.parametrize("name", ["det16k_d64", "det16k_d128", "det16k_d256"])
