@@ -5,7 +5,10 @@
 One step = one forward (attn_fwd: online softmax, tau = 8 conditional
 rescale, LSE) plus one backward (attn_bwd phases: D = rowsum(dO o O) and
 LSE*log2 e, the key-block dK/dV kernel, the query-block dQ kernel) over one
-batch of seeded synthetic bf16 inputs already resident in HBM. Throughput
+batch of seeded synthetic bf16 inputs already resident in HBM. The backward
+design is the library's default for the workload (at head_dim 128 and 256
+the dK/dV kernel stores dS and the dQ kernel runs dQ = alpha dS K);
+--bwd-recompute-dq, --bwd-store-ds and --bwd-fused-dq select one. Throughput
 counts algorithmic flops: forward 4*B*H*Sq*Sk*d, backward 2.5x, both halved
 for causal.
 
