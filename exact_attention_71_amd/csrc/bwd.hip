@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t n_pai
       const int64_t b = row / p.sv.seqlen_q, s = row % p.sv.seqlen_q;
       off = (b * p.hq + h) * p.sv.seqlen_q + s;
     }
-    p.dsum[off] = acc;
+    p.dsum[off] = -acc;
     p.lse2[off] = lse_log2(p.lse[off]);
   }
 }
@@ -302,10 +302,16 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     }
     const int mq0 = m * BM;              // first query row of this step
 
-    // S = Q K^T and dP = dO V^T: key on the lane, query on the register
+    // S = Q K^T and dP - D = dO V^T - D: key on the lane, query on the
+    // register; the dP accumulators start from the rows' -D (as in the dK/dV
+    // kernel, so both designs compute dS in the same order)
     f32x16 s[NQB], dp[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
+    for (int qb = 0; qb < NQB; ++qb) {
+      s[qb] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[qb][i] = sm.dsum[qb * 32 + c_row(i, g)];
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
         dp[qb] = mfma32(ao, vf[kk], dp[qb]);
       }
 
-    // P = 2^(S alpha log2e - LSE log2e), dS = P (dP - D)
+    // P = 2^(S alpha log2e - LSE log2e), dS = P (dP - D) (the stored rows hold -D)
     const bool need_mask = (n0 + BN > lk) || (causal && n0 + BN - 1 > mq0 + shift);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
@@ -325,7 +331,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       for (int j = 0; j < 4; ++j) {
         const int q4 = qb * 32 + 8 * j + 4 * g;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[q4]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dsum[q4]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * j + r;
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
             if (mykey >= lk || (causal && mykey > qrow + shift)) pv = 0.0f;
           }
           s[qb][i] = pv;
-          dp[qb][i] = pv * (dp[qb][i] - d4[r]);
+          dp[qb][i] = pv * dp[qb][i];
         }
       }
 

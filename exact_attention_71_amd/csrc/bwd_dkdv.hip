@@ -268,23 +268,34 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     };
     f32x16 s[NQB][KB], dp[NQB][KB];
     bf16x8 pb[NQB][KB][2], sb[NQB][KB][2];
+    // The rows' -D (stored negated) is the dP accumulators' starting value, so
+    // the accumulator ends at dP - D and dS = P o (dP - D) is one multiply.
+    // Register 4j + r of a tile is row 8j + 4g + r of its 32-row block.
+    f32x16 nd[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) { s[qb][kb] = f32x16{}; dp[qb][kb] = f32x16{}; }
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = lds_ldf4(al + 4 * (BM + qb * 32 + 8 * j));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nd[qb][4 * j + r] = v[r];
+      }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) { s[qb][kb] = f32x16{}; dp[qb][kb] = nd[qb]; }
     // element e of the P / dS pass: (qb, j, kb, r) -> register 4j + r of tile (qb, kb).
-    // Row values (LSE log2 e, then D) come in blocks of 4 rows (qb, j), read one
-    // block ahead: LDS returns in order, so a read issued just before its use
-    // would make the wait drain the operand fragments prefetched after it.
+    // LSE log2 e comes in blocks of 4 rows (qb, j), read one block ahead: LDS
+    // returns in order, so a read issued just before its use would make the
+    // wait drain the operand fragments prefetched after it.
     constexpr int NJ = 4 * NQB;
-    auto row_read = [&](int b) {   // block b of [LSE blocks | D blocks]
-      const int x = b % NJ;
-      return lds_ldf4(al + 4 * ((b < NJ ? 0 : BM) + (x / 4) * 32 + 8 * (x % 4)));
+    auto row_read = [&](int b) {   // LSE block b
+      return lds_ldf4(al + 4 * ((b / 4) * 32 + 8 * (b % 4)));
     };
     f32x4 rv_cur = {}, rv_next = row_read(0);
     auto row_block = [&](int b) {  // entering block b: rotate and prefetch b + 1
       rv_cur = rv_next;
-      if (b + 1 < 2 * NJ) rv_next = row_read(b + 1);
+      if (b + 1 < NJ) rv_next = row_read(b + 1);
     };
     auto p_elem = [&](int e) {
       const int qb = e / (KB * 16), rem = e % (KB * 16);
@@ -301,8 +312,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     auto s_elem = [&](int e) {
       const int qb = e / (KB * 16), rem = e % (KB * 16);
       const int j = rem / (KB * 4), kb = (rem / 4) % KB, r = rem % 4;
-      if (kb == 0 && r == 0) row_block(NJ + qb * 4 + j);
-      float ds = s[qb][kb][4 * j + r] * (dp[qb][kb][4 * j + r] - rv_cur[r]);
+      float ds = s[qb][kb][4 * j + r] * dp[qb][kb][4 * j + r];
       pin(ds);
       dp[qb][kb][4 * j + r] = ds;
       if ((j & 1) && kb == KB - 1 && r == 3) {

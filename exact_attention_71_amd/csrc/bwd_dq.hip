@@ -91,12 +91,12 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
       df[kk] = buf_load16(dr, voff + 32 * kk, 0);
     }
   }
-  float lse2 = __builtin_inff(), dsum = 0.0f;   // padding rows: P = 0
+  float lse2 = __builtin_inff(), ndsum = 0.0f;   // -D; padding rows: P = 0
   if (myq < lq) {
     const int64_t so = p.sv.cu_q ? (int64_t)h * p.sv.total_q + qs + myq
                                  : ((int64_t)t.seq * p.hq + h) * p.sv.seqlen_q + myq;
     lse2 = p.lse2[so];
-    dsum = p.dsum[so];
+    ndsum = p.dsum[so];
   }
 
   // ---- K / V ring: tile n into slot n % NS. Keys past the sequence read as
@@ -196,7 +196,7 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
     };
     auto ds_elem = [&](int q, int j) {
       const int kb = q / 2, i = 8 * (q % 2) + j;
-      float d = s[kb][i] * (dp[kb][i] - dsum);
+      float d = s[kb][i] * (dp[kb][i] + ndsum);
       pin(d);
       dp[kb][i] = d;
     };

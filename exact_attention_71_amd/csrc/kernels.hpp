@@ -49,7 +49,8 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;            // D = rowsum(dO o O), same layout as LSE
+  float* dsum;            // -D = -rowsum(dO o O), same layout as LSE (negated: the
+                          // dK/dV kernel starts its dP accumulators from it)
   float* lse2;            // LSE * log2(e), same layout as LSE
   float* dq_acc;          // fp32 [rows][Hq][d]
   int* sem;               // deterministic: one counter per (query block, query head)
