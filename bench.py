@@ -62,6 +62,23 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def stored_ds_read_bytes(w, lengths) -> int:
+    """Algorithmic HBM bytes of the dQ kernel that reads the stored dS: every
+    32 x 32 dS sub-tile with a visible (query, key) pair (2 KiB each) of every
+    (sequence, query head), K read once per (sequence, KV head), dQ written."""
+    seqs = lengths if w.varlen else [w.seqlen] * w.batch
+    subtiles = 0
+    for n in seqs:
+        nq, nk = -(-n // 32), -(-n // 32)
+        if w.causal:   # equal lengths: sub-tile (q, k) is visible iff k <= q
+            subtiles += sum(min(q + 1, nk) for q in range(nq))
+        else:
+            subtiles += nq * nk
+    tokens = sum(seqs)
+    return (subtiles * w.heads_q * 2048 + tokens * w.heads_kv * w.head_dim * 2
+            + tokens * w.heads_q * w.head_dim * 2)
+
+
 def _describe(w) -> str:
     if w.varlen:
         return (f"{w.name}: {w.num_seqs} packed seqs len U[{w.len_lo},{w.len_hi}], Hq{w.heads_q} "
@@ -377,6 +394,13 @@ def main() -> int:
     kernels = {names[n]: {"ms": round(kms[n], 4),
                           "tflops": round(kflops[n] / (kms[n] * 1e-3) / 1e12, 1)}
                for n in kms if n in kflops and kms[n] > 0.002}
+    if stored_ds and kms.get("bwd_dq", 0) > 0.002:
+        # HBM-bound: its roofline is bandwidth, against the 8 TB/s peak
+        b = stored_ds_read_bytes(w, lengths)
+        gbs = b / (kms["bwd_dq"] * 1e-3) / 1e9
+        kernels[names["bwd_dq"]].update({"bound": "hbm", "algorithmic_bytes": b,
+                                         "gbs": round(gbs, 1),
+                                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
     out = {
         "metric": "attention fwd/bwd TFLOPs/s at hdim128 bf16; % of MI355X BF16 MFMA peak",
         "value": round(value, 2),
