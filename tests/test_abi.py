@@ -286,6 +286,9 @@ def test_stored_ds_selection_and_workspace():
             ea.set_tuning("bwd_fused_dq", 1)
             assert ea.bwd_stores_ds(p) == 0
             ea.set_tuning("bwd_fused_dq", 0)
+        # parameters the calls would reject (Hq not a multiple of Hkv; head_dim 96)
+        assert ea.bwd_stores_ds(ea.make_params(1, 10, 10, 3, 2, 128, 0.1, False, False)) == -1
+        assert ea.bwd_stores_ds(ea.make_params(1, 10, 10, 2, 2, 96, 0.1, False, False)) == -1
         # one head's sub-tiles beyond 32-bit buffer offsets: recomputation
         big = ea.make_params(1, 40000, 40000, 1, 1, 256, 0.1, True, False)
         assert ea.bwd_stores_ds(big) == 0
