@@ -1,27 +1,34 @@
 """Throughput of the fused attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal8k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|NAME]
 
-One step = one forward (attn_fwd: online softmax, tau = 8 conditional
-rescale, LSE) plus one backward (attn_bwd phases: D = rowsum(dO o O) and
-LSE*log2 e, the key-block dK/dV kernel, the query-block dQ kernel) over one
-batch of seeded synthetic bf16 inputs already resident in HBM. The backward
-design is the library's default for the workload (at head_dim 128 and 256
-the dK/dV kernel stores dS and the dQ kernel runs dQ = alpha dS K);
---bwd-recompute-dq, --bwd-store-ds and --bwd-fused-dq select one. Throughput
-counts algorithmic flops: forward 4*B*H*Sq*Sk*d, backward 2.5x, both halved
-for causal.
+One step = one forward (attn_fwd[_varlen]: online softmax, tau = 8
+conditional rescale, LSE) plus, for the fwd+bwd workloads, one backward
+(attn_bwd phases: D = rowsum(dO o O) and LSE log2 e, the key-block dK/dV
+kernel, the query-block dQ kernel; or the fused kernel and its
+postprocess) over one batch of seeded synthetic bf16 inputs already resident
+in HBM. Each workload runs in the library's default backward design unless
+--bwd-design selects one. Throughput counts algorithmic flops: forward
+4*B*H*Sq*Sk*d, backward 2.5x, both halved for causal.
 
-Prints one JSON line. The "roofline" object covers the dominant kernel (the
-longest-running one; the dK/dV kernel for the fwd+bwd workloads), timed with
-HIP events on the stream it runs on. "cpu_baseline" times the float64 oracle
-on a bounded sample of the same workload.
+The default run measures every workload (small, fwd4k, causal8k, varlen_gqa,
+det16k_d64/128/256): each gets a sub-record in config.workloads with the
+forward and backward TFLOP/s and their fractions of the 2.5 PFLOP/s dense
+bf16 peak, ms per step, per-kernel times, workspace bytes and a bounded
+float64-oracle sample. The headline (value, roofline, cpu_baseline) is the
+largest single-GPU workload, varlen_gqa (16 packed causal sequences,
+Hq 32 / Hkv 4, d 128). config.ablations holds the longest-first schedule on
+and off (MHA and MQA), the fused design's deterministic (semaphore-ordered)
+and atomic dQ, and a forward sequence-length sweep.
+
+Prints one JSON line. The "roofline" object covers the headline's dominant
+kernel (the longest-running one), timed with HIP events on the stream it
+runs on.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -32,7 +39,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_causal8k.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+HEADLINE = "varlen_gqa"
+ORDER = ["small", "fwd4k", "causal8k", "varlen_gqa", "det16k_d64", "det16k_d128", "det16k_d256"]
+METRIC = "attention fwd/bwd TFLOPs/s at hdim128 bf16; % of MI355X BF16 MFMA peak"
 
 
 def sources_sha() -> str:
@@ -79,7 +89,7 @@ def stored_ds_read_bytes(w, lengths) -> int:
             + tokens * w.heads_q * w.head_dim * 2)
 
 
-def _describe(w) -> str:
+def describe(w) -> str:
     if w.varlen:
         return (f"{w.name}: {w.num_seqs} packed seqs len U[{w.len_lo},{w.len_hi}], Hq{w.heads_q} "
                 f"Hkv{w.heads_kv} d{w.head_dim} {'causal' if w.causal else 'non-causal'} {w.passes}")
@@ -118,10 +128,10 @@ def host_cpu() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, budget_s: float = 20.0) -> dict:
+def cpu_baseline(w, budget_s: float) -> dict:
     """Float64 oracle on a bounded sample: whole (sequence, head) slabs of the
-    workload, fwd (+bwd), until about budget_s seconds have been spent."""
-    import numpy as np
+    workload (for packed lengths, slabs at the longest length), fwd (+bwd),
+    until about budget_s seconds have been spent."""
     import oracle
     from oracle.attention import head_backward, head_forward
     from workloads import draw_lengths, make_inputs
@@ -155,11 +165,265 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "host": host_cpu(),
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"{heads} of {w.heads_q * (w.num_seqs if w.varlen else w.batch)} "
                       f"(sequence, head) slabs at length {sl}, {w.passes}, float64 numpy, "
                       f"{dt:.1f} s"}
+
+
+class Runner:
+    """One workload's inputs, outputs and workspaces on the GPU, driven through
+    the C ABI (ctypes) on torch's current stream."""
+
+    def __init__(self, torch, ea, w, opts, dev="cuda:0", inputs=None, lengths=None):
+        import ctypes
+        from workloads import draw_lengths, workload_inputs
+        self.torch, self.ea, self.w, self.ct = torch, ea, w, ctypes
+        self.lib = ea.load()
+        self.inp = inputs if inputs is not None else workload_inputs(w, device=dev)
+        self.lengths = lengths if lengths is not None else (
+            draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number) if w.varlen else None)
+        q, k = self.inp["q"], self.inp["k"]
+        self.varlen = w.varlen
+        if w.varlen:
+            self.cu_q = self.inp["cu_seqlens_q"].to(dev)
+            self.cu_k = self.inp["cu_seqlens_k"].to(dev)
+            mx = max(self.lengths)
+            tq, hq, d = q.shape
+            self.p = ea.make_params(w.num_seqs, mx, mx, w.heads_q, w.heads_kv, d, w.scale,
+                                    w.causal, w.deterministic, total_q=tq, total_k=k.shape[0],
+                                    options=opts)
+            self.lse = torch.empty((hq, tq), dtype=torch.float32, device=dev)
+        else:
+            self.cu_q = self.cu_k = None
+            b, s, hq, d = q.shape
+            self.p = ea.make_params(b, s, k.shape[1], w.heads_q, w.heads_kv, d, w.scale, w.causal,
+                                    w.deterministic, options=opts)
+            self.lse = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
+        self.o = torch.empty_like(q)
+        self.design = ea.bwd_design(self.p, self.varlen)
+        assert self.design > 0, "backward design not available for these parameters"
+        self.fws_bytes = ea.fwd_workspace_size(self.p, self.varlen)
+        self.bws_bytes = ea.bwd_workspace_size(self.p, self.varlen) if w.passes == "fwd+bwd" else 0
+        self.fws = torch.empty(max(1, self.fws_bytes), dtype=torch.uint8, device=dev)
+        self.with_bwd = w.passes == "fwd+bwd"
+        if self.with_bwd:
+            self.bws = torch.empty(max(1, self.bws_bytes), dtype=torch.uint8, device=dev)
+            self.dq, self.dk, self.dv = (torch.empty_like(self.inp[n]) for n in ("q", "k", "v"))
+
+    def stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def fwd(self):
+        i, ct = self.inp, self.ct
+        if self.varlen:
+            r = self.lib.attn_fwd_varlen(ct.byref(self.p), self.cu_q.data_ptr(), self.cu_k.data_ptr(),
+                                         i["q"].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
+                                         self.o.data_ptr(), self.lse.data_ptr(), self.fws.data_ptr(),
+                                         self.fws.numel(), self.stream())
+        else:
+            r = self.lib.attn_fwd(ct.byref(self.p), i["q"].data_ptr(), i["k"].data_ptr(),
+                                  i["v"].data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
+                                  self.fws.data_ptr(), self.fws.numel(), self.stream())
+        assert r == 0, r
+
+    def phase(self, mask):
+        i, ct = self.inp, self.ct
+        r = self.lib.attn_bwd_phases(
+            ct.byref(self.p), None if self.cu_q is None else self.cu_q.data_ptr(),
+            None if self.cu_k is None else self.cu_k.data_ptr(), mask, i["q"].data_ptr(),
+            i["k"].data_ptr(), i["v"].data_ptr(), self.o.data_ptr(), i["do"].data_ptr(),
+            self.lse.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
+            self.bws.data_ptr(), self.bws.numel(), self.stream())
+        assert r == 0, r
+
+    def bwd(self):
+        self.phase(self.ea.BWD_ALL)
+
+    def timed_steps(self, warmup, steps):
+        """Mean ms per step and per phase (HIP events on the launch stream)."""
+        torch, ea = self.torch, self.ea
+        ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        marks = {}
+
+        def timed(name, fn, on):
+            if not on:
+                fn()
+                return
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            marks.setdefault(name, []).append((a, b))
+
+        def step(on):
+            timed("fwd", self.fwd, on)
+            if not self.with_bwd:
+                return
+            timed("bwd_pre", lambda: self.phase(ea.BWD_PREPROCESS), on)
+            timed("bwd_main", lambda: self.phase(ea.BWD_MAIN), on)
+            timed("bwd_dq", lambda: self.phase(ea.BWD_DQ), on)
+            timed("bwd_post", lambda: self.phase(ea.BWD_POSTPROCESS), on)
+
+        for _ in range(warmup):
+            step(False)
+        torch.cuda.synchronize()
+        t0, t1 = ev(), ev()
+        t0.record()
+        for _ in range(steps):
+            step(True)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        kms = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in marks.items()}
+        return ms, kms
+
+    def abi_times(self, fn, n=10):
+        torch = self.torch
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4), "calls": n}
+
+
+DESIGN_NAMES = {1: "dK/dV kernel + dQ kernel recomputing S, dP",
+                2: "dK/dV kernel storing dS + dQ = alpha dS K kernel",
+                3: "fused dQ (fp32 atomics; ordered when deterministic)"}
+
+
+def frac(t):
+    return round(t / PEAK_BF16_TFLOPS, 4)
+
+
+def measure(torch, ea, w, args, opts, cpu_budget: float) -> dict:
+    """Sub-record of one workload."""
+    from workloads import workload_flops
+    print(f"[bench] workload {describe(w)}", file=sys.stderr, flush=True)
+    r = Runner(torch, ea, w, opts)
+    fl = workload_flops(w, r.lengths)
+    ms, kms = r.timed_steps(args.warmup, args.steps)
+    if r.with_bwd and w.deterministic:
+        assert ea.bwd_status(r.p, r.bws, r.varlen) == 0
+    bwd_ms = sum(kms.get(n, 0.0) for n in ("bwd_pre", "bwd_main", "bwd_dq", "bwd_post"))
+    total = fl["fwd+bwd"] if r.with_bwd else fl["fwd"]
+    fwd_t = fl["fwd"] / (kms["fwd"] * 1e-3) / 1e12
+    rec = {"workload": describe(w), "pass": w.passes, "ms_per_step": round(ms, 4),
+           "tflops": round(total / (ms * 1e-3) / 1e12, 2),
+           "fwd": {"ms": round(kms["fwd"], 4), "tflops": round(fwd_t, 1), "frac": frac(fwd_t)},
+           "workspace_bytes": {"fwd": r.fws_bytes, "bwd": r.bws_bytes}}
+    rec["frac"] = frac(rec["tflops"])
+    fused = r.design == ea.BWD_FUSED_DQ
+    stored = r.design == ea.BWD_STORED_DS
+    names = {"fwd": f"fwd_kernel<{w.head_dim}>",
+             "bwd_main": f"{'bwd_main' if fused else 'bwd_dkdv'}_kernel<{w.head_dim}>",
+             "bwd_dq": f"bwd_dq_{'ds_' if stored else ''}kernel<{w.head_dim}>",
+             "bwd_pre": "bwd_pre_kernel", "bwd_post": "bwd_post_kernel"}
+    half = fl["fwd"] / 2.0
+    kflops = {"fwd": fl["fwd"], "bwd_main": (5 if fused else 4) * half, "bwd_dq": half}
+    kernels = {}
+    for n, t in kms.items():
+        if t <= 0.002:
+            continue
+        e = {"ms": round(t, 4)}
+        if n in kflops:
+            e["tflops"] = round(kflops[n] / (t * 1e-3) / 1e12, 1)
+        kernels[names[n]] = e
+    if r.with_bwd:
+        bwd_t = fl["bwd"] / (bwd_ms * 1e-3) / 1e12
+        rec["bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bwd_t, 1), "frac": frac(bwd_t),
+                      "design": DESIGN_NAMES[r.design], "deterministic": bool(w.deterministic)}
+        if stored and kms.get("bwd_dq", 0) > 0.002:
+            b = stored_ds_read_bytes(w, r.lengths)
+            gbs = b / (kms["bwd_dq"] * 1e-3) / 1e9
+            kernels[names["bwd_dq"]].update({"bound": "hbm", "algorithmic_bytes": b,
+                                             "gbs": round(gbs, 1),
+                                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    rec["kernels"] = kernels
+    abi = {"attn_fwd" + ("_varlen" if r.varlen else ""): r.abi_times(r.fwd)}
+    if r.with_bwd:
+        abi["attn_bwd" + ("_varlen" if r.varlen else "")] = r.abi_times(r.bwd)
+    rec["abi_ms"] = abi
+    # the dominant kernel (for the roofline object)
+    dom = max((n for n in kms if n in kflops), key=lambda n: kms[n])
+    rec["_dominant"] = {"name": names[dom], "ms": kms[dom], "flops": kflops[dom]}
+    if cpu_budget > 0:
+        print(f"[bench] {w.name}: float64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, cpu_budget)
+    print(f"[bench] {w.name}: {rec['tflops']} TFLOP/s, {ms:.3f} ms/step; fwd {rec['fwd']}"
+          + (f"; bwd {rec['bwd']}" if r.with_bwd else ""), file=sys.stderr, flush=True)
+    del r
+    torch.cuda.empty_cache()
+    return rec
+
+
+def ablations(torch, ea, args) -> dict:
+    """Schedule and design ablations the pages report for their own hardware."""
+    from workloads import Workload, make_inputs, workload_flops, WORKLOADS
+    out = {}
+    # longest-first (LPT) schedule on / off, causal, MHA and MQA (blog page,
+    # scheduling section; digest page item 5)
+    for tag, hkv in (("mha", 16), ("mqa", 1)):
+        w = Workload(f"lpt_{tag}", 3, 2, 16, hkv, 8192, 128, True, "fwd+bwd")
+        inp = make_inputs(2, 8192, 8192, 16, hkv, 128, seed=71003)
+        fl = workload_flops(w)
+        res = {}
+        for name, opts in (("lpt", {}), ("natural", {"tile_order": 1})):
+            r = Runner(torch, ea, w, opts, inputs=inp)
+            ms, kms = r.timed_steps(args.warmup, args.steps)
+            bms = sum(kms.get(n, 0.0) for n in ("bwd_pre", "bwd_main", "bwd_dq", "bwd_post"))
+            res[name] = {"fwd_tflops": round(fl["fwd"] / (kms["fwd"] * 1e-3) / 1e12, 1),
+                         "bwd_tflops": round(fl["bwd"] / (bms * 1e-3) / 1e12, 1)}
+            del r
+        res["fwd_gain"] = round(res["lpt"]["fwd_tflops"] / res["natural"]["fwd_tflops"] - 1, 4)
+        res["bwd_gain"] = round(res["lpt"]["bwd_tflops"] / res["natural"]["bwd_tflops"] - 1, 4)
+        out[f"lpt_causal_{tag}"] = dict(res, workload=f"B2 Hq16 Hkv{hkv} S8192 d128 causal")
+        print(f"[bench] ablation lpt {tag}: {out[f'lpt_causal_{tag}']}", file=sys.stderr, flush=True)
+        del inp
+    # fused design: deterministic (semaphore-ordered dQ) vs atomic dQ (blog page,
+    # deterministic-mode section), and the split default for reference
+    w = WORKLOADS["det16k_d128"]
+    from workloads import workload_inputs
+    inp = workload_inputs(w, device="cuda:0")
+    fl = workload_flops(w)
+    res = {}
+    for name, det, opts in (("fused_deterministic", True, {"bwd_design": 3}),
+                            ("fused_atomic", False, {"bwd_design": 3}),
+                            ("split_default", True, {})):
+        wv = Workload(w.name, w.number, w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim,
+                      w.causal, w.passes, deterministic=det)
+        r = Runner(torch, ea, wv, opts, inputs=inp)
+        ms, kms = r.timed_steps(args.warmup, args.steps)
+        bms = sum(kms.get(n, 0.0) for n in ("bwd_pre", "bwd_main", "bwd_dq", "bwd_post"))
+        res[name] = {"bwd_tflops": round(fl["bwd"] / (bms * 1e-3) / 1e12, 1), "bwd_ms": round(bms, 4)}
+        del r
+    res["deterministic_over_atomic"] = round(res["fused_deterministic"]["bwd_tflops"]
+                                             / res["fused_atomic"]["bwd_tflops"], 4)
+    out["deterministic_vs_atomic"] = dict(res, workload="B1 H8 S16384 d128 causal")
+    print(f"[bench] ablation det: {out['deterministic_vs_atomic']}", file=sys.stderr, flush=True)
+    del inp
+    # forward sequence-length sweep, non-causal H16 d128, 16k tokens per batch
+    # (digest page, sequence-length benchmark table: 1k .. 32k)
+    sweep = {}
+    for s in (1024, 2048, 4096, 8192, 16384, 32768):
+        b = max(1, 16384 // s)
+        w = Workload(f"sweep{s}", 7, b, 16, 16, s, 128, False, "fwd")
+        r = Runner(torch, ea, w, {}, inputs=make_inputs(b, s, s, 16, 16, 128, seed=7100 + s,
+                                                        with_grad=False, device="cuda:0"))
+        ms, kms = r.timed_steps(max(3, args.warmup // 2), max(5, args.steps // 2))
+        t = workload_flops(w)["fwd"] / (kms["fwd"] * 1e-3) / 1e12
+        sweep[str(s)] = {"batch": b, "tflops": round(t, 1), "frac": frac(t)}
+        del r
+    out["fwd_seqlen_sweep"] = dict(sweep, workload="non-causal B*S = 16384 (B1 at 32768), H16 d128")
+    print(f"[bench] sweep: {sweep}", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    return out
 
 
 def sweep_tau_exp(torch, ea, args) -> int:
@@ -176,23 +440,20 @@ def sweep_tau_exp(torch, ea, args) -> int:
         lse = torch.empty((1, 8, 16384), dtype=torch.float32, device="cuda:0")
         for tau in (0, 4, 8, 16):
             for emu in (0, 1, 2, 4):
-                ea.set_tuning("tau", tau)
-                ea.set_tuning("exp_emulation", emu)
+                opts = dict(tau=-1.0 if tau == 0 else float(tau), exp_emulation=emu)
                 for _ in range(args.warmup):
-                    ea.fwd(q, k, v, causal=True, out=o, lse_out=lse)
+                    ea.fwd(q, k, v, causal=True, out=o, lse_out=lse, options=opts)
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
                 a.record()
                 for _ in range(args.steps):
-                    ea.fwd(q, k, v, causal=True, out=o, lse_out=lse)
+                    ea.fwd(q, k, v, causal=True, out=o, lse_out=lse, options=opts)
                 b.record()
                 torch.cuda.synchronize()
                 ms = a.elapsed_time(b) / args.steps
                 print(json.dumps({"sweep": "tau_exp", "head_dim": d, "tau": tau, "exp_emulation": emu,
                                   "fwd_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}),
                       flush=True)
-    ea.set_tuning("tau", 8)
-    ea.set_tuning("exp_emulation", -1)
     return 0
 
 
@@ -203,16 +464,14 @@ def main() -> int:
     # MFMA load, so the default warmup covers about 50 ms of steps
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="causal8k")
+    ap.add_argument("--workload", default="all", help="all, or one of " + ", ".join(ORDER))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--bwd-fused-dq", action="store_true",
-                    help="time the fused backward (dQ atomics) instead of dK/dV + dQ kernels")
-    ap.add_argument("--bwd-recompute-dq", action="store_true",
-                    help="dQ kernel recomputing S and dP instead of reading the dS the dK/dV "
-                         "kernel stores")
-    ap.add_argument("--bwd-store-ds", action="store_true",
-                    help="dQ from the dS the dK/dV kernel stores (fixed length)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of float64 oracle work for the headline workload (others: 1/4)")
+    ap.add_argument("--no-ablations", action="store_true")
+    ap.add_argument("--bwd-design", type=int, default=0,
+                    help="0 library default, 1 recomputing dQ, 2 stored dS (budget 1 TiB), "
+                         "3 fused dQ")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: forward throughput over tau in {0,4,8,16} x "
                          "exp_emulation in {0,1,2,4} x d in {64,128,256} (B1 H8 S16384 causal, "
@@ -229,206 +488,64 @@ def main() -> int:
     import torch
 
     import exact_attention_71_amd as ea
-    from workloads import WORKLOADS, draw_lengths, workload_flops, workload_inputs
+    from workloads import WORKLOADS
 
-    w = WORKLOADS[args.workload]
-    dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.sweep:
         return sweep_tau_exp(torch, ea, args)
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    print(f"[bench] workload {_describe(w)}", file=sys.stderr, flush=True)
-    inp = workload_inputs(w, device=dev)
-    lengths = draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number) if w.varlen else None
-    fl = workload_flops(w, lengths)
-    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
-    with_bwd = w.passes == "fwd+bwd"
-
-    if w.varlen:
-        cu_q = inp["cu_seqlens_q"].to(dev)
-        cu_k = inp["cu_seqlens_k"].to(dev)
-        mx = max(lengths)
-        tq, hq, d = q.shape
-        p = ea.make_params(w.num_seqs, mx, mx, w.heads_q, w.heads_kv, d, w.scale, w.causal,
-                           w.deterministic, total_q=tq, total_k=k.shape[0])
-        o = torch.empty_like(q)
-        lse = torch.empty((hq, tq), dtype=torch.float32, device=dev)
-    else:
-        cu_q = cu_k = None
-        b, s, hq, d = q.shape
-        p = ea.make_params(b, s, s, w.heads_q, w.heads_kv, d, w.scale, w.causal, w.deterministic)
-        o = torch.empty_like(q)
-        lse = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
-    varlen = w.varlen
-    lib = ea.load()
-    import ctypes
-    if args.bwd_fused_dq:
-        ea.set_tuning("bwd_fused_dq", 1)
-    if args.bwd_store_ds:
-        ea.set_tuning("bwd_store_ds", 1)
-    if args.bwd_recompute_dq:
-        ea.set_tuning("bwd_store_ds", 0)
-    fused = ea.get_tuning("bwd_fused_dq")
-    # the workspace size depends on the backward design (the stored dS lives there)
-    stored_ds = ea.bwd_stores_ds(p, varlen) == 1
-    fws = torch.empty(max(1, ea.fwd_workspace_size(p, varlen)), dtype=torch.uint8, device=dev)
-    bws = torch.empty(max(1, ea.bwd_workspace_size(p, varlen)), dtype=torch.uint8, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-
-    def run_fwd():
-        st = stream()
-        if varlen:
-            r = lib.attn_fwd_varlen(ctypes.byref(p), cu_q.data_ptr(), cu_k.data_ptr(), q.data_ptr(),
-                                    k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                    fws.data_ptr(), fws.numel(), st)
-        else:
-            r = lib.attn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                             lse.data_ptr(), fws.data_ptr(), fws.numel(), st)
-        assert r == 0, r
-
-    def run_bwd_phase(mask):
-        r = lib.attn_bwd_phases(ctypes.byref(p), None if cu_q is None else cu_q.data_ptr(),
-                                None if cu_k is None else cu_k.data_ptr(), mask, q.data_ptr(),
-                                k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                bws.data_ptr(), bws.numel(), stream())
-        assert r == 0, r
-
-    def stream():
-        return torch.cuda.current_stream().cuda_stream
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    # per-kernel HIP events on the launch stream: name -> list of (start, end)
-    marks = {}
-
-    def timed(name, fn, on):
-        if not on:
-            fn()
-            return
-        a, b = ev(), ev()
-        a.record()
-        fn()
-        b.record()
-        marks.setdefault(name, []).append((a, b))
-
-    def step(on: bool):
-        timed("fwd", run_fwd, on)
-        if not with_bwd:
-            return
-        timed("bwd_pre", lambda: run_bwd_phase(ea.BWD_PREPROCESS), on)
-        timed("bwd_main", lambda: run_bwd_phase(ea.BWD_MAIN), on)
-        timed("bwd_dq", lambda: run_bwd_phase(ea.BWD_DQ), on)
-        timed("bwd_post", lambda: run_bwd_phase(ea.BWD_POSTPROCESS), on)
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    t_start, t_end = ev(), ev()
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        step(True)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
-    kms = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in marks.items()}
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step; per kernel (ms): "
-          + ", ".join(f"{n} {t:.3f}" for n, t in kms.items()), file=sys.stderr, flush=True)
-    if with_bwd and w.deterministic:
-        assert ea.bwd_status(p, bws, varlen) == 0
-
-    # each public entry point as one ABI call (attn_fwd[_varlen]; attn_bwd[_varlen]
-    # = every backward launch), hipEvent-timed on the stream, median and min
-    def run_bwd_all():
-        st = stream()
-        if varlen:
-            r = lib.attn_bwd_varlen(ctypes.byref(p), cu_q.data_ptr(), cu_k.data_ptr(), q.data_ptr(),
-                                    k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                    bws.data_ptr(), bws.numel(), st)
-        else:
-            r = lib.attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                             do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                             bws.data_ptr(), bws.numel(), st)
-        assert r == 0, r
-
-    def abi_times(fn, n):
-        ts = []
-        for _ in range(n):
-            a, b = ev(), ev()
-            a.record()
-            fn()
-            b.record()
-            b.synchronize()
-            ts.append(a.elapsed_time(b))
-        ts.sort()
-        return {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4), "calls": n}
-
-    abi = {"attn_fwd" + ("_varlen" if varlen else ""): abi_times(run_fwd, 20)}
-    if with_bwd:
-        abi["attn_bwd" + ("_varlen" if varlen else "")] = abi_times(run_bwd_all, 20)
-
-    total_flops = fl["fwd+bwd"] if with_bwd else fl["fwd"]
-    value = total_flops / (ms * 1e-3) / 1e12
-    # algorithmic flops per kernel: forward 2 GEMMs; the key-block backward kernel
-    # S, dP, dV, dK (4 of the 5 backward GEMMs; all 5 when dQ is fused); the dQ
-    # kernel only dQ (its recomputed S and dP are not algorithmic work)
-    half = fl["fwd"] / 2.0
-    kflops = {"fwd": fl["fwd"], "bwd_main": (5 if fused else 4) * half,
-              "bwd_dq": 1 * half}
-    names = {"fwd": f"fwd_kernel<{w.head_dim}>",
-             "bwd_main": f"{'bwd_main' if fused else 'bwd_dkdv'}_kernel<{w.head_dim}>",
-             "bwd_dq": f"bwd_dq_{'ds_' if stored_ds else ''}kernel<{w.head_dim}>"}
-    dom = max((n for n in kms if n in kflops), key=lambda n: kms[n])
-    dom_ms = kms[dom]
-    dom_name = names[dom]
-    achieved = kflops[dom] / (dom_ms * 1e-3) / 1e12
-    kernels = {names[n]: {"ms": round(kms[n], 4),
-                          "tflops": round(kflops[n] / (kms[n] * 1e-3) / 1e12, 1)}
-               for n in kms if n in kflops and kms[n] > 0.002}
-    if stored_ds and kms.get("bwd_dq", 0) > 0.002:
-        # HBM-bound: its roofline is bandwidth, against the 8 TB/s peak
-        b = stored_ds_read_bytes(w, lengths)
-        gbs = b / (kms["bwd_dq"] * 1e-3) / 1e9
-        kernels[names["bwd_dq"]].update({"bound": "hbm", "algorithmic_bytes": b,
-                                         "gbs": round(gbs, 1),
-                                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    opts = {}
+    if args.bwd_design:
+        opts["bwd_design"] = args.bwd_design
+        if args.bwd_design == 2:
+            opts["ds_budget"] = 1 << 40
+    names = ORDER if args.workload == "all" else [args.workload]
+    head = HEADLINE if args.workload == "all" else args.workload
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget
+    recs = {}
+    for n in names:
+        recs[n] = measure(torch, ea, WORKLOADS[n], args, opts,
+                          cpu if n == head else (cpu / 4 if n != "small" else min(cpu, 2.0)))
+    h = recs[head]
+    dom = h.pop("_dominant")
+    for r in recs.values():
+        r.pop("_dominant", None)
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
     out = {
-        "metric": "attention fwd/bwd TFLOPs/s at hdim128 bf16; % of MI355X BF16 MFMA peak",
-        "value": round(value, 2),
+        "metric": METRIC,
+        "value": h["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
-        "config": {"workload": _describe(w), "pass": w.passes,
-                   "bwd_design": "fused dQ atomics" if fused else
-                                 ("dK/dV kernel storing dS + dQ = dS K kernel" if stored_ds
-                                  else "dK/dV kernel + dQ kernel recomputing S, dP"),
-                   "kernels": kernels, "abi_ms": abi, "device": device_info(torch),
-                   "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": dom_name,
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "config": {"workload": h["workload"], "pass": h["pass"],
+                   "fwd": h["fwd"], "bwd": h.get("bwd"),
+                   "pct_of_peak": round(100.0 * h["tflops"] / PEAK_BF16_TFLOPS, 2),
+                   "device": device_info(torch), "workloads": recs},
+        "roofline": {"bound": "mfma", "kernel": dom["name"], "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(dom_name, w.name),
-                     "avg_launch_ms": round(dom_ms, 4), "sources": sources_sha()},
+                     "traffic": measured_traffic(dom["name"], head.split(":")[0]),
+                     "avg_launch_ms": round(dom["ms"], 4), "workload": head,
+                     "sources": sources_sha()},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the float64 oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if "cpu_baseline" in h:
+        out["cpu_baseline"] = h["cpu_baseline"]
+    if args.workload == "all" and not args.no_ablations:
+        out["config"]["ablations"] = ablations(torch, ea, args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -7,16 +7,18 @@ fallback implementation.
 
 Entry points mirror the C ABI in ``include/attn71.h``:
 
-    fwd(q, k, v, causal=False, softmax_scale=None, return_lse=True)
+    fwd(q, k, v, causal=False, softmax_scale=None, return_lse=True, options=None)
     fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
-    bwd(q, k, v, o, do, lse, causal=False, softmax_scale=None, deterministic=False)
+    bwd(q, k, v, o, do, lse, causal=False, softmax_scale=None, deterministic=False, options=None)
     bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
-    bwd_phases(...)          the backward split into preprocess / main / postprocess
+    bwd_phases(...)          the backward split into its launches
+    bwd_design(params)       the backward design a call with these parameters runs
     tile_order(...)          the fixed-length tile schedule, evaluated on the host
-    set_tuning(key, value)   process-wide knobs ("tile_order", "persistent", "exp_emulation",
-                             "tau", "spin_limit", "bwd_fused_dq", "fwd_pingpong",
-                             "bwd_store_ds");
-                             get_tuning(key) reads back what was set
+
+Design and tuning choices are per call: ``options`` is a dict of
+``attn_options`` fields (bwd_design, tile_order, one_shot_grid,
+exp_emulation, tau, spin_limit, ds_budget); missing fields take the
+library's defaults. Nothing is process-global.
 """
 from __future__ import annotations
 
@@ -40,13 +42,23 @@ class AttnError(RuntimeError):
         super().__init__(f"{where}: {_lib().attn_status_string(status).decode()} (status {status})")
 
 
+BWD_AUTO, BWD_RECOMPUTE, BWD_STORED_DS, BWD_FUSED_DQ = 0, 1, 2, 3
+
+
+class AttnOptions(ctypes.Structure):
+    _fields_ = [("bwd_design", ctypes.c_int32), ("tile_order", ctypes.c_int32),
+                ("one_shot_grid", ctypes.c_int32), ("exp_emulation", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("spin_limit", ctypes.c_int32),
+                ("ds_budget", ctypes.c_int64)]
+
+
 class AttnParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
                 ("seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int32),
                 ("total_k", ctypes.c_int32), ("num_heads_q", ctypes.c_int32),
                 ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("deterministic", ctypes.c_int32)]
+                ("deterministic", ctypes.c_int32), ("opt", AttnOptions)]
 
 
 _LIB = None
@@ -56,8 +68,7 @@ _vp = ctypes.c_void_p
 EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
-           "attn_persistent_tile", "attn_bwd_stores_ds",
-           "attn_set_tuning"]
+           "attn_persistent_tile", "attn_bwd_design"]
 
 
 def _lib():
@@ -81,10 +92,9 @@ def _lib():
     lib.attn_bwd_status.argtypes = [_P, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_int32), _vp]
     lib.attn_tile_order.argtypes = [_P, ctypes.c_int32, _vp, ctypes.c_int64,
                                     ctypes.POINTER(ctypes.c_int64)]
-    lib.attn_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_int32]
     lib.attn_persistent_tile.argtypes = [ctypes.c_int32] * 5
     lib.attn_persistent_tile.restype = ctypes.c_int32
-    lib.attn_bwd_stores_ds.argtypes = [_P, ctypes.c_int32]
+    lib.attn_bwd_design.argtypes = [_P, ctypes.c_int32]
     for n in EXPORTS:
         if n not in ("attn_status_string", "attn_version", "attn_fwd_workspace_size",
                      "attn_bwd_workspace_size"):
@@ -120,11 +130,22 @@ def _expect(t: torch.Tensor, name: str, dtype=torch.bfloat16) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def make_options(options: Optional[dict] = None) -> AttnOptions:
+    """attn_options from a dict of its fields (missing fields: 0 = default)."""
+    o = AttnOptions()
+    for k, v in (options or {}).items():
+        if k not in dict(AttnOptions._fields_):
+            raise ValueError(f"unknown option {k!r}")
+        setattr(o, k, float(v) if k == "tau" else int(v))
+    return o
+
+
 def make_params(batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, scale, causal,
-                deterministic=False, total_q=0, total_k=0) -> AttnParams:
+                deterministic=False, total_q=0, total_k=0,
+                options: Optional[dict] = None) -> AttnParams:
     return AttnParams(int(batch), int(seqlen_q), int(seqlen_k), int(total_q), int(total_k),
                       int(heads_q), int(heads_kv), int(head_dim), float(scale), int(bool(causal)),
-                      int(bool(deterministic)))
+                      int(bool(deterministic)), make_options(options))
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
@@ -141,23 +162,24 @@ def bwd_workspace_size(p: AttnParams, varlen: bool = False) -> int:
     return _lib().attn_bwd_workspace_size(ctypes.byref(p), int(varlen))
 
 
-def bwd_stores_ds(p: AttnParams, varlen: bool = False) -> int:
-    """1: the backward stores dS and its dQ kernel runs dQ = alpha dS K; 0: dQ
-    recomputes S and dP (or is fused); -1: parameters the calls would reject."""
-    return _lib().attn_bwd_stores_ds(ctypes.byref(p), int(varlen))
+def bwd_design(p: AttnParams, varlen: bool = False) -> int:
+    """BWD_RECOMPUTE, BWD_STORED_DS or BWD_FUSED_DQ: the design a backward call
+    with these parameters runs; -1: parameters the calls would reject."""
+    return _lib().attn_bwd_design(ctypes.byref(p), int(varlen))
 
 
 # --------------------------------------------------------------------- forward
 def fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
         return_lse: bool = True, out: Optional[torch.Tensor] = None,
-        lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        lse_out: Optional[torch.Tensor] = None,
+        options: Optional[dict] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] bf16 -> (o [B, Sq, Hq, d], lse [B, Hq, Sq] fp32)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _expect(t, n)
     b, sq, hq, d = q.shape
     sk, hkv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    p = make_params(b, sq, sk, hq, hkv, d, scale, causal)
+    p = make_params(b, sq, sk, hq, hkv, d, scale, causal, options=options)
     o = torch.empty_like(q) if out is None else out
     lse = None
     if return_lse:
@@ -170,7 +192,8 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                causal: bool = False, softmax_scale: Optional[float] = None,
-               return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               return_lse: bool = True,
+               options: Optional[dict] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_seqlens int32 [n+1] -> (o, lse [Hq, Tq])."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _expect(t, n)
@@ -181,7 +204,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
     nseq = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     p = make_params(nseq, max_seqlen_q, max_seqlen_k, hq, hkv, d, scale, causal, total_q=tq,
-                    total_k=tk)
+                    total_k=tk, options=options)
     o = torch.empty_like(q)
     lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device) if return_lse else None
     ws = _workspace(fwd_workspace_size(p, True), q.device)
@@ -193,7 +216,8 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
 
 # -------------------------------------------------------------------- backward
 def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float] = None,
-        deterministic: bool = False, workspace: Optional[torch.Tensor] = None):
+        deterministic: bool = False, workspace: Optional[torch.Tensor] = None,
+        options: Optional[dict] = None):
     """Gradients (dq, dk, dv) of sum(do * o) for fixed-length BSHD inputs."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _expect(t, n)
@@ -201,7 +225,7 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float
     b, sq, hq, d = q.shape
     sk, hkv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    p = make_params(b, sq, sk, hq, hkv, d, scale, causal, deterministic)
+    p = make_params(b, sq, sk, hq, hkv, d, scale, causal, deterministic, options=options)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = workspace if workspace is not None else _workspace(bwd_workspace_size(p), q.device)
     _check(_lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
@@ -212,7 +236,8 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float
 
 def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                max_seqlen_k: int, causal: bool = False, softmax_scale: Optional[float] = None,
-               deterministic: bool = False):
+               deterministic: bool = False, workspace: Optional[torch.Tensor] = None,
+               options: Optional[dict] = None):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _expect(t, n)
     _expect(lse, "lse", torch.float32)
@@ -223,9 +248,9 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
     nseq = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     p = make_params(nseq, max_seqlen_q, max_seqlen_k, hq, hkv, d, scale, causal, deterministic,
-                    total_q=tq, total_k=tk)
+                    total_q=tq, total_k=tk, options=options)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = _workspace(bwd_workspace_size(p, True), q.device)
+    ws = workspace if workspace is not None else _workspace(bwd_workspace_size(p, True), q.device)
     _check(_lib().attn_bwd_varlen(ctypes.byref(p), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()),
@@ -263,20 +288,6 @@ def tile_order(p: AttnParams, which: int):
 def persistent_tile(g: int, r: int, grid: int, ntiles: int, nx: int = 8) -> int:
     """Tile position taken by persistent workgroup g in round r (-1: none)."""
     return int(_lib().attn_persistent_tile(g, r, grid, ntiles, nx))
-
-
-_TUNING = {"tile_order": 0, "persistent": 1, "exp_emulation": -1, "tau": 8,
-           "spin_limit": 1 << 26, "bwd_fused_dq": 0, "fwd_pingpong": 0, "bwd_store_ds": -1}
-
-
-def set_tuning(key: str, value: int) -> None:
-    _check(_lib().attn_set_tuning(key.encode(), int(value)), "attn_set_tuning")
-    _TUNING[key] = int(value)
-
-
-def get_tuning(key: str) -> int:
-    """Value last set through set_tuning (the library's default otherwise)."""
-    return _TUNING[key]
 
 
 def version() -> int:

@@ -22,18 +22,28 @@ constexpr int64_t kL2Bytes = 4ll << 20;         // L2 per XCD
 constexpr int64_t kMaxExtent = (1ll << 31) - 1; // 32-bit buffer offsets
 constexpr size_t kAlign = 256;
 
-struct Tuning {
-  int tile_order = 0;
-  int exp_emulation = -1; // -1: automatic (none: v_exp_f32 measured fastest at every head_dim)
-  int tau = 8;            // rescale threshold (log2 units); the pages' log2(256)
-  int spin_limit = 1 << 26;
-  int bwd_fused_dq = 0;   // 0: dK/dV kernel + separate dQ kernel; 1: dQ atomics in one kernel
-  int fwd_pingpong = 0;   // 1: phase-offset wave groups (d <= 128); 0: one phase per tile
-  int persistent = 1;     // 1: resident workgroups loop over the tiles; 0: one per tile
-  int bwd_store_ds = -1;  // 1: dK/dV kernel stores dS, dQ = dS K (fixed length, split design);
-                          // 0: dQ kernel recomputes S, dP; -1: stored at head_dim >= 128
+// Options of one call with defaults resolved (attn_options; all-zero = defaults).
+struct Opts {
+  int bwd_design;     // ATTN_BWD_* as requested (AUTO resolved by bwd_design_of)
+  bool natural;       // plain tile order
+  bool persistent;    // resident workgroups loop over the tiles
+  int exp_emulation;  // FMA-path exponentials of every 8
+  float tau;          // rescale threshold, log2 units
+  int spin_limit;
+  int64_t ds_budget;
 };
-Tuning g_tuning;
+Opts opts_of(const attn_params* p) {
+  const attn_options& o = p->opt;
+  Opts r;
+  r.bwd_design = o.bwd_design;
+  r.natural = o.tile_order != 0;
+  r.persistent = o.one_shot_grid == 0;
+  r.exp_emulation = o.exp_emulation;
+  r.tau = o.tau == 0.0f ? kTau : (o.tau < 0.0f ? 0.0f : o.tau);
+  r.spin_limit = o.spin_limit > 0 ? o.spin_limit : (1 << 26);
+  r.ds_budget = o.ds_budget > 0 ? o.ds_budget : ATTN_DS_BUDGET_DEFAULT;
+  return r;
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -50,6 +60,15 @@ attn_status check_params(const attn_params* p, bool varlen) {
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (varlen && (p->total_q < 0 || p->total_k < 0)) return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_options& o = p->opt;
+  if (o.bwd_design < ATTN_BWD_AUTO || o.bwd_design > ATTN_BWD_FUSED_DQ) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((o.tile_order != 0 && o.tile_order != 1) || (o.one_shot_grid != 0 && o.one_shot_grid != 1))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (o.exp_emulation != 0 && o.exp_emulation != 1 && o.exp_emulation != 2 && o.exp_emulation != 4)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!(o.tau == 0.0f || o.tau == -1.0f || (o.tau > 0.0f && o.tau <= 64.0f)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (o.spin_limit < 0 || o.ds_budget < 0) return ATTN_ERR_INVALID_ARGUMENT;
   // one (sequence, head) slab must stay within 32-bit byte offsets
   const int64_t d = p->head_dim;
   const int64_t ext_q = (int64_t)p->seqlen_q * p->num_heads_q * d * 4;  // fp32 dQ accumulator
@@ -86,31 +105,52 @@ struct BwdWs {
   size_t order_dq = 0, tile_prefix_dq = 0, ds = 0, ds_prefix = 0;
   size_t total = 0;
   int64_t n_sem = 0;
-  bool use_ds = false;
+  int design = ATTN_BWD_RECOMPUTE;
 };
-// Stored-dS backward: split design, and one (sequence, head)'s sub-tiles
-// (plus the rows a last query block may address past them) within 32-bit
-// buffer offsets (for packed sequences: at the longest lengths). Otherwise
-// the dQ kernel recomputes S and dP.
-bool bwd_uses_ds(const attn_params* p, bool) {
-  const bool on = g_tuning.bwd_store_ds < 0 ? p->head_dim >= 128 : g_tuning.bwd_store_ds != 0;
-  if (!on || g_tuning.bwd_fused_dq) return false;
-  const int64_t ext = ((int64_t)ds_nq32_of(p->seqlen_q) + 8) * ds_nk32_of(p->seqlen_k) * 2048;
-  return ext <= kMaxExtent;
+// Bytes of the stored-dS area: fixed length, B * Hq regions of the visible
+// sub-tiles (DsGeom); packed lengths, a bound from the totals and the longest
+// key length, 2 (ceil(total_q / 64) + batch) sub-rows of at most
+// 8 ceil(seqlen_k / 256) sub-tiles per query head (the exact regions are laid
+// out on the device by the varlen schedule pass).
+int64_t ds_area_bytes(const attn_params* p, bool varlen) {
+  if (varlen)
+    return (int64_t)p->num_heads_q * 2 * ((int64_t)cdiv(p->total_q, 64) + p->batch) *
+           (8ll * cdiv(p->seqlen_k, 256)) * 2048;
+  const DsGeom g = ds_geom(p->seqlen_q, p->seqlen_k, p->causal != 0);
+  return (int64_t)p->batch * p->num_heads_q * ds_region_tiles(g) * 2048;
+}
+// The backward design of a call (ATTN_BWD_AUTO resolved), -1 if the request
+// cannot be met (stored dS over the budget). Automatic: stored dS at
+// head_dim 128 and 256, where it measured 5 % and 11 % faster per fwd+bwd
+// step than recomputing S and dP in the dQ kernel; at 64 the dK/dV kernel's
+// extra writes cost more than the dQ kernel saves.
+int bwd_design_of(const attn_params* p, bool varlen) {
+  const Opts o = opts_of(p);
+  if (o.bwd_design == ATTN_BWD_FUSED_DQ || o.bwd_design == ATTN_BWD_RECOMPUTE) return o.bwd_design;
+  const bool fits = ds_area_bytes(p, varlen) <= o.ds_budget;
+  if (o.bwd_design == ATTN_BWD_STORED_DS) return fits ? ATTN_BWD_STORED_DS : -1;
+  return (p->head_dim >= 128 && fits) ? ATTN_BWD_STORED_DS : ATTN_BWD_RECOMPUTE;
 }
 int64_t bwd_mblocks(const attn_params* p, bool varlen) {
   const int bm = bwd_block_m(p->head_dim);
   return varlen ? (int64_t)cdiv(p->total_q, bm) + p->batch
                 : (int64_t)p->batch * cdiv(p->seqlen_q, bm);
 }
+// Workspace regions (256-byte aligned): -D and LSE log2 e per (row, query
+// head); the fp32 dQ accumulator and the semaphores only for the fused
+// design; ticket / status / tile counters; the varlen schedule tables; the
+// stored dS.
 BwdWs bwd_ws(const attn_params* p, bool varlen) {
   BwdWs w;
+  w.design = bwd_design_of(p, varlen);
+  const bool fused = w.design == ATTN_BWD_FUSED_DQ;
   const int64_t rq = rows_q_of(p, varlen);
   size_t off = 0;
   w.dsum = off; off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q));
   w.lse2 = off; off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q));
-  w.dq_acc = off; off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q * p->head_dim));
-  w.n_sem = p->deterministic ? bwd_mblocks(p, varlen) * p->num_heads_q : 0;
+  w.dq_acc = off;
+  if (fused) off = align_up(off + sizeof(float) * (size_t)(rq * p->num_heads_q * p->head_dim));
+  w.n_sem = fused && p->deterministic ? bwd_mblocks(p, varlen) * p->num_heads_q : 0;
   w.sem = off; off = align_up(off + sizeof(int) * (size_t)w.n_sem);
   w.misc = off; off = align_up(off + 64);
   if (varlen) {
@@ -120,18 +160,13 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
     w.order_dq = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
     w.tile_prefix_dq = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
   }
-  if (bwd_uses_ds(p, varlen)) {
-    w.use_ds = true;
-    // packed sequences: sum over s of ds_nq32(Lq_s) <= 2 (cdiv(total_q, 64) + batch) and
-    // ds_nk32(Lk_s) <= ds_nk32(longest); the exact prefix is computed on the device
-    const int64_t nq_total = varlen ? 2 * ((int64_t)cdiv(p->total_q, 64) + p->batch)
-                                    : (int64_t)p->batch * ds_nq32_of(p->seqlen_q);
+  if (w.design == ATTN_BWD_STORED_DS) {
     if (varlen) {
       w.ds_prefix = off;
       off = align_up(off + sizeof(int64_t) * ((size_t)p->batch + 1));
     }
     w.ds = off;
-    off = align_up(off + (size_t)nq_total * p->num_heads_q * ds_nk32_of(p->seqlen_k) * 2048);
+    off = align_up(off + (size_t)ds_area_bytes(p, varlen));
   }
   w.total = off;
   return w;
@@ -180,9 +215,9 @@ attn_status check_device() {
 }
 
 // CU count for persistent launches of the current device (after
-// check_device), or 0 when the knob asks for one workgroup per tile.
-int launch_cus() {
-  if (!g_tuning.persistent) return 0;
+// check_device), or 0 when the call asks for one workgroup per tile.
+int launch_cus(bool persistent) {
+  if (!persistent) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -227,19 +262,21 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   fp.nm = cdiv(p->seqlen_q, bm);
   fp.sec = section_width(2ll * p->seqlen_k * d * 2);
   fp.nxcd = kNxcd;
-  fp.natural = g_tuning.tile_order;
+  const Opts op = opts_of(p);
+  fp.natural = op.natural ? 1 : 0;
   fp.ntiles = fwd_grid(p, varlen);
   fp.causal = p->causal;
   fp.alpha = p->softmax_scale;
   fp.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  fp.tau = static_cast<float>(g_tuning.tau);
+  fp.tau = op.tau;
+  const int pcus = launch_cus(op.persistent);
   if (varlen) {
     char* base = static_cast<char*>(ws);
     int* order = reinterpret_cast<int*>(base + wl.order);
     int* tp = reinterpret_cast<int*>(base + wl.tile_prefix);
-    unsigned* queue = launch_cus() ? reinterpret_cast<unsigned*>(base + wl.queue) : nullptr;
+    unsigned* queue = pcus ? reinterpret_cast<unsigned*>(base + wl.queue) : nullptr;
     if (launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bm, order, tp, nullptr,
-                               1, queue, nullptr, 0, stream) != hipSuccess)
+                               1, queue, nullptr, 0, 0, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     fp.order = order;
     fp.tile_prefix = tp;
@@ -247,9 +284,8 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   }
   // the FMA-path exp2 issues from the same VALU port as v_exp_f32 here, and
   // with the hand-scheduled forward step every share E > 0 measured slower at
-  // head_dim 64, 128 and 256, so the automatic choice is none
-  const int emu = g_tuning.exp_emulation >= 0 ? g_tuning.exp_emulation : 0;
-  if (launch_fwd(fp, d, launch_cus(), emu, g_tuning.fwd_pingpong != 0, stream) != hipSuccess)
+  // head_dim 64, 128 and 256, so the default is none
+  if (launch_fwd(fp, d, pcus, op.exp_emulation, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -263,7 +299,9 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   if (st != ATTN_OK) return st;
   if (varlen && !cu_k) return ATTN_ERR_INVALID_ARGUMENT;
   if (phases <= 0 || phases > ATTN_BWD_ALL) return ATTN_ERR_INVALID_ARGUMENT;
-  const bool fused_mode = g_tuning.bwd_fused_dq != 0;
+  const BwdWs wl = bwd_ws(p, varlen);
+  if (wl.design < 0) return ATTN_ERR_UNSUPPORTED;   // stored dS requested over the budget
+  const bool fused_mode = wl.design == ATTN_BWD_FUSED_DQ;
   const bool pre = phases & ATTN_BWD_PREPROCESS, main = phases & ATTN_BWD_MAIN,
              post = (phases & ATTN_BWD_POSTPROCESS) && fused_mode,
              dqk = (phases & ATTN_BWD_DQ) && !fused_mode;
@@ -274,7 +312,6 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     return ATTN_ERR_INVALID_ARGUMENT;
   if (main && (!dk || !dv || !aligned16(dk) || !aligned16(dv))) return ATTN_ERR_INVALID_ARGUMENT;
   if ((post || dqk) && (!dq || !aligned16(dq))) return ATTN_ERR_INVALID_ARGUMENT;
-  const BwdWs wl = bwd_ws(p, varlen);
   if (ws_bytes < wl.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!ws) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->batch == 0) return ATTN_OK;
@@ -295,13 +332,15 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.status = reinterpret_cast<int*>(base + wl.misc + 4);
   bp.sv = make_sv(p, cu_q, cu_k);
   bp.hq = p->num_heads_q; bp.hkv = p->num_heads_kv; bp.group = p->num_heads_q / p->num_heads_kv;
-  const bool fused = g_tuning.bwd_fused_dq != 0;
+  const Opts op = opts_of(p);
+  const bool fused = fused_mode;
+  const bool use_ds = wl.design == ATTN_BWD_STORED_DS;
   const int bn = fused ? bwd_block_n(d) : dkdv_block_n(d), bm = bwd_block_m(d);
   bp.nn = cdiv(p->seqlen_k, bn);
   bp.nm = cdiv(p->seqlen_q, bm);
   bp.sec = section_width(2ll * bp.group * p->seqlen_q * d * 2);
   bp.nxcd = kNxcd;
-  bp.natural = g_tuning.tile_order;
+  bp.natural = op.natural ? 1 : 0;
   bp.ntiles = bwd_grid(p, varlen, fused);
   bp.ntiles_dq = dq_grid(p, varlen);
   bp.causal = p->causal;
@@ -311,10 +350,10 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.rows_q = rows_q_of(p, varlen);
   bp.n_sem = fused ? wl.n_sem : 0;
   bp.zero_acc = fused ? 1 : 0;
-  bp.spin_limit = g_tuning.spin_limit;
-  const int bmq = wl.use_ds ? DqDsCfg<128>::BM : dq_block_m(d);
+  bp.spin_limit = op.spin_limit;
+  const int bmq = use_ds ? DqDsCfg<128>::BM : dq_block_m(d);
   bp.nm_dq = cdiv(p->seqlen_q, bmq);
-  if (wl.use_ds) {
+  if (use_ds) {
     bp.ds = base + wl.ds;
     bp.ds_bytes = static_cast<int64_t>(wl.total - wl.ds);
     bp.ds_prefix = varlen ? reinterpret_cast<const int64_t*>(base + wl.ds_prefix) : nullptr;
@@ -333,7 +372,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   // static walk (measured 19 % slower dK/dV on 16 sequences of 512..8192):
   // there the persistent workgroups draw tiles from device counters, which
   // the varlen schedule pass clears.
-  const int pcus = launch_cus();
+  const int pcus = launch_cus(op.persistent);
   if (varlen && pcus) {
     bp.queue = reinterpret_cast<unsigned*>(base + wl.misc + 8);
     bp.queue_dq = reinterpret_cast<unsigned*>(base + wl.misc + 12);
@@ -344,12 +383,12 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
                                          const_cast<int*>(bp.tile_prefix),
                                          const_cast<int*>(bp.mb_prefix), bm, bp.queue,
                                          const_cast<int64_t*>(bp.ds_prefix), p->num_heads_q,
-                                         stream) != hipSuccess)
+                                         p->causal, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     if (varlen && !fused &&
         launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bmq,
                                const_cast<int*>(bp.order_dq), const_cast<int*>(bp.tile_prefix_dq),
-                               nullptr, 1, bp.queue_dq, nullptr, 0, stream) != hipSuccess)
+                               nullptr, 1, bp.queue_dq, nullptr, 0, 0, stream) != hipSuccess)
       return ATTN_ERR_HIP;
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
@@ -359,7 +398,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   if (dqk) {
-    const hipError_t e = wl.use_ds ? launch_bwd_dq_ds(bp, d, pcus, stream)
+    const hipError_t e = use_ds ? launch_bwd_dq_ds(bp, d, pcus, stream)
                                    : launch_bwd_dq(bp, d, pcus, stream);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
@@ -391,12 +430,13 @@ size_t attn_fwd_workspace_size(const attn_params* p, int32_t varlen) {
 
 size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen) {
   if (check_params(p, varlen != 0) != ATTN_OK) return (size_t)-1;
-  return bwd_ws(p, varlen != 0).total;
+  const BwdWs w = bwd_ws(p, varlen != 0);
+  return w.design < 0 ? (size_t)-1 : w.total;
 }
 
-int32_t attn_bwd_stores_ds(const attn_params* p, int32_t varlen) {
+int32_t attn_bwd_design(const attn_params* p, int32_t varlen) {
   if (check_params(p, varlen != 0) != ATTN_OK) return -1;
-  return bwd_ws(p, varlen != 0).use_ds ? 1 : 0;
+  return bwd_design_of(p, varlen != 0);
 }
 
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o,
@@ -464,7 +504,7 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
     *count = n;
     for (int i = 0; i < n && i < capacity; ++i) {
       const Tile t = fwd_tile_fixed(i, p->batch, p->num_heads_q, nm, sec, kNxcd,
-                                    g_tuning.tile_order != 0);
+                                    p->opt.tile_order != 0);
       out[3 * i] = t.seq; out[3 * i + 1] = t.head; out[3 * i + 2] = t.block;
     }
   } else {
@@ -476,7 +516,7 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
     *count = n;
     for (int i = 0; i < n && i < capacity; ++i) {
       const Tile t = bwd_tile_fixed(i, p->batch, p->num_heads_kv, nn, sec, which == 2, kNxcd,
-                                    g_tuning.tile_order != 0);
+                                    p->opt.tile_order != 0);
       out[3 * i] = t.seq; out[3 * i + 1] = t.head; out[3 * i + 2] = t.block;
     }
   }
@@ -487,39 +527,6 @@ int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles,
   if (g < 0 || g >= grid || r < 0 || ntiles < 0 || nx < 1 || grid < (ntiles < nx ? ntiles : nx))
     return -1;
   return persistent_index(g, r, grid, ntiles, nx);
-}
-
-attn_status attn_set_tuning(const char* key, int32_t value) {
-  if (!key) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!std::strcmp(key, "tile_order")) {
-    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.tile_order = value;
-  } else if (!std::strcmp(key, "persistent")) {
-    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.persistent = value;
-  } else if (!std::strcmp(key, "exp_emulation")) {
-    if (value != -1 && value != 0 && value != 1 && value != 2 && value != 4)
-      return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.exp_emulation = value;
-  } else if (!std::strcmp(key, "tau")) {
-    if (value < 0 || value > 64) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.tau = value;
-  } else if (!std::strcmp(key, "fwd_pingpong")) {
-    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.fwd_pingpong = value;
-  } else if (!std::strcmp(key, "bwd_fused_dq")) {
-    if (value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.bwd_fused_dq = value;
-  } else if (!std::strcmp(key, "bwd_store_ds")) {
-    if (value != -1 && value != 0 && value != 1) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.bwd_store_ds = value;
-  } else if (!std::strcmp(key, "spin_limit")) {
-    if (value < 1) return ATTN_ERR_INVALID_ARGUMENT;
-    g_tuning.spin_limit = value;
-  } else {
-    return ATTN_ERR_INVALID_ARGUMENT;
-  }
-  return ATTN_OK;
 }
 
 }  // extern "C"

@@ -93,14 +93,14 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
     const int r = slot / SPR, pos = slot % SPR;
     voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
   }
-  // ---- this wave's dS: sub-tile row qw0 / 32 of the head, NKB sub-tiles
-  // (contiguous, 2 KiB each) per key tile. Reads past the head's range give
-  // zero; a wave whose rows all lie past the sequence skips its MFMAs.
-  const int nk32 = ds_nk32_of(lk);
-  int ds_bh;
-  const int64_t ds_off = ds_region(p, t.seq, h, lq, lk, &ds_bh);
-  const rsrc_t dsr = raw_rsrc(p.ds + ds_off, ds_bh);
-  const int ds_row = (qw0 >> 5) * nk32 * 2048 + lane * 16;
+  // ---- this wave's dS: sub-row qw0 / 32 of the head's region (DsGeom),
+  // NKB sub-tiles (contiguous, 2 KiB each) per key tile. Reads past the row's
+  // range give zero; a wave whose rows all lie past the sequence skips its
+  // MFMAs.
+  int ds_rng;
+  const int64_t ds_off = ds_rows_at(p, ds_geom(lq, lk, causal), t.seq, h, qw0 >> 5, 1, &ds_rng);
+  const rsrc_t dsr = raw_rsrc(p.ds + ds_off, ds_rng);
+  const int ds_row = lane * 16;
   auto issue_k = [&](int n) {
     const int64_t t0 = (int64_t)n * BN * kstride;
     const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);

@@ -59,6 +59,9 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
 // only orders instructions with side effects, so pure VALU results would
 // otherwise be placed next to their (later) uses by instruction selection.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+// The same for a packed MFMA operand: formed here, not sunk next to its use
+// (where it would also sit inside the hazard window of an inline-asm MFMA).
+__device__ __forceinline__ void pin8(bf16x8& x) { asm volatile("" : "+v"(x)); }
 
 // Zero accumulator defined directly in AGPRs (an MFMA of zero operands with
 // C = 0), so a loop-carried accumulator never has a VGPR definition. The
@@ -213,6 +216,14 @@ template <typename T>
 __device__ __forceinline__ T keep_sgpr(T x) {
   asm volatile("" : "+s"(x));
   return x;
+}
+
+// A wave-uniform 64-bit value moved to scalar registers (the compiler cannot
+// always prove uniformity, e.g. of a value loaded through a per-tile index).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // Next tile position of a persistent workgroup in round r. queue == null:

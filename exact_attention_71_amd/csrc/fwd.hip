@@ -9,8 +9,9 @@
 // (blog page, correction-warpgroup list).
 //
 // gfx950 design (our own, not the pages' Blackwell pipeline):
-//  * workgroup = 4 wavefronts; each wave owns 32*QB query rows and runs both
-//    GEMMs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+//  * workgroup = 8 wavefronts, two per SIMD (4 at head_dim 256); each wave
+//    owns 32*QB query rows and runs both GEMMs on v_mfma_f32_32x32x16_bf16
+//    with fp32 accumulation;
 //  * S is computed transposed, S^T = K Q^T, so every lane owns one query row
 //    (lane % 32) and half of the keys of each 32-key block: the row max needs
 //    one exchange with lane ^ 32, the rescale factor is a per-lane scalar, and
@@ -32,18 +33,6 @@
 namespace attn71 {
 
 namespace {
-
-// Padded LDS rows: one extra 16-byte slot per row shifts consecutive rows by
-// one bank group, so 16 lanes reading 16 consecutive rows at the same column
-// hit 16 distinct bank groups, and every per-lane address is a lane base plus
-// a compile-time offset.
-template <int D, int BN>
-struct alignas(16) FwdSmem {
-  static constexpr int KR = D + 8;    // K row stride (elements)
-  static constexpr int VR = BN + 8;   // V^T row stride (elements)
-  alignas(16) bf16 k[2][BN * KR];
-  alignas(16) bf16 vt[2][D * VR];
-};
 
 __device__ __forceinline__ void seq_bounds(const SeqView& sv, int seq, int64_t* q0, int* lq,
                                            int64_t* k0, int* lk) {
@@ -489,258 +478,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Ping-pong variant (d <= 128): the 8 wavefronts form two groups of 4, one wave
-// of each group per SIMD. Every wave alternates
-//   MFMA phase (it):  S(it) = K(it) Q^T  and  O^T += V(it-1)^T P(it-1)
-//   VALU phase (it):  mask, row max, tau-rescale, P(it) = 2^(...), row sums,
-//                     P(it) packed to bf16 for the next MFMA phase
-// with a workgroup barrier between phases; group B starts one phase late, so
-// in every interval one wave per SIMD feeds the matrix core while its partner
-// runs the softmax. Group A stages K(it+1) and group B stages V(it+1) in their
-// VALU phases; each buffer is rewritten only after both groups' last read of
-// it (two phases earlier for B, three for A).
-// ---------------------------------------------------------------------------
-template <int D, int BN, int EMU>
-__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
-  constexpr int NW = 8;
-  constexpr int GT = 256;               // threads per group
-  constexpr int BM = NW * 32;
-  constexpr int KS = D / 16;
-  constexpr int NKB = BN / 32;
-  constexpr int NDB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int KCH = BN * CPR / GT;    // K chunks per group-A thread
-  constexpr int VUN = (BN / 4) * CPR;   // V units per tile
-  constexpr int VU = VUN / GT;          // V units per group-B thread
-  static_assert(KCH * GT == BN * CPR && VU * GT == VUN, "staging must divide evenly");
-  using SM = FwdSmem<D, BN>;
-  __shared__ SM sm;
-
-  Tile t;
-  if (p.sv.cu_q) {
-    t = varlen_tile(blockIdx.x, p.order, p.tile_prefix, p.sv.batch, p.hq, /*reverse=*/true);
-    if (t.seq < 0) return;
-  } else {
-    if ((int)blockIdx.x >= p.sv.batch * p.hq * p.nm) return;
-    t = fwd_tile_fixed(blockIdx.x, p.sv.batch, p.hq, p.nm, p.sec, p.nxcd, p.natural != 0);
-  }
-  int64_t qs, ks0;
-  int lq, lk;
-  seq_bounds(p.sv, t.seq, &qs, &lq, &ks0, &lk);
-  const int m0 = t.block * BM;
-  if (m0 >= lq) return;
-  const int h = t.head;
-  const int kvh = h / p.group;
-  const bool causal = p.causal != 0;
-  const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
-  const int n_tiles = cdiv(causal ? causal_key_end(m0 + BM, shift, lk) : lk, BN);
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const int grp = w >> 2;               // 0: group A (stages K), 1: group B (stages V)
-  const int gtid = tid & (GT - 1);
-  const int qw0 = m0 + w * 32;
-  const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
-  const bf16* __restrict__ qp = static_cast<const bf16*>(p.q);
-  const bf16* __restrict__ kp = static_cast<const bf16*>(p.k);
-  const bf16* __restrict__ vp = static_cast<const bf16*>(p.v);
-
-  const rsrc_t qr = make_rsrc(qp + qs * qstride + (int64_t)h * D, ((int64_t)(lq - 1) * qstride + D) * 2);
-  bf16x8 qf[KS];
-  {
-    const int voff = ((qw0 + c) * (int)qstride + 8 * g) * 2;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = buf_load16(qr, voff + 32 * kk, 0);
-  }
-
-  const int64_t kv_bytes = ((int64_t)(lk - 1) * kstride + D) * 2;
-  const bf16* kbase = kp + ks0 * kstride + (int64_t)kvh * D;
-  const bf16* vbase = vp + ks0 * kstride + (int64_t)kvh * D;
-  // group A: K chunks; group B: V units (same registers, different meaning)
-  constexpr int NREG = (KCH > 4 * VU) ? KCH : 4 * VU;
-  int soff[NREG];
-  bf16x8 sreg[NREG];
-#pragma unroll
-  for (int j = 0; j < NREG; ++j) {
-    if (grp == 0) {
-      const int u = gtid + GT * imin(j, KCH - 1);
-      soff[j] = ((u / CPR) * (int)kstride + (u % CPR) * 8) * 2;
-    } else {
-      const int u = gtid + GT * imin(j / 4, VU - 1);
-      int kg, dc;
-      unit_coords<CPR, BN / 4>(u, &kg, &dc);
-      soff[j] = ((4 * kg + (j & 3)) * (int)kstride + dc * 8) * 2;
-    }
-  }
-  auto load_stage = [&](int n) {
-    const int64_t t0 = (int64_t)n * BN * kstride;
-    const rsrc_t r = make_rsrc((grp == 0 ? kbase : vbase) + t0, kv_bytes - 2 * t0);
-    constexpr int NL = (KCH > 4 * VU) ? KCH : 4 * VU;
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      if ((grp == 0 && j < KCH) || (grp == 1 && j < 4 * VU)) sreg[j] = buf_load16(r, soff[j], 0);
-  };
-  auto store_stage = [&](int buf) {
-    if (grp == 0) {
-#pragma unroll
-      for (int j = 0; j < KCH; ++j) {
-        const int u = gtid + GT * j;
-        *reinterpret_cast<bf16x8*>(&sm.k[buf][(u / CPR) * SM::KR + (u % CPR) * 8]) = sreg[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < VU; ++j) {
-        const int u = gtid + GT * j;
-        int kg, dc;
-        unit_coords<CPR, BN / 4>(u, &kg, &dc);
-        const int pos = perm16(4 * kg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16x4 x;
-          x[0] = sreg[4 * j][e]; x[1] = sreg[4 * j + 1][e];
-          x[2] = sreg[4 * j + 2][e]; x[3] = sreg[4 * j + 3][e];
-          *reinterpret_cast<bf16x4*>(&sm.vt[buf][(dc * 8 + e) * SM::VR + pos]) = x;
-        }
-      }
-    }
-  };
-
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float mref = neg_inf(), lsum = 0.0f;
-  const float sl2 = p.scale_log2;
-  f32x16 s[NKB];
-  bf16x8 pb[NKB][2];
-
-  // prologue: K(0) by group A, V(0) by group B
-  if (n_tiles > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
-  if (grp == 1) __syncthreads();        // group B runs one phase behind
-
-  for (int it = 0; it <= n_tiles; ++it) {
-    // ---------------- MFMA phase
-    const bool more = it + 1 < n_tiles;
-    if (more) load_stage(it + 1);
-    const bool act = it < n_tiles && !(causal && it * BN > qw0 + 31 + shift);
-    const bool act_prev = it >= 1 && !(causal && (it - 1) * BN > qw0 + 31 + shift);
-    if (act) {
-      const int buf = it & 1;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &sm.k[buf][(kb * 32 + c) * SM::KR + (2 * kk + g) * 8]);
-          s[kb] = mfma32(a, qf[kk], s[kb]);
-        }
-    }
-    if (act_prev) {
-      const int buf = (it - 1) & 1;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int slot = kb * 4 + tt * 2 + g;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                &sm.vt[buf][(db * 32 + c) * SM::VR + slot * 8]);
-            oacc[db] = mfma32(a, pb[kb][tt], oacc[db]);
-          }
-        }
-    }
-    __syncthreads();
-    // ---------------- VALU phase
-    if (act) {
-      const int k0 = it * BN;
-      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
-      if (need_mask) {
-        const int qrow = qw0 + c;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + c_row(i, g);
-            const bool hide = key >= lk || (causal && key > qrow + shift);
-            s[kb][i] = hide ? neg_inf() : s[kb][i];
-          }
-      }
-      float mx = neg_inf();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kb][i], s[kb][i + 1]);
-      mx = fmaxf(mx, xor32(mx));
-      const float mnew = fmaxf(mref, mx);
-      if (wave_any((mnew - mref) * sl2 > p.tau)) {
-        const float fac = (mref == neg_inf()) ? 0.0f : fast_exp2((mref - mnew) * sl2);
-        lsum *= fac;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= fac;
-        mref = mnew;
-      }
-      const float nb = (mref == neg_inf()) ? 0.0f : -mref * sl2;
-      float acc = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = __builtin_fmaf(s[kb][i], sl2, nb);
-          const float e = ((i & 7) < EMU) ? emu_exp2(x) : fast_exp2(x);
-          s[kb][i] = e;
-          acc += e;
-        }
-        pb[kb][0] = pack_half(s[kb], 0);
-        pb[kb][1] = pack_half(s[kb], 1);
-      }
-      lsum += acc;
-    }
-    if (more) store_stage((it + 1) & 1);
-    __syncthreads();
-  }
-  if (grp == 0) __syncthreads();        // match group B's extra barrier
-
-  // ---- epilogue: O = O_acc / l (true statistics), LSE = alpha*m + ln(l)
-  const float lt = lsum + xor32(lsum);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  const int row = qw0 + c;
-  if (row < lq) {
-    bf16* dst = static_cast<bf16*>(p.o) + (qs + row) * qstride + (int64_t)h * D + 4 * g;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16& x = oacc[db];
-        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * j) =
-            pack4(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv, x[4 * j + 3] * inv);
-      }
-    if (g == 0 && p.lse) {
-      const float val = lt > 0.0f ? mref * p.alpha + fast_log2(lt) * 0.69314718055994531f
-                                  : neg_inf();
-      const int64_t off = p.sv.cu_q ? (int64_t)h * p.sv.total_q + qs + row
-                                    : ((int64_t)t.seq * p.hq + h) * p.sv.seqlen_q + row;
-      p.lse[off] = val;
-    }
-  }
-}
-
 template <int D, int EMU>
-hipError_t launch_d(const FwdParams& p, int cus, bool pingpong, hipStream_t stream) {
+hipError_t launch_d(const FwdParams& p, int cus, hipStream_t stream) {
   using C = FwdCfg<D>;
-  if constexpr (C::NW == 8 && C::QB == 1) {
-    if (pingpong) {   // one workgroup per tile
-      hipLaunchKernelGGL((fwd_pp_kernel<D, C::BN, EMU>), dim3(p.ntiles), dim3(512), 0, stream, p);
-      return hipGetLastError();
-    }
-  }
   static const int occ = resident_per_cu(fwd_kernel<D, C::NW, C::QB, C::BN, EMU>, C::NW * 64);
   const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
   hipLaunchKernelGGL((fwd_kernel<D, C::NW, C::QB, C::BN, EMU>), dim3(grid), dim3(C::NW * 64), 0,
@@ -751,14 +491,12 @@ hipError_t launch_d(const FwdParams& p, int cus, bool pingpong, hipStream_t stre
 }  // namespace
 
 // exp_emulation: 0 = all exp2 on v_exp_f32; E = 1, 2, 4: E of every 8 on the
-// FMA path. pingpong: use the two-group phase-offset kernel where it exists
-// (d <= 128).
-hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, bool pingpong,
-                      hipStream_t stream) {
+// FMA path.
+hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, hipStream_t stream) {
   if (p.ntiles <= 0) return hipSuccess;
   switch (d * 8 + exp_emulation) {
 #define ATTN71_FWD_CASE(D, E) \
-    case D * 8 + E: return launch_d<D, E>(p, cus, pingpong, stream);
+    case D * 8 + E: return launch_d<D, E>(p, cus, stream);
     ATTN71_FWD_CASE(64, 0) ATTN71_FWD_CASE(64, 1) ATTN71_FWD_CASE(64, 2) ATTN71_FWD_CASE(64, 4)
     ATTN71_FWD_CASE(128, 0) ATTN71_FWD_CASE(128, 1) ATTN71_FWD_CASE(128, 2) ATTN71_FWD_CASE(128, 4)
     ATTN71_FWD_CASE(256, 0) ATTN71_FWD_CASE(256, 1) ATTN71_FWD_CASE(256, 2) ATTN71_FWD_CASE(256, 4)

@@ -80,37 +80,88 @@ struct BwdParams {
   int64_t rows_q;         // total query rows (B*Sq or total_q)
   int64_t n_sem;          // semaphore words to clear (deterministic)
   int spin_limit;         // bounded wait for the deterministic chain
-  // Stored dS (null: the dQ kernel recomputes S and dP). Per (sequence,
-  // query head): ds_nq32_of(Lq) x ds_nk32_of(Lk) sub-tiles of 32 queries x 32
-  // keys, bf16, 2 KiB each, in the register order of the dK/dV kernel; the
-  // regions of the heads of a sequence follow each other, sequences in order.
+  // Stored dS (null: the dQ kernel recomputes S and dP): per (sequence,
+  // query head) a region of 32-query x 32-key bf16 sub-tiles, 2 KiB each, in
+  // the register order of the dK/dV kernel, holding only the sub-tiles that
+  // kernel writes (DsGeom below); the regions of the heads of a sequence follow
+  // each other, sequences in order.
   char* ds;
   const int64_t* ds_prefix;  // varlen: first sub-tile of each sequence (null: fixed length)
-  int64_t ds_bytes;          // size of the dS area (regions are clamped to it)
+  int64_t ds_bytes;          // size of the dS area (every range is clamped to it)
 };
 
-// Stored-dS geometry: query blocks of 32 rounded to the dK/dV step (64 rows
-// at most), key blocks of 32 rounded to the dK/dV workgroup (256 keys at
-// most), so every sub-tile the dK/dV kernel writes lies inside its head.
-__host__ __device__ inline int ds_nq32_of(int seqlen_q) { return (seqlen_q + 63) / 64 * 2; }
-__host__ __device__ inline int ds_nk32_of(int seqlen_k) { return (seqlen_k + 255) / 256 * 8; }
+// Stored-dS geometry of one (sequence, query head) with lq queries and lk
+// keys. Sub-row r holds queries 32r .. 32r+31 (rows = 2 ceil(lq / 64): whole
+// dK/dV steps of up to 64 queries); it stores sub-columns 0 .. width(r) - 1,
+// 32 keys each. Widths are whole key blocks of 256 keys (the dK/dV workgroup)
+// and constant over groups of 8 sub-rows (256 queries): group G stores the
+// key blocks that reach into it, all kb of them without a causal mask, and
+// blocks [0, G + c) with c = 1 + ceil((lk - lq) / 256) under the bottom-right
+// causal diagonal (key block n writes the rows from its first visible one on,
+// and 256 n - (lk - lq) >= 256 (G + 1) keeps it out of group G). A row's
+// sub-tiles are contiguous; rows follow each other.
+struct DsGeom {
+  int rows;       // stored sub-rows
+  int kb;         // key blocks of 256 keys
+  int c;          // causal: group G holds min(max(G + c, 0), kb) blocks
+  int causal;
+  int64_t p0;     // causal: ds_psum(max(c, 0))
+};
 
-// Byte offset from p.ds of the stored-dS region of (sequence s, query head h)
-// with lq queries and lk keys; *bh_bytes = the region's size, clamped to the
-// dS area (packed lengths beyond the maximum the caller declared would
-// otherwise place a region past it; the buffer range then drops the stores).
-__device__ inline int64_t ds_region(const BwdParams& p, int s, int h, int lq, int lk,
-                                    int* bh_bytes) {
-  const int nq = ds_nq32_of(lq), nk = ds_nk32_of(lk);
-  const int64_t first = p.ds_prefix ? p.ds_prefix[s] : (int64_t)s * p.hq * nq * nk;
-  const int64_t off = (first + (int64_t)h * nq * nk) * 2048;
+__host__ __device__ inline int64_t ds_clampi(int64_t a, int64_t lo, int64_t hi) {
+  return a < lo ? lo : (a > hi ? hi : a);
+}
+// sum over a = 0 .. n-1 of min(a, kb) (n >= 0)
+__host__ __device__ inline int64_t ds_psum(int64_t n, int64_t kb) {
+  const int64_t n1 = n < kb + 1 ? n : kb + 1;
+  return n1 * (n1 - 1) / 2 + (n - n1) * kb;
+}
+__host__ __device__ inline DsGeom ds_geom(int lq, int lk, bool causal) {
+  DsGeom g;
+  g.rows = (lq + 63) / 64 * 2;
+  g.kb = (lk + 255) / 256;
+  g.causal = causal ? 1 : 0;
+  const int shift = lk - lq;
+  // ceil(shift / 256) for either sign
+  const int cdv = shift >= 0 ? (shift + 255) / 256 : -((-shift) / 256);
+  g.c = 1 + cdv;
+  g.p0 = causal ? ds_psum(g.c > 0 ? g.c : 0, g.kb) : 0;
+  return g;
+}
+// key blocks (of 256) stored for the rows of group G
+__host__ __device__ inline int ds_group_blocks(const DsGeom& g, int G) {
+  return g.causal ? (int)ds_clampi((int64_t)G + g.c, 0, g.kb) : g.kb;
+}
+// sub-tiles stored in sub-row r
+__host__ __device__ inline int ds_width(const DsGeom& g, int r) { return 8 * ds_group_blocks(g, r >> 3); }
+// sub-tiles stored before sub-row r (0 <= r <= rows)
+__host__ __device__ inline int64_t ds_row_start(const DsGeom& g, int r) {
+  if (!g.causal) return (int64_t)r * 8 * g.kb;
+  const int G = r >> 3;
+  const int64_t a = (int64_t)G + g.c;
+  const int64_t full = ds_psum(a > 0 ? a : 0, g.kb) - g.p0;   // blocks of groups 0 .. G-1
+  return 64 * full + (int64_t)(r - 8 * G) * 8 * ds_group_blocks(g, G);
+}
+// sub-tiles of the whole region
+__host__ __device__ inline int64_t ds_region_tiles(const DsGeom& g) { return ds_row_start(g, g.rows); }
+
+// Byte offset from p.ds of sub-row r of the region of (sequence s, query head
+// h) and, in *range, the bytes of the nr rows from there that lie inside the
+// dS area (a region past the area, from packed lengths beyond the maximum the
+// caller declared, gets range 0: its stores are dropped and its reads give
+// zero). Rows past the region get range 0 too. Wave-uniform.
+__device__ inline int64_t ds_rows_at(const BwdParams& p, const DsGeom& g, int s, int h, int r,
+                                     int nr, int* range) {
+  const int64_t reg = ds_region_tiles(g);
+  const int64_t first = p.ds_prefix ? p.ds_prefix[s] : (int64_t)s * p.hq * reg;
+  const int64_t off = (first + (int64_t)h * reg + ds_row_start(g, r)) * 2048;
+  int64_t n = r < g.rows ? (ds_row_start(g, r + nr < g.rows ? r + nr : g.rows) - ds_row_start(g, r)) * 2048 : 0;
   const int64_t room = p.ds_bytes - off;
-  const int64_t size = (int64_t)nq * nk * 2048;
-  // wave-uniform by construction (the tile is); made explicit for SGPRs
-  *bh_bytes = __builtin_amdgcn_readfirstlane(room <= 0 ? 0 : static_cast<int>(size < room ? size : room));
-  const int64_t r = room <= 0 ? 0 : off;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r >> 32));
+  if (n > room) n = room;
+  *range = __builtin_amdgcn_readfirstlane(n <= 0 ? 0 : static_cast<int>(n > 0x7fffffffLL ? 0x7fffffffLL : n));
+  const int64_t o = n <= 0 ? 0 : off;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(o));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(o >> 32));
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
@@ -181,8 +232,7 @@ inline int persistent_grid(int ntiles, int resident, int nx) {
 
 // Launchers. `cus` is the device's CU count for persistent launches, or 0 for
 // a one-shot grid of one workgroup per tile (p.ntiles).
-hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, bool pingpong,
-                      hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 // fused = true: dQ accumulated with fp32 atomics (or the deterministic
 // semaphore chain) inside the dK/dV kernel; false: dK/dV only.
@@ -200,10 +250,11 @@ hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
 // = first query block of actual sequence s with cdiv(len of q_cu, mb_blk);
 // clears *queue (optional) for the tile tickets of the launch that follows.
 // Optional ds_prefix[s] = first stored-dS sub-tile of sequence s (lengths
-// from q_cu and count_cu, ds_heads query heads each; see ds_region).
+// from q_cu and count_cu, ds_heads query heads each; see DsGeom).
 hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
                                   int nseq, int heads, int blk, int* order, int* tile_prefix,
                                   int* mb_prefix, int mb_blk, unsigned* queue,
-                                  int64_t* ds_prefix, int ds_heads, hipStream_t stream);
+                                  int64_t* ds_prefix, int ds_heads, int causal,
+                                  hipStream_t stream);
 
 }  // namespace attn71

@@ -19,7 +19,8 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(const int* __restr
                                                               int* order, int* tile_prefix,
                                                               int* mb_prefix, int mb_blk,
                                                               unsigned* queue,
-                                                              int64_t* ds_prefix, int ds_heads) {
+                                                              int64_t* ds_prefix, int ds_heads,
+                                                              int causal) {
   for (int s = threadIdx.x; s < nseq; s += blockDim.x) order[varlen_rank(key_cu, nseq, s)] = s;
   if (queue && threadIdx.x == 128) *queue = 0u;   // tile tickets of the launch that follows
   __syncthreads();
@@ -42,8 +43,8 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(const int* __restr
     int64_t acc = 0;
     ds_prefix[0] = 0;
     for (int s = 0; s < nseq; ++s) {
-      acc += (int64_t)ds_heads * ds_nq32_of(q_cu[s + 1] - q_cu[s]) *
-             ds_nk32_of(count_cu[s + 1] - count_cu[s]);
+      acc += (int64_t)ds_heads *
+             ds_region_tiles(ds_geom(q_cu[s + 1] - q_cu[s], count_cu[s + 1] - count_cu[s], causal != 0));
       ds_prefix[s + 1] = acc;
     }
   }
@@ -54,10 +55,11 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(const int* __restr
 hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
                                   int nseq, int heads, int blk, int* order, int* tile_prefix,
                                   int* mb_prefix, int mb_blk, unsigned* queue,
-                                  int64_t* ds_prefix, int ds_heads, hipStream_t stream) {
+                                  int64_t* ds_prefix, int ds_heads, int causal,
+                                  hipStream_t stream) {
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(256), 0, stream, key_cu, count_cu,
                      q_cu, nseq, heads, blk, order, tile_prefix, mb_prefix, mb_blk, queue,
-                     ds_prefix, ds_heads);
+                     ds_prefix, ds_heads, causal);
   return hipGetLastError();
 }
 

@@ -47,8 +47,10 @@
  *     error from the HIP runtime. Calls are asynchronous on `stream` (NULL =
  *     the default stream); faults surface at the caller's next
  *     synchronisation. Nothing is thrown across the ABI.
- *   - Reentrant; the only global state is a per-device attribute cache and
- *     the process-wide tuning knobs of attn_set_tuning.
+ *   - Reentrant. Every design choice and tuning value travels with the call
+ *     (attn_params.opt); the only global state is a once-initialised
+ *     per-device attribute cache (architecture, compute units). Workspace
+ *     sizes are pure functions of the parameters.
  */
 #ifndef ATTN71_H
 #define ATTN71_H
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ATTN71_VERSION 100 /* 0.1.0 */
+#define ATTN71_VERSION 200 /* 0.2.0: per-call options, visible-only stored dS */
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -70,6 +72,55 @@ typedef enum attn_status {
   ATTN_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the *_workspace_size value */
   ATTN_ERR_HIP = 4                  /* the HIP runtime refused a query or a launch */
 } attn_status;
+
+/* Backward designs (attn_options.bwd_design). All compute the same
+ * gradients; they differ in how dQ is formed (blog page, backward, 2-CTA
+ * backward and deterministic-mode sections):
+ *   ATTN_BWD_AUTO        stored dS at head_dim 128 and 256 when the dS area
+ *                        fits opt.ds_budget, else recomputing dQ;
+ *   ATTN_BWD_RECOMPUTE   a dK/dV kernel (one workgroup per key block, four
+ *                        GEMMs) plus a dQ kernel (one workgroup per query
+ *                        block) that recomputes S and dP; no atomics, every
+ *                        output written once: bit-reproducible;
+ *   ATTN_BWD_STORED_DS   the dK/dV kernel also writes the bf16 dS it forms
+ *                        into the workspace and the dQ kernel runs
+ *                        dQ = alpha dS K as its only GEMM; bit-reproducible;
+ *                        needs the dS area to fit opt.ds_budget
+ *                        (ATTN_ERR_UNSUPPORTED otherwise);
+ *   ATTN_BWD_FUSED_DQ    one key-block kernel for all five GEMMs that adds
+ *                        each tile's dQ into an fp32 buffer with atomics, or,
+ *                        with deterministic = 1, in a fixed order behind
+ *                        per-block semaphores; a postprocess converts dQ. */
+#define ATTN_BWD_AUTO 0
+#define ATTN_BWD_RECOMPUTE 1
+#define ATTN_BWD_STORED_DS 2
+#define ATTN_BWD_FUSED_DQ 3
+
+/* Per-call options. An all-zero struct selects every default. */
+typedef struct attn_options {
+  int32_t bwd_design;    /* ATTN_BWD_* above (default ATTN_BWD_AUTO) */
+  int32_t tile_order;    /* 0 (default): longest first over L2-sized batch-head
+                            sections, one contiguous range per XCD (blog page,
+                            scheduling section); 1: natural order (batch-head
+                            major, blocks ascending) */
+  int32_t one_shot_grid; /* 0 (default): as many workgroups as fit at once loop
+                            over the tiles (packed lengths: tickets from a
+                            workspace counter); 1: one workgroup per tile */
+  int32_t exp_emulation; /* 0 (default): every exp2 on v_exp_f32; 1, 2 or 4:
+                            that many of every 8 on the Cody-Waite + Horner FMA
+                            path (blog page, faster exponential section) */
+  float tau;             /* forward rescale threshold on the running-max jump,
+                            log2 units: 0 selects the default 8 = log2 256
+                            (digest page item 3; blog page, forward section);
+                            a value in (0, 64] is used as given; -1 selects 0
+                            (rescale on every increase of the row max) */
+  int32_t spin_limit;    /* deterministic fused backward: bound on each wait of
+                            the ordered dQ chain in polls (0: default 2^26) */
+  int64_t ds_budget;     /* bytes of stored dS the backward may place in its
+                            workspace (0: default ATTN_DS_BUDGET_DEFAULT) */
+} attn_options;
+
+#define ATTN_DS_BUDGET_DEFAULT (4ll << 30)
 
 typedef struct attn_params {
   int32_t batch;         /* fixed: B. varlen: number of packed sequences */
@@ -82,12 +133,12 @@ typedef struct attn_params {
   int32_t head_dim;      /* 64, 128 or 256 */
   float softmax_scale;   /* alpha */
   int32_t causal;        /* 0 or 1 */
-  int32_t deterministic; /* backward only, 0 or 1. The default split backward
-                            writes every output once and is bit-identical across
-                            runs either way; with bwd_fused_dq = 1, 0 = fp32
-                            atomics for dQ, 1 = fixed accumulation order,
-                            bit-identical dQ/dK/dV across runs (blog page,
-                            deterministic-mode section) */
+  int32_t deterministic; /* backward only, 0 or 1: bit-identical dQ/dK/dV across
+                            runs (blog page, deterministic-mode section). The
+                            recomputing and stored-dS designs write every output
+                            once and are bit-identical either way; the fused
+                            design orders its dQ additions when set */
+  attn_options opt;      /* per-call design and tuning options (zero: defaults) */
 } attn_params;
 
 /* "OK", "invalid argument", ... ; never NULL. */
@@ -96,21 +147,29 @@ const char* attn_status_string(attn_status status);
 int attn_version(void);
 
 /* Workspace bytes for a forward / backward call with these parameters
- * (varlen = 1 for the *_varlen calls). 0 means no workspace is needed.
- * Returns (size_t)-1 for parameters that the calls would reject. */
+ * (varlen = 1 for the *_varlen calls), a pure function of its arguments.
+ * 0 means no workspace is needed. Returns (size_t)-1 for parameters that the
+ * calls would reject. Packed lengths are sized from the totals, the batch
+ * count and the maxima seqlen_q / seqlen_k (the lengths themselves live on
+ * the device; the sizing variants of a spec that takes num_seqs and the
+ * maxima need the totals as well, for the per-row statistics). */
 size_t attn_fwd_workspace_size(const attn_params* p, int32_t varlen);
 size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen);
 
-/* 1 if a backward call with these parameters, under the current tuning
- * (attn_set_tuning "bwd_store_ds", "bwd_fused_dq"), has its dK/dV kernel store
- * dS into the workspace and computes dQ = alpha dS K from it; 0 if its dQ
- * kernel recomputes S and dP (or dQ is fused); -1 for parameters the calls
- * would reject. The stored dS takes B * Hq * ceil(Sq/64)*2 * ceil(Sk/256)*8
- * * 2 KiB of the workspace (about 2 bytes per query-key pair); for packed
- * lengths the workspace holds Hq * 2 (ceil(total_q/64) + batch) *
- * ceil(seqlen_k/256)*8 * 2 KiB, a bound from the total and the longest key
- * length (seqlen_k must bound every sequence's key length). */
-int32_t attn_bwd_stores_ds(const attn_params* p, int32_t varlen);
+/* The backward design a call with these parameters runs (ATTN_BWD_RECOMPUTE,
+ * ATTN_BWD_STORED_DS or ATTN_BWD_FUSED_DQ: opt.bwd_design with AUTO
+ * resolved), or -1 for parameters the calls would reject (including an
+ * explicit ATTN_BWD_STORED_DS whose dS does not fit opt.ds_budget).
+ * Stored dS keeps only the sub-tiles the causal mask leaves visible: per
+ * (sequence, query head) the 32-query rows of a 256-query group hold the
+ * 32 x 32 sub-tiles (2 KiB) of every 256-key block that reaches into the
+ * group, about 1 byte per query-key pair under a causal mask and 2 without
+ * (B2 H16 S8192 causal d128: 2.06 GiB). Packed lengths are sized by
+ * Hq * 2 (ceil(total_q/64) + batch) * ceil(seqlen_k/256) * 8 sub-tiles,
+ * a bound from the totals and the longest key length (seqlen_k must bound
+ * every sequence's key length; sequences beyond it drop stores rather than
+ * write past the workspace). */
+int32_t attn_bwd_design(const attn_params* p, int32_t varlen);
 
 /* Forward, fixed length. lse may be NULL (the LSE is optional on the pages:
  * blog page, correction-warpgroup list, "optionally compute and store LSE"). */
@@ -127,20 +186,9 @@ attn_status attn_fwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
                             size_t workspace_bytes, hipStream_t stream);
 
 /* Backward, fixed length: dq, dk, dv from q, k, v, the forward's o and lse
- * (required) and dout. Launches on `stream`: preprocess (D = rowsum(dO o O));
- * main; postprocess. Two designs, chosen by attn_set_tuning("bwd_fused_dq"):
- *   0 (default) main = a dK/dV kernel (one workgroup per key block, four
- *     GEMMs) plus a dQ kernel (one workgroup per query block, S and dP
- *     recomputed): no atomics, bit-reproducible whatever `deterministic` says;
- *   1 main = one kernel that also adds each tile's dQ into an fp32 buffer with
- *     atomics (blog page, 2-CTA backward, dQ atomic accumulation), or, with
- *     deterministic = 1, in a fixed order behind per-block semaphores (blog
- *     page, deterministic mode); postprocess converts dQ to bf16.
- * In the split design the dQ kernel either recomputes S and dP from q, k, v,
- * dout and lse, or (attn_bwd_stores_ds = 1) reads the dS that
- * the dK/dV kernel wrote into the workspace and runs dQ = alpha dS K, its
- * only GEMM (blog page, backward section: dQ is dS times the key block).
- * Both write dQ once: bit-reproducible either way. */
+ * (required) and dout. Launches on `stream`: preprocess (D = rowsum(dO o O)),
+ * then the kernels of opt.bwd_design (see ATTN_BWD_*): dK/dV and dQ kernels,
+ * or the fused kernel and its postprocess. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -163,7 +211,7 @@ attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
  * accumulator and, in deterministic mode, the ordering state. A MAIN phase
  * run without it still terminates and stays in bounds, but dQ accumulates on
  * the previous values and the deterministic order is not guaranteed. When
- * the call stores dS (attn_bwd_stores_ds), the DQ phase reads what the MAIN
+ * the call stores dS (attn_bwd_design), the DQ phase reads what the MAIN
  * phase of the same workspace wrote: run MAIN before DQ. */
 #define ATTN_BWD_PREPROCESS 1  /* D = rowsum(dO o O); fused design: clear dQ accumulator, semaphores */
 #define ATTN_BWD_MAIN 2        /* key-block kernel: dK, dV (fused design: + dQ accumulation) */
@@ -183,10 +231,10 @@ attn_status attn_bwd_phases(const attn_params* p, const int32_t* cu_seqlens_q,
 attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* workspace,
                             int32_t* status_out, hipStream_t stream);
 
-/* Tile order of the fixed-length kernels, evaluated on the host with the
- * same arithmetic the kernels use (scheduling section of the blog page:
- * longest first, L2-sized batch-head sections; here also one contiguous range
- * per XCD). which = 0: forward, out[3*i..3*i+2] = (batch, query head,
+/* Tile order of the fixed-length kernels under p->opt.tile_order, evaluated
+ * on the host with the same arithmetic the kernels use (scheduling section
+ * of the blog page: longest first, L2-sized batch-head sections; here also
+ * one contiguous range per XCD). which = 0: forward, out[3*i..3*i+2] = (batch, query head,
  * query block) of workgroup i; which = 1: dK/dV (or fused) backward,
  * which = 2: fused deterministic backward in ticket order, (batch, KV head,
  * key block); which = 3: dQ kernel, (batch, query head, query block).
@@ -202,40 +250,6 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
  * workgroup g stays on XCD g % nx; rounds alternate direction). Requires
  * grid >= min(ntiles, nx). No GPU is needed. */
 int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles, int32_t nx);
-
-/* Process-wide tuning knobs (not synchronised with launches in flight):
- *   "bwd_fused_dq"  0 = dK/dV kernel + dQ kernel (default), 1 = one kernel with
- *                   dQ atomics / semaphore-ordered adds (see attn_bwd);
- *   "fwd_pingpong"  1 = forward with two wave groups offset by one phase so
- *                   MFMA and softmax overlap (head_dim <= 128; measured slower on
- *                   MI355X so far), 0 = one phase per key tile (default);
- *   "tile_order"    0 = longest first + XCD ranges (default), 1 = natural
- *                   (batch-head major, blocks ascending, no remap);
- *   "persistent"    1 = resident workgroups loop over the tiles (default: a
- *                   static walk for fixed lengths, tickets from a workspace
- *                   counter for packed variable lengths); 0 = one workgroup
- *                   per tile;
- *   "exp_emulation" -1 = automatic (default: 0, the fastest measured at
- *                   every head_dim); 0 = every exp2 on
- *                   v_exp_f32; 1, 2 or 4 = that many of every 8 on the
- *                   Cody-Waite + Horner FMA path (blog page, faster exponential
- *                   section);
- *   "tau"           forward rescale threshold on the running-max jump, in
- *                   log2 units, 0..64 (default 8 = log2 256: digest page item
- *                   3; blog page, forward section). 0 rescales on every
- *                   increase of the row max;
- *   "spin_limit"    bound on each wait of the deterministic chain (default
- *                   2^26 polls);
- *   "bwd_store_ds"  split backward: -1 = automatic (default:
- *                   stored dS at head_dim 128 and 256, where it measured 5 %
- *                   and 11 % faster per fwd+bwd step; recomputation at 64,
- *                   where the dK/dV kernel's extra writes cost more than the
- *                   dQ kernel saves), 1 = the dK/dV kernel stores dS and dQ = alpha dS K,
- *                   0 = the dQ kernel recomputes S and dP. Heads whose
- *                   stored dS would exceed 2 GiB (at the longest lengths)
- *                   always recompute.
- * Returns ATTN_ERR_INVALID_ARGUMENT for unknown keys or values. */
-attn_status attn_set_tuning(const char* key, int32_t value);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ea.load()
-    assert ea.version() == 100
+    assert ea.version() == 200
     assert lib.attn_status_string(0) == b"OK"
     assert lib.attn_status_string(3) == b"workspace too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -46,7 +46,8 @@ def _p(**kw):
     base.update(kw)
     return ea.make_params(base["batch"], base["seqlen_q"], base["seqlen_k"], base["heads_q"],
                           base["heads_kv"], base["head_dim"], base["scale"], base["causal"],
-                          base["deterministic"], base.get("total_q", 0), base.get("total_k", 0))
+                          base["deterministic"], base.get("total_q", 0), base.get("total_k", 0),
+                          options=base.get("options"))
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
@@ -113,35 +114,59 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_workspace_sizes():
-    p = _p()
-    assert ea.fwd_workspace_size(p) == 0
     rows, hq, d = 2 * 300, 4, 128
+    p = _p(options=dict(bwd_design=ea.BWD_RECOMPUTE))
+    assert ea.fwd_workspace_size(p) == 0
     need = ea.bwd_workspace_size(p)
-    assert need >= rows * hq * 4 + rows * hq * d * 4          # D and the dQ accumulator
-    pd = _p(deterministic=True)
-    assert ea.bwd_workspace_size(pd) > need                     # + semaphores
+    assert 2 * rows * hq * 4 <= need < 2 * rows * hq * 4 + 1024   # -D, LSE log2 e, counters
+    fused = ea.bwd_workspace_size(_p(options=dict(bwd_design=ea.BWD_FUSED_DQ)))
+    assert fused >= need + rows * hq * d * 4                       # + the fp32 dQ accumulator
+    fused_det = ea.bwd_workspace_size(_p(deterministic=True, options=dict(bwd_design=3)))
+    assert fused_det > fused                                       # + semaphores
+    # deterministic costs nothing outside the fused design
+    assert ea.bwd_workspace_size(_p(deterministic=True, options=dict(bwd_design=1))) == need
     pv = _p(total_q=1000, total_k=1000, batch=5)
     assert ea.fwd_workspace_size(pv, True) > 0
     assert ea.fwd_workspace_size(_p(head_dim=80)) == SIZE_MAX
     assert ea.bwd_workspace_size(_p(heads_q=5)) == SIZE_MAX
 
 
-def test_tuning_knobs():
-    ea.set_tuning("tile_order", 1)
-    ea.set_tuning("tile_order", 0)
-    for e in (1, 2, 4, 0, -1):
-        ea.set_tuning("exp_emulation", e)
-    for t in (0, 64, 8):
-        ea.set_tuning("tau", t)
-    with pytest.raises(ea.AttnError):
-        ea.set_tuning("no_such_knob", 1)
-    for bad in (3, 5, 8, -2):
-        with pytest.raises(ea.AttnError):
-            ea.set_tuning("exp_emulation", bad)
-    for bad in (-1, 65):
-        with pytest.raises(ea.AttnError):
-            ea.set_tuning("tau", bad)
-    assert ea.get_tuning("tau") == 8 and ea.get_tuning("exp_emulation") == -1
+@pytest.mark.parametrize("opt", [dict(bwd_design=4), dict(bwd_design=-1), dict(tile_order=2),
+                                 dict(one_shot_grid=-1), dict(exp_emulation=3),
+                                 dict(exp_emulation=8), dict(tau=-2.0), dict(tau=65.0),
+                                 dict(tau=float("nan")), dict(spin_limit=-1),
+                                 dict(ds_budget=-1)])
+def test_options_are_validated(opt):
+    lib = ea.load()
+    p = _p(options=opt)
+    assert lib.attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+    assert lib.attn_bwd(ctypes.byref(p), *([FAKE] * 9), FAKE, 1 << 30, None) == INVALID
+    assert ea.fwd_workspace_size(p) == SIZE_MAX and ea.bwd_workspace_size(p) == SIZE_MAX
+    assert ea.bwd_design(p) == -1
+
+
+def test_valid_options_pass_validation():
+    lib = ea.load()
+    for opt in (dict(tau=-1.0), dict(tau=64.0), dict(tau=0.5), dict(exp_emulation=4),
+                dict(tile_order=1, one_shot_grid=1), dict(spin_limit=5), dict(ds_budget=1)):
+        p = _p(options=opt)
+        # fails on the null q pointer, i.e. after the options were accepted
+        assert lib.attn_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+        assert ea.bwd_workspace_size(p) != SIZE_MAX
+
+
+def test_workspace_size_is_a_pure_function_of_the_parameters():
+    """No process-wide state: sizes and designs depend on the parameters
+    (options included) alone, whatever other calls ran in between."""
+    cases = [_p(head_dim=d, causal=c, options=dict(bwd_design=b))
+             for d in (64, 128, 256) for c in (False, True) for b in range(4)]
+    first = [(ea.bwd_workspace_size(p), ea.bwd_design(p), ea.fwd_workspace_size(p)) for p in cases]
+    for p in reversed(cases):
+        ea.bwd_workspace_size(p)
+        ea.tile_order(p, 0)
+    again = [(ea.bwd_workspace_size(p), ea.bwd_design(p), ea.fwd_workspace_size(p)) for p in cases]
+    assert first == again
+    assert not hasattr(ea.load(), "attn_set_tuning") or "attn_set_tuning" not in ea.EXPORTS
 
 
 # ------------------------------------------------------------------ tile order
@@ -194,14 +219,12 @@ def test_backward_tile_orders(b, s, hq, hkv, d):
             assert all(idx[n] > idx[n + 1] for n in range(nn - 1))
 
 
-def test_natural_tile_order_knob():
-    p = _p(batch=1, seqlen_q=1024, seqlen_k=1024, heads_q=2, heads_kv=2, causal=True)
-    ea.set_tuning("tile_order", 1)
-    try:
-        nat = ea.tile_order(p, 0)
-    finally:
-        ea.set_tuning("tile_order", 0)
-    assert nat == [(0, h, m) for h in range(2) for m in range(4)]
+def test_natural_tile_order_option():
+    p = _p(batch=1, seqlen_q=1024, seqlen_k=1024, heads_q=2, heads_kv=2, causal=True,
+           options=dict(tile_order=1))
+    assert ea.tile_order(p, 0) == [(0, h, m) for h in range(2) for m in range(4)]
+    q = _p(batch=1, seqlen_q=1024, seqlen_k=1024, heads_q=2, heads_kv=2, causal=True)
+    assert ea.tile_order(q, 0) != ea.tile_order(p, 0)
 
 
 @pytest.mark.parametrize("n,grid,nx", [(1024, 256, 8), (1000, 256, 8), (300, 256, 8), (7, 7, 8),
@@ -249,51 +272,102 @@ def test_persistent_schedule_balances_causal_key_blocks():
     assert max(tot) == min(tot) == sum(steps) // 256
 
 
-def test_persistent_knob():
-    for v in (0, 1):
-        ea.set_tuning("persistent", v)
-    with pytest.raises(ea.AttnError):
-        ea.set_tuning("persistent", 2)
-    ea.set_tuning("persistent", 1)
+def test_stored_ds_selection_and_budget():
+    """Stored dS: automatic at head_dim 128 and 256 when its area fits the
+    budget, never at 64 or with another design requested; an explicit request
+    over the budget is refused (size -1, design -1)."""
+    for d, auto in ((64, 1), (128, 2), (256, 2)):
+        for varlen in (False, True):
+            kw = dict(batch=3, seqlen_q=300, seqlen_k=700, heads_q=4, heads_kv=2, head_dim=d,
+                      causal=True)
+            if varlen:
+                kw.update(total_q=500, total_k=1200)
+            assert ea.bwd_design(_p(**kw), varlen) == auto
+            for b in (1, 2, 3):
+                assert ea.bwd_design(_p(**kw, options=dict(bwd_design=b)), varlen) == b
+            area = (ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=2)), varlen)
+                    - ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=1)), varlen))
+            assert area > 0
+            tight = _p(**kw, options=dict(bwd_design=2, ds_budget=area - 1024))
+            assert ea.bwd_design(tight, varlen) == -1
+            assert ea.bwd_workspace_size(tight, varlen) == SIZE_MAX
+            assert ea.bwd_design(_p(**kw, options=dict(ds_budget=area - 1024)), varlen) == 1
+            assert ea.bwd_design(_p(**kw, options=dict(bwd_design=2, ds_budget=area)), varlen) == 2
+    # parameters the calls would reject (Hq not a multiple of Hkv; head_dim 96)
+    assert ea.bwd_design(ea.make_params(1, 10, 10, 3, 2, 128, 0.1, False, False)) == -1
+    assert ea.bwd_design(ea.make_params(1, 10, 10, 2, 2, 96, 0.1, False, False)) == -1
+    # no per-head size limit: S = 40000 causal d256 stores dS once the budget allows it
+    big = ea.make_params(1, 40000, 40000, 1, 1, 256, 0.1, True, False,
+                         options=dict(bwd_design=2, ds_budget=1 << 34))
+    assert ea.bwd_design(big) == 2
 
 
-def test_stored_ds_selection_and_workspace():
-    """Stored dS: automatic at head_dim 128 and 256, never with the fused
-    design; its workspace holds 2 KiB per 32 x 32 sub-tile of every (sequence,
-    query head) (packed lengths: a bound from the total and the longest, plus
-    the per-sequence offsets)."""
-    try:
-        for d, auto in ((64, 0), (128, 1), (256, 1)):
-            p = ea.make_params(2, 300, 700, 4, 2, d, 0.1, True, False)
-            pv = ea.make_params(3, 300, 700, 4, 2, d, 0.1, True, False, total_q=500, total_k=1200)
-            base_ws = base_vws = None
-            for mode, want in ((-1, auto), (0, 0), (1, 1)):
-                ea.set_tuning("bwd_store_ds", mode)
-                assert ea.bwd_stores_ds(p) == want, (d, mode)
-                assert ea.bwd_stores_ds(pv, varlen=True) == want, (d, mode)
-                if mode == 0:
-                    base_ws = ea.bwd_workspace_size(p)
-                    base_vws = ea.bwd_workspace_size(pv, varlen=True)
-            ea.set_tuning("bwd_store_ds", 1)
-            nq32, nk32 = -(-300 // 64) * 2, -(-700 // 256) * 8
-            extra = 2 * 4 * nq32 * nk32 * 2048
-            assert ea.bwd_workspace_size(p) - base_ws >= extra
-            assert ea.bwd_workspace_size(p) - base_ws < extra + 256
-            # packed: 2 (cdiv(500, 64) + 3) 32-row blocks bound sum_s ds_nq32(Lq_s)
-            vextra = 4 * 2 * (-(-500 // 64) + 3) * nk32 * 2048
-            assert ea.bwd_workspace_size(pv, varlen=True) - base_vws >= vextra + 8 * 4
-            assert ea.bwd_workspace_size(pv, varlen=True) - base_vws < vextra + 512
-            ea.set_tuning("bwd_fused_dq", 1)
-            assert ea.bwd_stores_ds(p) == 0
-            ea.set_tuning("bwd_fused_dq", 0)
-        # parameters the calls would reject (Hq not a multiple of Hkv; head_dim 96)
-        assert ea.bwd_stores_ds(ea.make_params(1, 10, 10, 3, 2, 128, 0.1, False, False)) == -1
-        assert ea.bwd_stores_ds(ea.make_params(1, 10, 10, 2, 2, 96, 0.1, False, False)) == -1
-        # one head's sub-tiles beyond 32-bit buffer offsets: recomputation
-        big = ea.make_params(1, 40000, 40000, 1, 1, 256, 0.1, True, False)
-        assert ea.bwd_stores_ds(big) == 0
-        with pytest.raises(ea.AttnError):
-            ea.set_tuning("bwd_store_ds", 2)
-    finally:
-        ea.set_tuning("bwd_store_ds", -1)
-        ea.set_tuning("bwd_fused_dq", 0)
+# ------------------------------------------------------- stored-dS layout
+def _dkdv_writes(lq, lk, d, causal):
+    """(sub-row, sub-column) pairs the dK/dV kernel stores: key block n of
+    256 keys (128 at head_dim 256) walks query steps of 32 rows (64 at head
+    dim 64) from the first that sees its first key (bottom-right diagonal)
+    to the end; every wave stores all of its sub-columns at every step."""
+    bn, bm = (256, 64) if d == 64 else ((256, 32) if d == 128 else (128, 32))
+    shift, nm = lk - lq, -(-lq // bm)
+    out = set()
+    for n in range(-(-lk // bn)):
+        m_first = min(max(0, n * bn - shift) // bm, nm) if causal else 0
+        for m in range(m_first, nm):
+            for r in range(m * bm // 32, (m + 1) * bm // 32):
+                for k in range(n * bn // 32, (n + 1) * bn // 32):
+                    out.add((r, k))
+    return out
+
+
+def _dq_reads(lq, lk, d, causal):
+    """(sub-row, sub-column) pairs the dQ kernel uses: wave rows 32 r (r with
+    rows inside the sequence), key tiles of 32 keys (64 at head_dim 64), the
+    sub-tiles with a visible pair for some row of the wave."""
+    bn, bmq = (64 if d == 64 else 32), 256
+    shift = lk - lq
+    out = set()
+    for r in range(-(-lq // 32)):
+        m0 = (32 * r) // bmq * bmq
+        kend = max(0, min(m0 + bmq + shift, lk)) if causal else lk
+        for n in range(-(-kend // bn)):
+            k0 = n * bn
+            lim = 32 * r + 31 + shift - k0 if causal else bn - 1
+            nv = 0 if lim < 0 else min(lim // 32 + 1, bn // 32)
+            for j in range(nv):
+                out.add((r, k0 // 32 + j))
+    return out
+
+
+def _ds_width(lq, lk, causal, r):
+    kb = -(-lk // 256)
+    if not causal:
+        return 8 * kb
+    shift = lk - lq
+    c = 1 + (-(-shift // 256))
+    return 8 * min(max(r // 8 + c, 0), kb)
+
+
+@pytest.mark.parametrize("lq,lk", [(300, 300), (8192, 8192), (1000, 1000), (64, 64), (1, 1),
+                                   (256, 257), (700, 300), (300, 700), (17, 4096), (4096, 17),
+                                   (513, 1024), (1024, 513), (2000, 2000 + 255), (33, 33)])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_stored_ds_layout_holds_every_write_and_read(lq, lk, d, causal):
+    """The visible-only layout (rows of whole 256-key blocks, widths constant
+    over 256-query groups) holds every sub-tile the dK/dV kernel writes, the
+    dQ kernel reads only written sub-tiles, and the library's area for B x Hq
+    regions equals the brute-force sum of the row widths."""
+    writes = _dkdv_writes(lq, lk, d, causal)
+    reads = _dq_reads(lq, lk, d, causal)
+    rows = -(-lq // 64) * 2
+    assert reads <= writes
+    for r, k in writes:
+        assert r < rows and k < _ds_width(lq, lk, causal, r), (r, k)
+    region = sum(_ds_width(lq, lk, causal, r) for r in range(rows))
+    kw = dict(batch=2, seqlen_q=lq, seqlen_k=lk, heads_q=3, heads_kv=1, head_dim=d, causal=causal)
+    area = (ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=2, ds_budget=1 << 40)))
+            - ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=1))))
+    assert 2 * 3 * region * 2048 <= area < 2 * 3 * region * 2048 + 256
+    if causal and d == 128 and lq == lk and lq % 256 == 0:
+        assert len(writes) == region       # tight: nothing stored that is not written

@@ -20,17 +20,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(params=[(0, 0, 0), (1, 0, 0), (1, 1, 0), (0, 0, 1)],
-                ids=["plainfwd-splitdq", "pingpong-splitdq", "pingpong-fuseddq", "plainfwd-storedds"])
+DESIGNS = {"recompute": dict(bwd_design=ea.BWD_RECOMPUTE),
+           "fused": dict(bwd_design=ea.BWD_FUSED_DQ),
+           "stored": dict(bwd_design=ea.BWD_STORED_DS)}
+
+
+@pytest.fixture(params=list(DESIGNS))
 def design(request):
-    pp, fused, ds = request.param
-    ea.set_tuning("fwd_pingpong", pp)
-    ea.set_tuning("bwd_fused_dq", fused)
-    ea.set_tuning("bwd_store_ds", ds)
-    yield request.param
-    ea.set_tuning("fwd_pingpong", 0)
-    ea.set_tuning("bwd_fused_dq", 0)
-    ea.set_tuning("bwd_store_ds", -1)
+    """Backward design under test (per-call options)."""
+    return DESIGNS[request.param]
 
 
 def _dev(inp):
@@ -55,7 +53,8 @@ def test_causal_unequal_lengths_match_oracle(sq, sk, hq, hkv, d, design):
     what = f"s{sq}/{sk} hq{hq} hkv{hkv} d{d}"
     print(f"[bottom-right] {what} design {design}", flush=True)
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=scale)
-    dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, softmax_scale=scale)
+    dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, softmax_scale=scale,
+                        options=design)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, True)
     check_o(o, o_ref, what)
@@ -75,12 +74,12 @@ def test_causal_unequal_lengths_deterministic(sq, sk, d, design):
     scale = 1.0 / math.sqrt(d)
     print(f"[bottom-right det] s{sq}/{sk} d{d} design {design}", flush=True)
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=scale)
-    p = ea.make_params(1, sq, sk, hq, hkv, d, scale, True, True)
+    p = ea.make_params(1, sq, sk, hq, hkv, d, scale, True, True, options=design)
     ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
     runs = []
     for _ in range(3):
         runs.append(ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True,
-                           softmax_scale=scale, deterministic=True, workspace=ws))
+                           softmax_scale=scale, deterministic=True, workspace=ws, options=design))
         torch.cuda.synchronize()
         assert ea.bwd_status(p, ws) == 0
     for r in runs[1:]:
@@ -104,7 +103,7 @@ def test_varlen_causal_per_sequence_lengths(design):
                            max(lk), causal=True, softmax_scale=scale)
     dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
                                g["cu_seqlens_k"], max(lq), max(lk), causal=True,
-                               softmax_scale=scale)
+                               softmax_scale=scale, options=design)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, True,
                                               inp["cu_seqlens_q"], inp["cu_seqlens_k"])

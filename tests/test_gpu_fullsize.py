@@ -98,12 +98,9 @@ def test_causal8k_full_size_fwd_bwd():
                              f"causal8k bwd b{b} h{h}")
     _identities(dk, dv, do, 1, "causal8k identities")
     # the fused design (fp32 dQ atomics across key blocks and XCDs) at full size
-    ea.set_tuning("bwd_fused_dq", 1)
-    try:
-        dq2, dk2, dv2 = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale)
-        torch.cuda.synchronize()
-    finally:
-        ea.set_tuning("bwd_fused_dq", 0)
+    dq2, dk2, dv2 = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale,
+                           options=dict(bwd_design=ea.BWD_FUSED_DQ))
+    torch.cuda.synchronize()
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)   # same dK/dV arithmetic
     _check_grads_sampled(dq2, dk2, dv2, q, k, v, do, 0, 1, 1, w.scale, True, rows, cols,
                          "causal8k fused bwd")
@@ -112,13 +109,10 @@ def test_causal8k_full_size_fwd_bwd():
     # reads the dS the dK/dV kernel stores)
     p = ea.make_params(w.batch, w.seqlen, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, w.scale,
                        True, False)
-    assert ea.bwd_stores_ds(p) == 1
-    ea.set_tuning("bwd_store_ds", 0)
-    try:
-        dq3, dk3, dv3 = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale)
-        torch.cuda.synchronize()
-    finally:
-        ea.set_tuning("bwd_store_ds", -1)
+    assert ea.bwd_design(p) == ea.BWD_STORED_DS
+    dq3, dk3, dv3 = ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale,
+                           options=dict(bwd_design=ea.BWD_RECOMPUTE))
+    torch.cuda.synchronize()
     assert torch.equal(dk, dk3) and torch.equal(dv, dv3)   # same dK/dV arithmetic
     for b, h in ((0, 1), (1, 9)):
         _check_grads_sampled(dq3, dk3, dv3, q, k, v, do, b, h, 1, w.scale, True, rows, cols,
@@ -158,18 +152,17 @@ def test_varlen_gqa_full_size_fwd_bwd():
         sl = slice(cuh[s], cuh[s + 1])
         _identities(dk[sl].unsqueeze(0), dv[sl].unsqueeze(0), do[sl].unsqueeze(0), group,
                     f"varlen identities seq{s}")
-    # the default here stores dS; the recomputing dQ kernel gives the same dK, dV
-    # bits and dQ within the bar on the shortest and the longest sequence
+    # the default here recomputes dQ (the stored-dS bound from the totals is
+    # over the default budget); stored dS with a budget that admits it gives
+    # the same dK, dV bits and dQ within the bar on the shortest and the
+    # longest sequence
     p = ea.make_params(w.num_seqs, mx, mx, w.heads_q, w.heads_kv, w.head_dim, w.scale, True,
                        False, total_q=q.shape[0], total_k=k.shape[0])
-    assert ea.bwd_stores_ds(p, varlen=True) == 1
-    ea.set_tuning("bwd_store_ds", 0)
-    try:
-        dq2, dk2, dv2 = ea.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, causal=True,
-                                      softmax_scale=w.scale)
-        torch.cuda.synchronize()
-    finally:
-        ea.set_tuning("bwd_store_ds", -1)
+    assert ea.bwd_design(p, varlen=True) == ea.BWD_RECOMPUTE
+    big = dict(bwd_design=ea.BWD_STORED_DS, ds_budget=1 << 40)
+    dq2, dk2, dv2 = ea.bwd_varlen(q, k, v, o, do, lse, cu, cu, mx, mx, causal=True,
+                                  softmax_scale=w.scale, options=big)
+    torch.cuda.synchronize()
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
     for s in (int(order[0]), int(order[-1])):
         sl = slice(cuh[s], cuh[s + 1])
@@ -179,7 +172,7 @@ def test_varlen_gqa_full_size_fwd_bwd():
         for h in (2, 29):
             dq_ref = oracle.head_dq_rows(_h(qs, 0, h), _h(ks, 0, h // group), _h(vs, 0, h // group),
                                          _h(dos, 0, h), w.scale, True, rows)
-            for x, tag in ((dq, "stored dS"), (dq2, "recomputed")):
+            for x, tag in ((dq, "recomputed"), (dq2, "stored dS")):
                 assert rel_l2(x[sl][rows, h], dq_ref) <= GRAD_REL, (s, h, tag)
 
 
@@ -196,25 +189,22 @@ def test_det16k_full_size_bit_identical_and_parity(name):
     rows = _rows(w.seqlen, extra=16, seed=7)
     cols = _rows(w.seqlen, extra=4, seed=8)
     _check_rows(o, lse, q, k, v, 0, 5, 5, w.scale, True, rows, name)
-    for fused, stored in ((0, 0), (1, 0), (0, 1)):
-        ea.set_tuning("bwd_fused_dq", fused)
-        ea.set_tuning("bwd_store_ds", stored)
-        try:
-            ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
-            runs = []
-            for _ in range(3):
-                runs.append(ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale,
-                                   deterministic=True, workspace=ws))
-                torch.cuda.synchronize()
-                assert ea.bwd_status(p, ws) == 0
-        finally:
-            ea.set_tuning("bwd_fused_dq", 0)
-            ea.set_tuning("bwd_store_ds", -1)
+    for design in (ea.BWD_RECOMPUTE, ea.BWD_FUSED_DQ, ea.BWD_STORED_DS):
+        opts = dict(bwd_design=design)
+        pd = ea.make_params(1, w.seqlen, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, w.scale,
+                            True, True, options=opts)
+        ws = torch.empty(ea.bwd_workspace_size(pd), dtype=torch.uint8, device=DEV)
+        runs = []
+        for _ in range(3):
+            runs.append(ea.bwd(q, k, v, o, do, lse, causal=True, softmax_scale=w.scale,
+                               deterministic=True, workspace=ws, options=opts))
+            torch.cuda.synchronize()
+            assert ea.bwd_status(pd, ws) == 0
         del ws
         for r in runs[1:]:
             for a, b in zip(runs[0], r):
-                assert torch.equal(a, b), (name, fused, stored)
+                assert torch.equal(a, b), (name, design)
         dq, dk, dv = runs[0]
-        what = f"{name} fused={fused} stored_ds={stored}"
+        what = f"{name} design={design}"
         _check_grads_sampled(dq, dk, dv, q, k, v, do, 0, 2, 1, w.scale, True, rows, cols, what)
         _identities(dk, dv, do, 1, what)

@@ -19,27 +19,26 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(params=[(1, 0, 0), (0, 0, 0), (1, 1, 0), (0, 0, 1)],
-                ids=["pingpong-splitdq", "plainfwd-splitdq", "pingpong-fuseddq", "plainfwd-storedds"])
+DESIGNS = {"recompute": dict(bwd_design=ea.BWD_RECOMPUTE),
+           "fused": dict(bwd_design=ea.BWD_FUSED_DQ),
+           "stored": dict(bwd_design=ea.BWD_STORED_DS)}
+
+
+@pytest.fixture(params=list(DESIGNS))
 def bwd_mode(request):
-    """Kernel designs under test: forward ping-pong on/off, backward with the
-    separate dQ kernel (recomputing S and dP, or from the dS the dK/dV kernel
-    stored; packed variable lengths always recompute) or with fused dQ atomics."""
-    pp, fused, ds = request.param
-    ea.set_tuning("fwd_pingpong", pp)
-    ea.set_tuning("bwd_fused_dq", fused)
-    ea.set_tuning("bwd_store_ds", ds)
-    yield request.param
-    ea.set_tuning("fwd_pingpong", 0)
-    ea.set_tuning("bwd_fused_dq", 0)
-    ea.set_tuning("bwd_store_ds", -1)
+    """Backward design under test, as per-call options: the dQ kernel
+    recomputing S and dP, the dQ kernel reading the dS the dK/dV kernel stored
+    (fixed and packed lengths), or dQ fused into the key-block kernel with
+    fp32 atomics (semaphore-ordered when deterministic)."""
+    return DESIGNS[request.param]
 
 
 def _dev(inp):
     return {k: v.to(DEV) for k, v in inp.items()}
 
 
-def _run_fixed(b, s, hq, hkv, d, causal, seed, scaled=False, det=False, sk=None, bwd=True):
+def _run_fixed(b, s, hq, hkv, d, causal, seed, scaled=False, det=False, sk=None, bwd=True,
+               opts=None):
     sk = s if sk is None else sk
     inp = make_inputs(b, s, sk, hq, hkv, d, seed=seed, scaled_heads=scaled)
     g = _dev(inp)
@@ -53,7 +52,7 @@ def _run_fixed(b, s, hq, hkv, d, causal, seed, scaled=False, det=False, sk=None,
     if not bwd:
         return
     dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=causal,
-                        softmax_scale=scale, deterministic=det)
+                        softmax_scale=scale, deterministic=det, options=opts)
     torch.cuda.synchronize()
     ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal)
     check_grads((dq, dk, dv), ref, what)
@@ -65,7 +64,7 @@ def test_small_workload_fwd_bwd(bwd_mode):
     g = _dev(inp)
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=False, softmax_scale=w.scale)
     dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=False,
-                        softmax_scale=w.scale)
+                        softmax_scale=w.scale, options=bwd_mode)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], w.scale, False)
     e = check_o(o, o_ref, "small")
@@ -78,12 +77,12 @@ def test_small_workload_fwd_bwd(bwd_mode):
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_lengths(d, causal, bwd_mode):
-    _run_fixed(1, 300, 2, 2, d, causal, seed=100 + d)
+    _run_fixed(1, 300, 2, 2, d, causal, seed=100 + d, opts=bwd_mode)
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (4, 1), (6, 3)])
 def test_grouped_heads(hq, hkv, bwd_mode):
-    _run_fixed(2, 200, hq, hkv, 128, True, seed=7 + hq + hkv)
+    _run_fixed(2, 200, hq, hkv, 128, True, seed=7 + hq + hkv, opts=bwd_mode)
 
 
 def test_non_causal_unequal_lengths():
@@ -92,8 +91,8 @@ def test_non_causal_unequal_lengths():
 
 def test_scaled_heads_exercise_rescale(bwd_mode):
     """Q, K x3 on half the heads: logit std ~9, max jumps above tau occur."""
-    _run_fixed(1, 1024, 4, 4, 128, True, seed=31, scaled=True)
-    _run_fixed(1, 700, 2, 2, 64, False, seed=32, scaled=True)
+    _run_fixed(1, 1024, 4, 4, 128, True, seed=31, scaled=True, opts=bwd_mode)
+    _run_fixed(1, 700, 2, 2, 64, False, seed=32, scaled=True, opts=bwd_mode)
 
 
 def test_lse_is_optional_and_output_unchanged():
@@ -117,7 +116,8 @@ def test_varlen_matches_oracle(causal, bwd_mode):
     o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], mx, mx,
                            causal=causal, softmax_scale=scale)
     dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
-                               g["cu_seqlens_k"], mx, mx, causal=causal, softmax_scale=scale)
+                               g["cu_seqlens_k"], mx, mx, causal=causal, softmax_scale=scale,
+                               options=bwd_mode)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal,
                                               inp["cu_seqlens_q"], inp["cu_seqlens_k"])
@@ -137,7 +137,8 @@ def test_varlen_non_causal_different_key_lengths(bwd_mode):
     o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], max(lq),
                            max(lk), causal=False, softmax_scale=scale)
     dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
-                               g["cu_seqlens_k"], max(lq), max(lk), softmax_scale=scale)
+                               g["cu_seqlens_k"], max(lq), max(lk), softmax_scale=scale,
+                               options=bwd_mode)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, False,
                                               inp["cu_seqlens_q"], inp["cu_seqlens_k"])
@@ -156,12 +157,13 @@ def test_deterministic_backward_is_bit_identical(d, bwd_mode):
     g = _dev(inp)
     scale = 1.0 / math.sqrt(d)
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=scale)
-    p = ea.make_params(1, s, s, hq, hkv, d, scale, True, True)
+    p = ea.make_params(1, s, s, hq, hkv, d, scale, True, True, options=bwd_mode)
     ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
     runs = []
     for _ in range(3):
         runs.append(ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True,
-                           softmax_scale=scale, deterministic=True, workspace=ws))
+                           softmax_scale=scale, deterministic=True, workspace=ws,
+                           options=bwd_mode))
         torch.cuda.synchronize()
         assert ea.bwd_status(p, ws) == 0
     for r in runs[1:]:
@@ -176,9 +178,10 @@ def test_backward_phases_equal_full_backward(bwd_mode):
     inp = make_inputs(1, s, s, hq, hkv, d, seed=61)
     g = _dev(inp)
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
-    p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True)
+    p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True, options=bwd_mode)
     ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
-    full = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True)
+    full = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
+                  options=bwd_mode)
     dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
     for ph in (ea.BWD_PREPROCESS, ea.BWD_MAIN, ea.BWD_DQ, ea.BWD_POSTPROCESS):
         ea.bwd_phases(p, ph, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
@@ -187,16 +190,12 @@ def test_backward_phases_equal_full_backward(bwd_mode):
         assert torch.equal(a, b)
 
 
-def test_forward_independent_of_tile_order(bwd_mode):
+def test_forward_independent_of_tile_order():
     """No cross-tile reduction in the forward: any tile order gives the same bits."""
     inp = make_inputs(2, 1024, 1024, 8, 8, 128, seed=71, with_grad=False)
     g = _dev(inp)
     o1, l1 = ea.fwd(g["q"], g["k"], g["v"], causal=True)
-    ea.set_tuning("tile_order", 1)
-    try:
-        o2, l2 = ea.fwd(g["q"], g["k"], g["v"], causal=True)
-    finally:
-        ea.set_tuning("tile_order", 0)
+    o2, l2 = ea.fwd(g["q"], g["k"], g["v"], causal=True, options=dict(tile_order=1))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
@@ -209,13 +208,8 @@ def test_tau_and_exp_emulation_variants_match_oracle(d, emu, tau):
     rescale and the polynomial change rounding, not the result."""
     inp = make_inputs(1, 700, 700, 2, 2, d, seed=81 + d, scaled_heads=True, with_grad=False)
     g = _dev(inp)
-    ea.set_tuning("exp_emulation", emu)
-    ea.set_tuning("tau", tau)
-    try:
-        o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
-    finally:
-        ea.set_tuning("exp_emulation", -1)
-        ea.set_tuning("tau", 8)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True,
+                    options=dict(exp_emulation=emu, tau=-1.0 if tau == 0 else float(tau)))
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], 1 / math.sqrt(d), True)
     e = check_o(o, o_ref, f"emu{emu} tau{tau} d{d}")
@@ -242,31 +236,28 @@ def test_deterministic_main_without_preprocess_stays_in_bounds():
     inp = make_inputs(1, s, s, hq, hkv, d, seed=111)
     g = _dev(inp)
     o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
-    p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True)
+    fused = dict(bwd_design=ea.BWD_FUSED_DQ)   # the ticket / semaphore path
+    p = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True, options=fused)
     ws = torch.empty(ea.bwd_workspace_size(p), dtype=torch.uint8, device=DEV)
-    ea.set_tuning("bwd_fused_dq", 1)       # the ticket / semaphore path
     first = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
-                   workspace=ws)
+                   workspace=ws, options=fused)
     dq, dk, dv = (torch.empty_like(x) for x in (g["q"], g["k"], g["v"]))
-    ea.set_tuning("spin_limit", 1 << 14)
-    try:
-        ea.bwd_phases(p, ea.BWD_PREPROCESS | ea.BWD_MAIN | ea.BWD_POSTPROCESS, g["q"], g["k"], g["v"], o, g["do"], lse,
-                      dq, dk, dv, ws)
-        ea.bwd_phases(p, ea.BWD_MAIN, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
-        torch.cuda.synchronize()
-    finally:
-        ea.set_tuning("spin_limit", 1 << 26)
-    again = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
-                   workspace=ws)
+    short = ea.make_params(1, s, s, hq, hkv, d, 1.0 / math.sqrt(d), True, True,
+                           options=dict(fused, spin_limit=1 << 14))
+    ea.bwd_phases(short, ea.BWD_PREPROCESS | ea.BWD_MAIN | ea.BWD_POSTPROCESS, g["q"], g["k"],
+                  g["v"], o, g["do"], lse, dq, dk, dv, ws)
+    ea.bwd_phases(short, ea.BWD_MAIN, g["q"], g["k"], g["v"], o, g["do"], lse, dq, dk, dv, ws)
     torch.cuda.synchronize()
-    ea.set_tuning("bwd_fused_dq", 0)
+    again = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, deterministic=True,
+                   workspace=ws, options=fused)
+    torch.cuda.synchronize()
     assert ea.bwd_status(p, ws) == 0
     for a, b in zip(first, again):
         assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("varlen", [False, True])
-def test_persistent_and_one_shot_launches_agree(varlen):
+def test_persistent_and_one_shot_launches_agree(varlen, bwd_mode):
     """Resident workgroups looping over tiles compute every tile exactly as a
     one-workgroup-per-tile grid does: same bits for O, LSE, dQ, dK, dV."""
     d = 128
@@ -276,24 +267,80 @@ def test_persistent_and_one_shot_launches_agree(varlen):
         inp = make_inputs(2, 3000, 3000, 8, 4, d, seed=122)
     g = _dev(inp)
 
-    def run():
+    def run(opts):
         if varlen:
             mx = 3000
             o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"],
-                                   mx, mx, causal=True)
+                                   mx, mx, causal=True, options=opts)
             grads = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
-                                  g["cu_seqlens_k"], mx, mx, causal=True)
+                                  g["cu_seqlens_k"], mx, mx, causal=True, options=opts)
         else:
-            o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True)
-            grads = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True)
+            o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, options=opts)
+            grads = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, options=opts)
         torch.cuda.synchronize()
         return (o, lse) + tuple(grads)
 
-    a = run()
-    ea.set_tuning("persistent", 0)
-    try:
-        b = run()
-    finally:
-        ea.set_tuning("persistent", 1)
-    for x, y in zip(a, b):
-        assert torch.equal(x, y)
+    a = run(bwd_mode)
+    b = run(dict(bwd_mode, one_shot_grid=1))
+    fused = bwd_mode["bwd_design"] == ea.BWD_FUSED_DQ
+    for i, (x, y) in enumerate(zip(a, b)):
+        if fused and i == 2:   # dQ of the fused design: unordered fp32 atomics
+            continue
+        assert torch.equal(x, y), i
+
+
+def test_designs_back_to_back_without_global_state():
+    """Designs are per-call options: interleaved calls with different designs on
+    the same inputs each meet the oracle bar, and the two split designs (same
+    dK/dV kernel arithmetic) give bit-equal dK, dV."""
+    s, hq, hkv, d = 700, 4, 2, 128
+    inp = make_inputs(1, s, s, hq, hkv, d, seed=131)
+    g = _dev(inp)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=scale)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True)
+    seq = [ea.BWD_RECOMPUTE, ea.BWD_STORED_DS, ea.BWD_FUSED_DQ, ea.BWD_RECOMPUTE, ea.BWD_STORED_DS]
+    out = [ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True, softmax_scale=scale,
+                  options=dict(bwd_design=b)) for b in seq]
+    torch.cuda.synchronize()
+    for b, r in zip(seq, out):
+        check_grads(r, ref, f"design {b}")
+    for a, b in ((0, 3), (1, 4), (0, 1)):
+        assert torch.equal(out[a][1], out[b][1]) and torch.equal(out[a][2], out[b][2])
+    assert torch.equal(out[0][0], out[3][0]) and torch.equal(out[1][0], out[4][0])
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (6, 2)])
+def test_stored_ds_lengths_beyond_declared_maximum_stay_in_the_workspace(hq, hkv):
+    """Packed lengths longer than the declared maxima (a caller error the
+    device cannot see before it runs): the stored-dS bound is computed from the
+    declared maxima, and every query head's stores must stay inside the
+    workspace. The workspace is a slice of a larger buffer filled with a
+    canary; the canary must survive. dK and dV do not depend on the stored dS
+    and must still meet the oracle bar."""
+    lengths = [512, 300, 700]
+    declared = 256
+    d = 128
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=141, lengths=lengths)
+    g = _dev(inp)
+    scale = 1.0 / math.sqrt(d)
+    mx = max(lengths)
+    o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], mx, mx,
+                           causal=True, softmax_scale=scale)
+    opts = dict(bwd_design=ea.BWD_STORED_DS)
+    p = ea.make_params(len(lengths), declared, declared, hq, hkv, d, scale, True, False,
+                       total_q=sum(lengths), total_k=sum(lengths), options=opts)
+    need = ea.bwd_workspace_size(p, varlen=True)
+    pad = 1 << 20
+    buf = torch.full((pad + need + pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = buf[pad:pad + need]
+    print(f"[canary] hq{hq} hkv{hkv} lengths {lengths} declared {declared} ws {need}", flush=True)
+    dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
+                               g["cu_seqlens_k"], declared, declared, causal=True,
+                               softmax_scale=scale, workspace=ws, options=opts)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 0xA5) and torch.all(buf[pad + need:] == 0xA5)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True,
+                                    inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    from parity import rel_l2
+    assert rel_l2(dk, ref[1]) <= 2e-2 and rel_l2(dv, ref[2]) <= 2e-2
