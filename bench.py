@@ -186,14 +186,19 @@ class Runner:
             draw_lengths(w.num_seqs, w.len_lo, w.len_hi, 71000 + w.number) if w.varlen else None)
         q, k = self.inp["q"], self.inp["k"]
         self.varlen = w.varlen
+        self.plan = None
         if w.varlen:
             self.cu_q = self.inp["cu_seqlens_q"].to(dev)
             self.cu_k = self.inp["cu_seqlens_k"].to(dev)
             mx = max(self.lengths)
             tq, hq, d = q.shape
+            # the schedule of the packed batch is computed once and cached
+            # (attn_varlen_plan_build) for every forward and backward call
+            self.plan = ea.varlen_plan(self.cu_q, self.cu_k, mx, mx, tq, k.shape[0], w.heads_q,
+                                       w.heads_kv, d, w.causal)
             self.p = ea.make_params(w.num_seqs, mx, mx, w.heads_q, w.heads_kv, d, w.scale,
                                     w.causal, w.deterministic, total_q=tq, total_k=k.shape[0],
-                                    options=opts)
+                                    options=opts, plan=self.plan)
             self.lse = torch.empty((hq, tq), dtype=torch.float32, device=dev)
         else:
             self.cu_q = self.cu_k = None
@@ -211,6 +216,28 @@ class Runner:
         if self.with_bwd:
             self.bws = torch.empty(max(1, self.bws_bytes), dtype=torch.uint8, device=dev)
             self.dq, self.dk, self.dv = (torch.empty_like(self.inp[n]) for n in ("q", "k", "v"))
+        self.check_device_buffers()
+
+    def check_device_buffers(self):
+        """Every pointer this runner hands to the C ABI is device memory of the
+        current GPU, contiguous, of the dtype the call expects (raw ctypes calls
+        skip the binding's own checks)."""
+        torch = self.torch
+        dev = torch.device("cuda", torch.cuda.current_device())
+        want = {"q": torch.bfloat16, "k": torch.bfloat16, "v": torch.bfloat16, "o": torch.bfloat16,
+                "lse": torch.float32, "fws": torch.uint8}
+        bufs = {"q": self.inp["q"], "k": self.inp["k"], "v": self.inp["v"], "o": self.o,
+                "lse": self.lse, "fws": self.fws}
+        if self.varlen:
+            bufs.update(cu_q=self.cu_q, cu_k=self.cu_k, plan=self.plan.buf)
+            want.update(cu_q=torch.int32, cu_k=torch.int32, plan=torch.uint8)
+        if self.with_bwd:
+            bufs.update(do=self.inp["do"], bws=self.bws, dq=self.dq, dk=self.dk, dv=self.dv)
+            want.update(do=torch.bfloat16, bws=torch.uint8, dq=torch.bfloat16, dk=torch.bfloat16,
+                        dv=torch.bfloat16)
+        for n, t in bufs.items():
+            assert t.device == dev, f"{n} is on {t.device}, not {dev}"
+            assert t.is_contiguous() and t.dtype == want[n], (n, t.dtype, t.is_contiguous())
 
     def stream(self):
         return self.torch.cuda.current_stream().cuda_stream
@@ -315,6 +342,7 @@ def measure(torch, ea, w, args, opts, cpu_budget: float) -> dict:
     total = fl["fwd+bwd"] if r.with_bwd else fl["fwd"]
     fwd_t = fl["fwd"] / (kms["fwd"] * 1e-3) / 1e12
     rec = {"workload": describe(w), "pass": w.passes, "ms_per_step": round(ms, 4),
+           "varlen_plan": r.plan is not None,
            "tflops": round(total / (ms * 1e-3) / 1e12, 2),
            "fwd": {"ms": round(kms["fwd"], 4), "tflops": round(fwd_t, 1), "frac": frac(fwd_t)},
            "workspace_bytes": {"fwd": r.fws_bytes, "bwd": r.bws_bytes}}
@@ -371,7 +399,7 @@ def ablations(torch, ea, args) -> dict:
     # scheduling section; digest page item 5)
     for tag, hkv in (("mha", 16), ("mqa", 1)):
         w = Workload(f"lpt_{tag}", 3, 2, 16, hkv, 8192, 128, True, "fwd+bwd")
-        inp = make_inputs(2, 8192, 8192, 16, hkv, 128, seed=71003)
+        inp = make_inputs(2, 8192, 8192, 16, hkv, 128, seed=71003, device="cuda:0")
         fl = workload_flops(w)
         res = {}
         for name, opts in (("lpt", {}), ("natural", {"tile_order": 1})):

@@ -52,13 +52,32 @@ class AttnOptions(ctypes.Structure):
                 ("ds_budget", ctypes.c_int64)]
 
 
+class AttnVarlenPlan(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
+                ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
+                ("seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int32),
+                ("total_k", ctypes.c_int32), ("num_heads_q", ctypes.c_int32),
+                ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("causal", ctypes.c_int32)]
+
+
 class AttnParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
                 ("seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int32),
                 ("total_k", ctypes.c_int32), ("num_heads_q", ctypes.c_int32),
                 ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("deterministic", ctypes.c_int32), ("opt", AttnOptions)]
+                ("deterministic", ctypes.c_int32), ("opt", AttnOptions),
+                ("varlen_plan", ctypes.POINTER(AttnVarlenPlan))]
+
+
+class VarlenPlan:
+    """A built varlen plan: the C struct plus the torch buffer that holds its
+    tables (kept alive here)."""
+
+    def __init__(self, struct: AttnVarlenPlan, buf: torch.Tensor):
+        self.struct = struct
+        self.buf = buf
 
 
 _LIB = None
@@ -68,7 +87,8 @@ _vp = ctypes.c_void_p
 EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
-           "attn_persistent_tile", "attn_bwd_design"]
+           "attn_persistent_tile", "attn_bwd_design",
+           "attn_bwd_ds_subtile", "attn_varlen_plan_size", "attn_varlen_plan_build"]
 
 
 def _lib():
@@ -95,9 +115,16 @@ def _lib():
     lib.attn_persistent_tile.argtypes = [ctypes.c_int32] * 5
     lib.attn_persistent_tile.restype = ctypes.c_int32
     lib.attn_bwd_design.argtypes = [_P, ctypes.c_int32]
+    lib.attn_varlen_plan_size.argtypes = [_P]
+    lib.attn_varlen_plan_size.restype = ctypes.c_size_t
+    lib.attn_varlen_plan_build.argtypes = [_P, _vp, _vp, _vp, ctypes.c_size_t,
+                                           ctypes.POINTER(AttnVarlenPlan), _vp]
+    lib.attn_bwd_ds_subtile.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int64)]
+    lib.attn_bwd_ds_subtile.restype = ctypes.c_int64
     for n in EXPORTS:
         if n not in ("attn_status_string", "attn_version", "attn_fwd_workspace_size",
-                     "attn_bwd_workspace_size"):
+                     "attn_bwd_workspace_size", "attn_bwd_ds_subtile", "attn_varlen_plan_size"):
             getattr(lib, n).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -142,10 +169,32 @@ def make_options(options: Optional[dict] = None) -> AttnOptions:
 
 def make_params(batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, scale, causal,
                 deterministic=False, total_q=0, total_k=0,
-                options: Optional[dict] = None) -> AttnParams:
-    return AttnParams(int(batch), int(seqlen_q), int(seqlen_k), int(total_q), int(total_k),
-                      int(heads_q), int(heads_kv), int(head_dim), float(scale), int(bool(causal)),
-                      int(bool(deterministic)), make_options(options))
+                options: Optional[dict] = None, plan: Optional["VarlenPlan"] = None) -> AttnParams:
+    p = AttnParams(int(batch), int(seqlen_q), int(seqlen_k), int(total_q), int(total_k),
+                   int(heads_q), int(heads_kv), int(head_dim), float(scale), int(bool(causal)),
+                   int(bool(deterministic)), make_options(options))
+    if plan is not None:
+        p.varlen_plan = ctypes.pointer(plan.struct)
+    return p
+
+
+def varlen_plan(cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                total_q: int, total_k: int, heads_q: int, heads_kv: int, head_dim: int,
+                causal: bool) -> VarlenPlan:
+    """attn_varlen_plan_build: the schedule of one packed batch, computed once
+    on the current stream for every later varlen call with these parameters."""
+    _expect(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _expect(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    nseq = cu_seqlens_q.numel() - 1
+    p = make_params(nseq, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, head_dim, 1.0, causal,
+                    total_q=total_q, total_k=total_k)
+    n = _lib().attn_varlen_plan_size(ctypes.byref(p))
+    buf = _workspace(n, cu_seqlens_q.device)
+    st = AttnVarlenPlan()
+    _check(_lib().attn_varlen_plan_build(ctypes.byref(p), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                         _ptr(buf), buf.numel(), ctypes.byref(st), _stream()),
+           "attn_varlen_plan_build")
+    return VarlenPlan(st, buf)
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
@@ -192,8 +241,8 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                causal: bool = False, softmax_scale: Optional[float] = None,
-               return_lse: bool = True,
-               options: Optional[dict] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               return_lse: bool = True, options: Optional[dict] = None,
+               plan: Optional[VarlenPlan] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_seqlens int32 [n+1] -> (o, lse [Hq, Tq])."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _expect(t, n)
@@ -204,7 +253,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
     nseq = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     p = make_params(nseq, max_seqlen_q, max_seqlen_k, hq, hkv, d, scale, causal, total_q=tq,
-                    total_k=tk, options=options)
+                    total_k=tk, options=options, plan=plan)
     o = torch.empty_like(q)
     lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device) if return_lse else None
     ws = _workspace(fwd_workspace_size(p, True), q.device)
@@ -237,7 +286,7 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float
 def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                max_seqlen_k: int, causal: bool = False, softmax_scale: Optional[float] = None,
                deterministic: bool = False, workspace: Optional[torch.Tensor] = None,
-               options: Optional[dict] = None):
+               options: Optional[dict] = None, plan: Optional[VarlenPlan] = None):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _expect(t, n)
     _expect(lse, "lse", torch.float32)
@@ -248,7 +297,7 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
     nseq = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     p = make_params(nseq, max_seqlen_q, max_seqlen_k, hq, hkv, d, scale, causal, deterministic,
-                    total_q=tq, total_k=tk, options=options)
+                    total_q=tq, total_k=tk, options=options, plan=plan)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = workspace if workspace is not None else _workspace(bwd_workspace_size(p, True), q.device)
     _check(_lib().attn_bwd_varlen(ctypes.byref(p), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
@@ -283,6 +332,14 @@ def tile_order(p: AttnParams, which: int):
     _check(lib.attn_tile_order(ctypes.byref(p), which, buf, count.value, ctypes.byref(count)),
            "attn_tile_order")
     return [tuple(buf[3 * i:3 * i + 3]) for i in range(count.value)]
+
+
+def ds_subtile(p: AttnParams, row32: int, col32: int):
+    """(index of the stored-dS sub-tile (row32, col32) in a (sequence, head)
+    region or -1, sub-tiles in the region), host evaluation."""
+    n = ctypes.c_int64(0)
+    i = _lib().attn_bwd_ds_subtile(ctypes.byref(p), int(row32), int(col32), ctypes.byref(n))
+    return int(i), int(n.value)
 
 
 def persistent_tile(g: int, r: int, grid: int, ntiles: int, nx: int = 8) -> int:

@@ -86,27 +86,57 @@ int64_t rows_q_of(const attn_params* p, bool varlen) {
 }
 
 // ------------------------------------------------------------ workspace maps
+// Varlen schedule tables of one kernel (see SchedSet): offsets in a buffer.
+enum SetKind { kSetFwd = 0, kSetDkdv = 1, kSetFused = 2, kSetDq = 3, kSetDqDs = 4, kNumSets = 5 };
+struct SetMap {
+  size_t order = 0, tile_prefix = 0, mb_prefix = 0, ds_prefix = 0, queue = 0;
+  bool mb = false, ds = false;
+};
+size_t map_set(size_t off, int64_t nseq, int kind, SetMap* m) {
+  m->mb = kind == kSetDkdv || kind == kSetFused;
+  m->ds = kind == kSetDkdv;
+  m->order = off; off = align_up(off + sizeof(int) * (size_t)nseq);
+  m->tile_prefix = off; off = align_up(off + sizeof(int) * ((size_t)nseq + 1));
+  if (m->mb) { m->mb_prefix = off; off = align_up(off + sizeof(int) * ((size_t)nseq + 1)); }
+  if (m->ds) { m->ds_prefix = off; off = align_up(off + sizeof(int64_t) * ((size_t)nseq + 1)); }
+  m->queue = off; off = align_up(off + sizeof(unsigned));
+  return off;
+}
+
 struct FwdWs {
-  size_t order = 0, tile_prefix = 0, queue = 0, total = 0;
+  SetMap set;
+  size_t total = 0;
 };
 FwdWs fwd_ws(const attn_params* p, bool varlen) {
   FwdWs w;
-  if (!varlen) return w;
-  size_t off = 0;
-  w.order = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
-  w.tile_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
-  w.queue = off; off = align_up(off + sizeof(unsigned));
-  w.total = off;
+  if (varlen && !p->varlen_plan) w.total = map_set(0, p->batch, kSetFwd, &w.set);
   return w;
 }
 
+// A varlen plan: the tables of all five kernels.
+struct PlanMap {
+  SetMap set[kNumSets];
+  size_t total = 0;
+};
+PlanMap plan_map(const attn_params* p) {
+  PlanMap m;
+  size_t off = 0;
+  for (int k = 0; k < kNumSets; ++k) off = map_set(off, p->batch, k, &m.set[k]);
+  m.total = off;
+  return m;
+}
+
 struct BwdWs {
-  size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, order = 0, tile_prefix = 0, mb_prefix = 0;
-  size_t order_dq = 0, tile_prefix_dq = 0, ds = 0, ds_prefix = 0;
+  size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, ds = 0;
+  SetMap main, dq;        // varlen tables of the key-block and dQ kernels (no plan)
+  bool tables = false;
   size_t total = 0;
   int64_t n_sem = 0;
   int design = ATTN_BWD_RECOMPUTE;
 };
+// schedule-table kinds of a backward design
+int main_kind(int design) { return design == ATTN_BWD_FUSED_DQ ? kSetFused : kSetDkdv; }
+int dq_kind(int design) { return design == ATTN_BWD_STORED_DS ? kSetDqDs : kSetDq; }
 // Bytes of the stored-dS area: fixed length, B * Hq regions of the visible
 // sub-tiles (DsGeom); packed lengths, a bound from the totals and the longest
 // key length, 2 (ceil(total_q / 64) + batch) sub-rows of at most
@@ -127,7 +157,8 @@ int64_t ds_area_bytes(const attn_params* p, bool varlen) {
 int bwd_design_of(const attn_params* p, bool varlen) {
   const Opts o = opts_of(p);
   if (o.bwd_design == ATTN_BWD_FUSED_DQ || o.bwd_design == ATTN_BWD_RECOMPUTE) return o.bwd_design;
-  const bool fits = ds_area_bytes(p, varlen) <= o.ds_budget;
+  const bool fits = ds_area_bytes(p, varlen) <= o.ds_budget &&
+                    ds_geom(p->seqlen_q, p->seqlen_k, p->causal != 0).rows < kDsMaxRows;
   if (o.bwd_design == ATTN_BWD_STORED_DS) return fits ? ATTN_BWD_STORED_DS : -1;
   return (p->head_dim >= 128 && fits) ? ATTN_BWD_STORED_DS : ATTN_BWD_RECOMPUTE;
 }
@@ -153,18 +184,12 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
   w.n_sem = fused && p->deterministic ? bwd_mblocks(p, varlen) * p->num_heads_q : 0;
   w.sem = off; off = align_up(off + sizeof(int) * (size_t)w.n_sem);
   w.misc = off; off = align_up(off + 64);
-  if (varlen) {
-    w.order = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
-    w.tile_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
-    w.mb_prefix = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
-    w.order_dq = off; off = align_up(off + sizeof(int) * (size_t)p->batch);
-    w.tile_prefix_dq = off; off = align_up(off + sizeof(int) * ((size_t)p->batch + 1));
+  if (varlen && !p->varlen_plan && w.design > 0) {
+    w.tables = true;
+    off = map_set(off, p->batch, main_kind(w.design), &w.main);
+    if (!fused) off = map_set(off, p->batch, dq_kind(w.design), &w.dq);
   }
   if (w.design == ATTN_BWD_STORED_DS) {
-    if (varlen) {
-      w.ds_prefix = off;
-      off = align_up(off + sizeof(int64_t) * ((size_t)p->batch + 1));
-    }
     w.ds = off;
     off = align_up(off + (size_t)ds_area_bytes(p, varlen));
   }
@@ -235,6 +260,48 @@ SeqView make_sv(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k) 
   return sv;
 }
 
+// Schedule-table descriptor of one kernel's varlen tables at `m` in `base`.
+// Query-block kernels (forward, dQ) sort the sequences by key length and
+// count query blocks; key-block kernels sort by query length and count key
+// blocks.
+SchedSet make_set(const attn_params* p, int kind, const int32_t* cu_q, const int32_t* cu_k,
+                  char* base, const SetMap& m) {
+  SchedSet s;
+  std::memset(&s, 0, sizeof(s));
+  const int d = p->head_dim;
+  const bool qblocks = kind == kSetFwd || kind == kSetDq || kind == kSetDqDs;
+  s.key_cu = qblocks ? cu_k : cu_q;
+  s.count_cu = qblocks ? cu_q : cu_k;
+  s.heads = qblocks ? p->num_heads_q : p->num_heads_kv;
+  s.blk = kind == kSetFwd ? fwd_block_m(d)
+        : kind == kSetDkdv ? dkdv_block_n(d)
+        : kind == kSetFused ? bwd_block_n(d)
+        : kind == kSetDq ? dq_block_m(d) : DqDsCfg<128>::BM;
+  s.order = reinterpret_cast<int*>(base + m.order);
+  s.tile_prefix = reinterpret_cast<int*>(base + m.tile_prefix);
+  s.mb_prefix = m.mb ? reinterpret_cast<int*>(base + m.mb_prefix) : nullptr;
+  s.mb_blk = bwd_block_m(d);
+  s.queue = reinterpret_cast<unsigned*>(base + m.queue);
+  s.ds_prefix = m.ds ? reinterpret_cast<int64_t*>(base + m.ds_prefix) : nullptr;
+  s.ds_heads = p->num_heads_q;
+  s.causal = p->causal;
+  s.ds_tiles = ds_area_bytes(p, true) / 2048;
+  return s;
+}
+
+// A plan passed with the parameters must have been built for them.
+attn_status check_plan(const attn_params* p, bool varlen) {
+  const attn_varlen_plan* pl = p->varlen_plan;
+  if (!pl) return ATTN_OK;
+  if (!varlen || !pl->data || pl->bytes < plan_map(p).total) return ATTN_ERR_INVALID_ARGUMENT;
+  if (pl->batch != p->batch || pl->seqlen_q != p->seqlen_q || pl->seqlen_k != p->seqlen_k ||
+      pl->total_q != p->total_q || pl->total_k != p->total_k ||
+      pl->num_heads_q != p->num_heads_q || pl->num_heads_kv != p->num_heads_kv ||
+      pl->head_dim != p->head_dim || pl->causal != p->causal)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  return ATTN_OK;
+}
+
 attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
                      const void* q, const void* k, const void* v, void* o, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -245,6 +312,8 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARGUMENT;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARGUMENT;
+  st = check_plan(p, varlen);
+  if (st != ATTN_OK) return st;
   const FwdWs wl = fwd_ws(p, varlen);
   if (ws_bytes < wl.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (wl.total && !ws) return ATTN_ERR_INVALID_ARGUMENT;
@@ -271,16 +340,22 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   fp.tau = op.tau;
   const int pcus = launch_cus(op.persistent);
   if (varlen) {
-    char* base = static_cast<char*>(ws);
-    int* order = reinterpret_cast<int*>(base + wl.order);
-    int* tp = reinterpret_cast<int*>(base + wl.tile_prefix);
-    unsigned* queue = pcus ? reinterpret_cast<unsigned*>(base + wl.queue) : nullptr;
-    if (launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bm, order, tp, nullptr,
-                               1, queue, nullptr, 0, 0, stream) != hipSuccess)
-      return ATTN_ERR_HIP;
-    fp.order = order;
-    fp.tile_prefix = tp;
-    fp.queue = queue;
+    // the tables from a plan, or from a schedule pass into the workspace
+    char* tb = static_cast<char*>(p->varlen_plan ? p->varlen_plan->data : ws);
+    const SetMap m = p->varlen_plan ? plan_map(p).set[kSetFwd] : wl.set;
+    const SchedSet s = make_set(p, kSetFwd, cu_q, cu_k, tb, m);
+    if (!p->varlen_plan) {
+      SchedArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.q_cu = cu_q;
+      a.nseq = p->batch;
+      a.nsets = 1;
+      a.set[0] = s;
+      if (launch_varlen_schedule(a, stream) != hipSuccess) return ATTN_ERR_HIP;
+    }
+    fp.order = s.order;
+    fp.tile_prefix = s.tile_prefix;
+    fp.queue = pcus ? s.queue : nullptr;
   }
   // the FMA-path exp2 issues from the same VALU port as v_exp_f32 here, and
   // with the hand-scheduled forward step every share E > 0 measured slower at
@@ -290,15 +365,18 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   return ATTN_OK;
 }
 
+// launch = false: validate only (no HIP call at all).
 attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int phases,
                      const void* q, const void* k, const void* v, const void* o, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool launch = true) {
   const bool varlen = cu_q != nullptr;
   attn_status st = check_params(p, varlen);
   if (st != ATTN_OK) return st;
   if (varlen && !cu_k) return ATTN_ERR_INVALID_ARGUMENT;
   if (phases <= 0 || phases > ATTN_BWD_ALL) return ATTN_ERR_INVALID_ARGUMENT;
+  st = check_plan(p, varlen);
+  if (st != ATTN_OK) return st;
   const BwdWs wl = bwd_ws(p, varlen);
   if (wl.design < 0) return ATTN_ERR_UNSUPPORTED;   // stored dS requested over the budget
   const bool fused_mode = wl.design == ATTN_BWD_FUSED_DQ;
@@ -314,7 +392,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   if ((post || dqk) && (!dq || !aligned16(dq))) return ATTN_ERR_INVALID_ARGUMENT;
   if (ws_bytes < wl.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!ws) return ATTN_ERR_INVALID_ARGUMENT;
-  if (p->batch == 0) return ATTN_OK;
+  if (p->batch == 0 || !launch) return ATTN_OK;
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -356,40 +434,45 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   if (use_ds) {
     bp.ds = base + wl.ds;
     bp.ds_bytes = static_cast<int64_t>(wl.total - wl.ds);
-    bp.ds_prefix = varlen ? reinterpret_cast<const int64_t*>(base + wl.ds_prefix) : nullptr;
+
     bp.ntiles_dq = varlen ? (cdiv(p->total_q, bmq) + p->batch) * p->num_heads_q
                           : p->batch * p->num_heads_q * bp.nm_dq;
   }
   bp.sec_dq = section_width(2ll * p->seqlen_k * d * 2);
-  if (varlen) {
-    bp.order = reinterpret_cast<int*>(base + wl.order);
-    bp.tile_prefix = reinterpret_cast<int*>(base + wl.tile_prefix);
-    bp.mb_prefix = reinterpret_cast<int*>(base + wl.mb_prefix);
-    bp.order_dq = reinterpret_cast<int*>(base + wl.order_dq);
-    bp.tile_prefix_dq = reinterpret_cast<int*>(base + wl.tile_prefix_dq);
-  }
   // Packed sequences of very different lengths make tiles too unequal for a
   // static walk (measured 19 % slower dK/dV on 16 sequences of 512..8192):
   // there the persistent workgroups draw tiles from device counters, which
   // the varlen schedule pass clears.
   const int pcus = launch_cus(op.persistent);
-  if (varlen && pcus) {
-    bp.queue = reinterpret_cast<unsigned*>(base + wl.misc + 8);
-    bp.queue_dq = reinterpret_cast<unsigned*>(base + wl.misc + 12);
+  SchedArgs sched;
+  std::memset(&sched, 0, sizeof(sched));
+  if (varlen) {
+    // the tables from a plan, or from the schedule pass of PREPROCESS into the
+    // workspace (one launch for the key-block and the dQ kernel's tables)
+    char* tb = p->varlen_plan ? static_cast<char*>(p->varlen_plan->data) : base;
+    const PlanMap pm = p->varlen_plan ? plan_map(p) : PlanMap();
+    const SetMap mm = p->varlen_plan ? pm.set[main_kind(wl.design)] : wl.main;
+    const SetMap dm = p->varlen_plan ? pm.set[dq_kind(wl.design)] : wl.dq;
+    sched.q_cu = cu_q;
+    sched.nseq = p->batch;
+    sched.set[sched.nsets++] = make_set(p, main_kind(wl.design), cu_q, cu_k, tb, mm);
+    if (!fused) sched.set[sched.nsets++] = make_set(p, dq_kind(wl.design), cu_q, cu_k, tb, dm);
+    const SchedSet& ms = sched.set[0];
+    bp.order = ms.order;
+    bp.tile_prefix = ms.tile_prefix;
+    bp.mb_prefix = ms.mb_prefix;
+    bp.queue = pcus ? ms.queue : nullptr;
+    if (use_ds) bp.ds_prefix = ms.ds_prefix;
+    if (!fused) {
+      const SchedSet& qs = sched.set[1];
+      bp.order_dq = qs.order;
+      bp.tile_prefix_dq = qs.tile_prefix;
+      bp.queue_dq = pcus ? qs.queue : nullptr;
+    }
+    if (p->varlen_plan) sched.nsets = 0;   // computed when the plan was built
   }
   if (pre) {
-    if (varlen && launch_varlen_schedule(cu_q, cu_k, cu_q, p->batch, p->num_heads_kv, bn,
-                                         const_cast<int*>(bp.order),
-                                         const_cast<int*>(bp.tile_prefix),
-                                         const_cast<int*>(bp.mb_prefix), bm, bp.queue,
-                                         const_cast<int64_t*>(bp.ds_prefix), p->num_heads_q,
-                                         p->causal, stream) != hipSuccess)
-      return ATTN_ERR_HIP;
-    if (varlen && !fused &&
-        launch_varlen_schedule(cu_k, cu_q, cu_q, p->batch, p->num_heads_q, bmq,
-                               const_cast<int*>(bp.order_dq), const_cast<int*>(bp.tile_prefix_dq),
-                               nullptr, 1, bp.queue_dq, nullptr, 0, 0, stream) != hipSuccess)
-      return ATTN_ERR_HIP;
+    if (varlen && launch_varlen_schedule(sched, stream) != hipSuccess) return ATTN_ERR_HIP;
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (main) {
@@ -432,6 +515,42 @@ size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen) {
   if (check_params(p, varlen != 0) != ATTN_OK) return (size_t)-1;
   const BwdWs w = bwd_ws(p, varlen != 0);
   return w.design < 0 ? (size_t)-1 : w.total;
+}
+
+size_t attn_varlen_plan_size(const attn_params* p) {
+  if (check_params(p, true) != ATTN_OK) return (size_t)-1;
+  return plan_map(p).total;
+}
+
+attn_status attn_varlen_plan_build(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
+                                   void* data, size_t bytes, attn_varlen_plan* plan,
+                                   hipStream_t stream) {
+  attn_status st = check_params(p, true);
+  if (st != ATTN_OK) return st;
+  if (!cu_q || !cu_k || !data || !plan) return ATTN_ERR_INVALID_ARGUMENT;
+  const PlanMap m = plan_map(p);
+  if (bytes < m.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  plan->data = data;
+  plan->bytes = bytes;
+  plan->batch = p->batch;
+  plan->seqlen_q = p->seqlen_q;
+  plan->seqlen_k = p->seqlen_k;
+  plan->total_q = p->total_q;
+  plan->total_k = p->total_k;
+  plan->num_heads_q = p->num_heads_q;
+  plan->num_heads_kv = p->num_heads_kv;
+  plan->head_dim = p->head_dim;
+  plan->causal = p->causal;
+  if (p->batch == 0) return ATTN_OK;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  SchedArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_cu = cu_q;
+  a.nseq = p->batch;
+  for (int k = 0; k < kNumSets; ++k)
+    a.set[a.nsets++] = make_set(p, k, cu_q, cu_k, static_cast<char*>(data), m.set[k]);
+  return launch_varlen_schedule(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int32_t attn_bwd_design(const attn_params* p, int32_t varlen) {
@@ -521,6 +640,14 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
     }
   }
   return ATTN_OK;
+}
+
+int64_t attn_bwd_ds_subtile(const attn_params* p, int32_t row32, int32_t col32,
+                            int64_t* region_tiles) {
+  if (check_params(p, false) != ATTN_OK) return -1;
+  const DsGeom g = ds_geom(p->seqlen_q, p->seqlen_k, p->causal != 0);
+  if (region_tiles) *region_tiles = ds_region_tiles(g);
+  return ds_subtile(g, row32, col32);
 }
 
 int32_t attn_persistent_tile(int32_t g, int32_t r, int32_t grid, int32_t ntiles, int32_t nx) {

@@ -125,38 +125,31 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   const int kvh0 = kvh * p.group;
   int i_h = 0;
   // Stored dS (DS): sub-tiles of 32 queries x 32 keys per (sequence, query
-  // head), 2 KiB each, row by row (DsGeom: a sub-row holds the sub-tiles of
-  // the key blocks that reach its group): two 1 KiB fragments (16-row halves
-  // tt of the sub-tile), each the 64 lanes' packed B operands of dK^T in lane
-  // order, except that lanes 32..63 swap 64-byte halves (slot L ^ 4), which
-  // makes the dQ kernel's transposing reads conflict-free. The compute
-  // cursor's NQB sub-rows start at byte ds_off of the area (ds_w bytes each);
-  // the regions of the group's heads follow each other (ds_reg bytes each).
-  // Packed lengths clamp every store range to the area (ds_rng_of).
-  DsGeom dsg{};
-  int64_t ds_off = 0, ds_head = 0, ds_reg = 0, ds_rs0 = 0;
-  int ds_w = 0, ds_w0 = 0, ds_r = 0, ds_r0 = 0;
+  // head), 2 KiB each, key-block major (DsGeom: this tile's keys lie in one
+  // 256-key block, whose column holds 16 KiB per 32-query sub-row from its
+  // first written row on): two 1 KiB fragments (16-row halves tt of the
+  // sub-tile), each the 64 lanes' packed B operands of dK^T in lane order,
+  // except that lanes 32..63 swap 64-byte halves (slot L ^ 4), which makes
+  // the dQ kernel's transposing reads conflict-free. The column of the
+  // compute cursor's head starts at ds_col (ds_rng bytes; 0 for a packed
+  // sequence whose regions did not fit the area, which drops its stores);
+  // its step's sub-rows at byte ds_soff of it. The regions of the group's
+  // heads follow each other (ds_reg bytes each).
+  const char* ds_col = nullptr;
+  int64_t ds_reg = 0;
+  int ds_rng = 0, ds_soff = 0, ds_soff0 = 0, ds_sub = 0;
   if constexpr (DS) {
-    dsg = ds_geom(lq, lk, causal);
-    ds_r0 = __builtin_amdgcn_readfirstlane(m_first * BM / 32);
+    const DsGeom dsg = ds_geom(lq, lk, causal);
+    const int blk = n0 >> 8, r0 = ds_r0(dsg, blk);
     ds_reg = uniform64(ds_region_tiles(dsg) * 2048);
-    ds_rs0 = uniform64(ds_row_start(dsg, ds_r0) * 2048);
-    ds_w0 = __builtin_amdgcn_readfirstlane(ds_width(dsg, ds_r0) * 2048);
-    const int64_t first = p.ds_prefix ? p.ds_prefix[t.seq] * 2048
-                                      : (int64_t)t.seq * p.hq * ds_reg;
-    ds_head = keep_sgpr(uniform64(first + (int64_t)kvh0 * ds_reg));
-    ds_off = keep_sgpr(ds_head + ds_rs0);
-    ds_w = ds_w0;
-    ds_r = ds_r0;
+    ds_soff0 = __builtin_amdgcn_readfirstlane((m_first * BM / 32 - r0) * 16384);
+    ds_sub = ((n0 & 255) >> 5) * 2048;   // this workgroup's first sub-column in the block
+    const int64_t first = p.ds_prefix ? p.ds_prefix[t.seq] : (int64_t)t.seq * p.hq * ds_region_tiles(dsg);
+    ds_rng = first < 0 ? 0 : __builtin_amdgcn_readfirstlane((dsg.rows - r0) * 16384);
+    ds_col = keep_sgpr(p.ds + uniform64(first < 0 ? 0 : first * 2048 + (int64_t)kvh0 * ds_reg +
+                                                       ds_col_start(dsg, blk) * 2048));
+    ds_soff = ds_soff0;
   }
-  // end of the dS area for the clamp (fixed length: sized exactly, no clamp)
-  int64_t ds_end = 0;
-  if constexpr (DS) ds_end = keep_sgpr(uniform64(p.ds_prefix ? p.ds_bytes : (int64_t)1 << 62));
-  auto ds_rng_of = [&]() -> int {   // bytes of this step's sub-rows inside the area
-    const int64_t room = ds_end - ds_off;
-    const int n = NQB * ds_w;
-    return room <= 0 ? 0 : (room < n ? static_cast<int>(room) : n);
-  };
   const int64_t q_tile = (qs * qstride + (int64_t)kvh0 * D) * 2;
   const char* const q_seq = keep_sgpr(static_cast<const char*>(p.q) + q_tile);
   const char* const do_seq = keep_sgpr(static_cast<const char*>(p.dout) + q_tile);
@@ -401,15 +394,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (DS) {
           if (db == NDB - 1) {   // last read of sb[qb][*][tt]: store it (waited for a step later)
-            const rsrc_t dr = raw_rsrc(p.ds + ds_off, ds_rng_of());
-            const int so = (wk0 >> 5) * 2048;
+            const rsrc_t dr = raw_rsrc(ds_col, ds_rng);
+            const int so = ds_soff + ds_sub + (KPW >> 5) * w * 2048;
             // lane offset recomputed here from an opaque lane id: kept live
             // across the step it costs a VGPR
             const int ln = opaque_lane_id();
             const int ds_voff = (ln ^ ((ln >> 5) << 2)) << 4;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-              buf_store16_nt(dr, ds_voff, so + qb * ds_w + kb * 2048 + tt * 1024, sb[qb][kb][tt]);
+              buf_store16_nt(dr, ds_voff, so + qb * 16384 + kb * 2048 + tt * 1024, sb[qb][kb][tt]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -448,15 +441,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     step_body(mq0, need_mask, f0, f1, has_next, iss, nxt);
     if constexpr (DS) {   // the compute cursor's next sub-rows
       if (wrap) {
-        ds_head = keep_sgpr(ds_head + ds_reg);
-        ds_off = keep_sgpr(ds_head + ds_rs0);
-        ds_w = ds_w0;
-        ds_r = ds_r0;
+        ds_col = keep_sgpr(ds_col + ds_reg);
+        ds_soff = ds_soff0;
       } else {
-        ds_off = keep_sgpr(ds_off + (int64_t)NQB * ds_w);
-        ds_r += NQB;
-        if ((ds_r & 7) == 0)
-          ds_w = __builtin_amdgcn_readfirstlane(8 * 2048 * ds_group_blocks(dsg, ds_r >> 3));
+        ds_soff += NQB * 16384;
       }
     }
     advance_slot(st);

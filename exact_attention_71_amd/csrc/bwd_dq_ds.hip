@@ -93,13 +93,21 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
     const int r = slot / SPR, pos = slot % SPR;
     voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
   }
-  // ---- this wave's dS: sub-row qw0 / 32 of the head's region (DsGeom),
-  // NKB sub-tiles (contiguous, 2 KiB each) per key tile. Reads past the row's
-  // range give zero; a wave whose rows all lie past the sequence skips its
-  // MFMAs.
-  int ds_rng;
-  const int64_t ds_off = ds_rows_at(p, ds_geom(lq, lk, causal), t.seq, h, qw0 >> 5, 1, &ds_rng);
-  const rsrc_t dsr = raw_rsrc(p.ds + ds_off, ds_rng);
+  // ---- this wave's dS: sub-row qw0 / 32 of the head's region (DsGeom,
+  // key-block major), NKB sub-tiles (contiguous, 2 KiB each) per key tile.
+  // Each 256-key block's column starts at its own base; key tiles are issued
+  // in order, so a cursor (block ds_cb, its first sub-tile ds_cs) walks the
+  // columns. Reads of sub-rows the block never stored (above its first
+  // written row: sub-tiles no row of this wave sees), of rows past the
+  // sequence, and of a packed sequence whose regions did not fit give zero.
+  const DsGeom dsg = ds_geom(lq, lk, causal);
+  const int ds_r = qw0 >> 5;
+  const int64_t ds_first = p.ds_prefix ? p.ds_prefix[t.seq]
+                                       : (int64_t)t.seq * p.hq * ds_region_tiles(dsg);
+  const bool ds_ok = ds_first >= 0 && ds_r < dsg.rows;
+  const int64_t ds_head = ds_ok ? ds_first + (int64_t)h * ds_region_tiles(dsg) : 0;
+  int ds_cb = 0;
+  int64_t ds_cs = 0;
   const int ds_row = lane * 16;
   auto issue_k = [&](int n) {
     const int64_t t0 = (int64_t)n * BN * kstride;
@@ -108,11 +116,20 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
 #pragma unroll
     for (int i = 0; i < CH; ++i) dma16(kr, lds_k + st * TILE + (i * NW + w) * 1024, voffs[i]);
   };
-  auto issue_ds = [&](int n) {
+  auto issue_ds = [&](int n) {   // n = the previous call's n + 1 (or 0 first)
     const int sd = n % NSD;
+    const int k0 = n * NKB, b = k0 >> 3;
+    while (ds_cb < b) {
+      ds_cs += 8ll * (dsg.rows - ds_r0(dsg, ds_cb));
+      ++ds_cb;
+    }
+    const int r0 = ds_r0(dsg, b);
+    const bool live = ds_ok && ds_r >= r0;
+    const int64_t base = live ? (ds_head + ds_cs + 8ll * (ds_r - r0)) * 2048 : 0;
+    const rsrc_t dsr = raw_rsrc(p.ds + uniform64(base), __builtin_amdgcn_readfirstlane(live ? 16384 : 0));
 #pragma unroll
     for (int i = 0; i < CD; ++i)
-      dma16_nt(dsr, lds_s + (sd * NW + w) * DSW + i * 1024, ds_row + n * NKB * 2048 + i * 1024);
+      dma16_nt(dsr, lds_s + (sd * NW + w) * DSW + i * 1024, ds_row + (k0 & 7) * 2048 + i * 1024);
   };
 
   // K^T by transposing reads (see bwd_dq.hip): 16-lane group (g, dh), lane

@@ -86,83 +86,72 @@ struct BwdParams {
   // kernel writes (DsGeom below); the regions of the heads of a sequence follow
   // each other, sequences in order.
   char* ds;
-  const int64_t* ds_prefix;  // varlen: first sub-tile of each sequence (null: fixed length)
-  int64_t ds_bytes;          // size of the dS area (every range is clamped to it)
+  const int64_t* ds_prefix;  // varlen: first sub-tile of each sequence, -1 for a
+                             // sequence whose regions do not fit the area (its
+                             // stores are dropped); null: fixed length
+  int64_t ds_bytes;          // size of the dS area
 };
 
-// Stored-dS geometry of one (sequence, query head) with lq queries and lk
-// keys. Sub-row r holds queries 32r .. 32r+31 (rows = 2 ceil(lq / 64): whole
-// dK/dV steps of up to 64 queries); it stores sub-columns 0 .. width(r) - 1,
-// 32 keys each. Widths are whole key blocks of 256 keys (the dK/dV workgroup)
-// and constant over groups of 8 sub-rows (256 queries): group G stores the
-// key blocks that reach into it, all kb of them without a causal mask, and
-// blocks [0, G + c) with c = 1 + ceil((lk - lq) / 256) under the bottom-right
-// causal diagonal (key block n writes the rows from its first visible one on,
-// and 256 n - (lk - lq) >= 256 (G + 1) keeps it out of group G). A row's
-// sub-tiles are contiguous; rows follow each other.
+// Stored-dS layout of one (sequence, query head) with lq queries and lk
+// keys, key-block major. Sub-tiles are 32 queries x 32 keys of bf16 (2 KiB).
+// The keys form kb = ceil(lk / 256) blocks of 256 (8 sub-columns: the dK/dV
+// workgroup, or two of them at head_dim 256); block n keeps the sub-rows
+// r0(n) .. rows - 1 (rows = 2 ceil(lq / 64): whole dK/dV steps of up to 64
+// queries), 16 KiB per sub-row with its 8 sub-tiles in column order, and the
+// blocks follow each other. r0(n) is where the dK/dV kernel's first step for
+// the block begins: 0 without a causal mask; under the bottom-right diagonal
+// (query i sees key j iff j <= i + lk - lq) the first 64-query step that sees
+// key 256 n, r0(n) = min(rows, 2 max(0, 4n + f)) with f = floor((lq - lk) / 64).
+// The dK/dV kernel then advances by a constant 16 KiB per step; the dQ
+// kernel, which reads one sub-row across the blocks, moves to a new column
+// base every 8 sub-tiles.
+// A key-block column of 16 KiB per sub-row is addressed with 32-bit offsets.
+constexpr int kDsMaxRows = (1 << 17) - 1;   // sub-rows: queries < 4194240
 struct DsGeom {
-  int rows;       // stored sub-rows
-  int kb;         // key blocks of 256 keys
-  int c;          // causal: group G holds min(max(G + c, 0), kb) blocks
+  int rows;       // sub-rows of a block that starts at row 0
+  int kb;         // key blocks
+  int f;          // causal: r0(n) = min(rows, 2 max(0, 4n + f))
   int causal;
-  int64_t p0;     // causal: ds_psum(max(c, 0))
 };
 
-__host__ __device__ inline int64_t ds_clampi(int64_t a, int64_t lo, int64_t hi) {
-  return a < lo ? lo : (a > hi ? hi : a);
-}
-// sum over a = 0 .. n-1 of min(a, kb) (n >= 0)
-__host__ __device__ inline int64_t ds_psum(int64_t n, int64_t kb) {
-  const int64_t n1 = n < kb + 1 ? n : kb + 1;
-  return n1 * (n1 - 1) / 2 + (n - n1) * kb;
+__host__ __device__ inline int64_t ds_floordiv(int64_t a, int64_t b) {
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
 }
 __host__ __device__ inline DsGeom ds_geom(int lq, int lk, bool causal) {
   DsGeom g;
   g.rows = (lq + 63) / 64 * 2;
   g.kb = (lk + 255) / 256;
+  g.f = (int)ds_floordiv((int64_t)lq - lk, 64);
   g.causal = causal ? 1 : 0;
-  const int shift = lk - lq;
-  // ceil(shift / 256) for either sign
-  const int cdv = shift >= 0 ? (shift + 255) / 256 : -((-shift) / 256);
-  g.c = 1 + cdv;
-  g.p0 = causal ? ds_psum(g.c > 0 ? g.c : 0, g.kb) : 0;
   return g;
 }
-// key blocks (of 256) stored for the rows of group G
-__host__ __device__ inline int ds_group_blocks(const DsGeom& g, int G) {
-  return g.causal ? (int)ds_clampi((int64_t)G + g.c, 0, g.kb) : g.kb;
+// first stored sub-row of key block n
+__host__ __device__ inline int ds_r0(const DsGeom& g, int n) {
+  if (!g.causal) return 0;
+  const int64_t a = 4ll * n + g.f;
+  const int64_t r = a > 0 ? 2 * a : 0;
+  return (int)(r < g.rows ? r : g.rows);
 }
-// sub-tiles stored in sub-row r
-__host__ __device__ inline int ds_width(const DsGeom& g, int r) { return 8 * ds_group_blocks(g, r >> 3); }
-// sub-tiles stored before sub-row r (0 <= r <= rows)
-__host__ __device__ inline int64_t ds_row_start(const DsGeom& g, int r) {
-  if (!g.causal) return (int64_t)r * 8 * g.kb;
-  const int G = r >> 3;
-  const int64_t a = (int64_t)G + g.c;
-  const int64_t full = ds_psum(a > 0 ? a : 0, g.kb) - g.p0;   // blocks of groups 0 .. G-1
-  return 64 * full + (int64_t)(r - 8 * G) * 8 * ds_group_blocks(g, G);
+// sub-tiles of blocks 0 .. n-1 (0 <= n <= kb): 8 sum_j (rows - r0(j)). Under
+// the causal mask r0(j) is 0 for j < j1 (4j + f <= 0), 8j + 2f for
+// j1 <= j < j2 and rows from j2 on (8j + 2f >= rows).
+__host__ __device__ inline int64_t ds_col_start(const DsGeom& g, int n) {
+  if (!g.causal) return 8ll * n * g.rows;
+  const int64_t j1 = ds_floordiv(-(int64_t)g.f, 4) + 1 > 0 ? ds_floordiv(-(int64_t)g.f, 4) + 1 : 0;
+  int64_t j2 = ds_floordiv((int64_t)g.rows - 2ll * g.f + 7, 8);
+  if (j2 < j1) j2 = j1;
+  const int64_t a = j1 < n ? j1 : n, b = j2 < n ? j2 : n;
+  int64_t r0sum = 8 * (b * (b - 1) / 2 - a * (a - 1) / 2) + 2ll * g.f * (b - a);
+  if (n > j2) r0sum += (int64_t)g.rows * (n - j2);
+  return 8 * ((int64_t)n * g.rows - r0sum);
 }
 // sub-tiles of the whole region
-__host__ __device__ inline int64_t ds_region_tiles(const DsGeom& g) { return ds_row_start(g, g.rows); }
-
-// Byte offset from p.ds of sub-row r of the region of (sequence s, query head
-// h) and, in *range, the bytes of the nr rows from there that lie inside the
-// dS area (a region past the area, from packed lengths beyond the maximum the
-// caller declared, gets range 0: its stores are dropped and its reads give
-// zero). Rows past the region get range 0 too. Wave-uniform.
-__device__ inline int64_t ds_rows_at(const BwdParams& p, const DsGeom& g, int s, int h, int r,
-                                     int nr, int* range) {
-  const int64_t reg = ds_region_tiles(g);
-  const int64_t first = p.ds_prefix ? p.ds_prefix[s] : (int64_t)s * p.hq * reg;
-  const int64_t off = (first + (int64_t)h * reg + ds_row_start(g, r)) * 2048;
-  int64_t n = r < g.rows ? (ds_row_start(g, r + nr < g.rows ? r + nr : g.rows) - ds_row_start(g, r)) * 2048 : 0;
-  const int64_t room = p.ds_bytes - off;
-  if (n > room) n = room;
-  *range = __builtin_amdgcn_readfirstlane(n <= 0 ? 0 : static_cast<int>(n > 0x7fffffffLL ? 0x7fffffffLL : n));
-  const int64_t o = n <= 0 ? 0 : off;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(o));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(o >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+__host__ __device__ inline int64_t ds_region_tiles(const DsGeom& g) { return ds_col_start(g, g.kb); }
+// sub-tile index of (sub-row r, sub-column k) in the region, -1 if not stored
+__host__ __device__ inline int64_t ds_subtile(const DsGeom& g, int r, int k) {
+  const int n = k >> 3;
+  if (r < 0 || k < 0 || n >= g.kb || r >= g.rows || r < ds_r0(g, n)) return -1;
+  return ds_col_start(g, n) + 8ll * (r - ds_r0(g, n)) + (k & 7);
 }
 
 // Tile sizes (rows of the query block and keys of the key block) per head dim.
@@ -244,17 +233,35 @@ hipError_t launch_bwd_dq(const BwdParams& p, int d, int cus, hipStream_t stream)
 // dQ = alpha dS K from the dS the dK/dV kernel stored (p.ds; see bwd_dq_ds.hip).
 hipError_t launch_bwd_dq_ds(const BwdParams& p, int d, int cus, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdParams& p, int d, hipStream_t stream);
-// Varlen pre-pass: order[] = sequences by decreasing length of key_cu (ties
-// by index), tile_prefix[vs] = first tile of virtual sequence vs with
-// cdiv(len of count_cu, blk) * heads tiles each, and (optional) mb_prefix[s]
-// = first query block of actual sequence s with cdiv(len of q_cu, mb_blk);
-// clears *queue (optional) for the tile tickets of the launch that follows.
-// Optional ds_prefix[s] = first stored-dS sub-tile of sequence s (lengths
-// from q_cu and count_cu, ds_heads query heads each; see DsGeom).
-hipError_t launch_varlen_schedule(const int* key_cu, const int* count_cu, const int* q_cu,
-                                  int nseq, int heads, int blk, int* order, int* tile_prefix,
-                                  int* mb_prefix, int mb_blk, unsigned* queue,
-                                  int64_t* ds_prefix, int ds_heads, int causal,
-                                  hipStream_t stream);
+// Varlen pre-pass tables. One set: order[] = sequences by decreasing length
+// of key_cu (ties by index), tile_prefix[vs] = first tile of virtual sequence
+// vs with cdiv(len of count_cu, blk) * heads tiles each; optional
+// mb_prefix[s] = first query block of actual sequence s with
+// cdiv(len of q_cu, mb_blk); optional ds_prefix[s] = first stored-dS
+// sub-tile of sequence s (lengths from q_cu and count_cu, ds_heads query
+// heads each; see DsGeom), or -1 when its regions would end past ds_tiles
+// sub-tiles; clears *queue (optional) for the tile tickets of the launches
+// that follow.
+struct SchedSet {
+  const int* key_cu;
+  const int* count_cu;
+  int heads, blk;
+  int* order;
+  int* tile_prefix;
+  int* mb_prefix;
+  int mb_blk;
+  unsigned* queue;
+  int64_t* ds_prefix;
+  int ds_heads, causal;
+  int64_t ds_tiles;
+};
+constexpr int kMaxSchedSets = 5;
+struct SchedArgs {
+  const int* q_cu;
+  int nseq, nsets;
+  SchedSet set[kMaxSchedSets];
+};
+// One launch (a single workgroup) computes every set of `a`.
+hipError_t launch_varlen_schedule(const SchedArgs& a, hipStream_t stream);
 
 }  // namespace attn71

@@ -122,6 +122,25 @@ typedef struct attn_options {
 
 #define ATTN_DS_BUDGET_DEFAULT (4ll << 30)
 
+/* A varlen plan: the schedule tables of one packed batch (the order of the
+ * sequences longest first, tile and block prefix sums, stored-dS offsets,
+ * tile-ticket counters) for every kernel, built once by
+ * attn_varlen_plan_build and reused by any number of attn_fwd_varlen /
+ * attn_bwd_varlen / attn_bwd_phases calls on the same sequences (blog page,
+ * scheduling section: the metadata can be cached, so the sort costs
+ * nothing). The caller owns `data` (attn_varlen_plan_size bytes of device
+ * memory). The fields below `bytes` record the parameters the plan was built
+ * for; a call whose parameters differ in any of them is rejected
+ * (ATTN_ERR_INVALID_ARGUMENT). The cu_seqlens contents cannot be checked:
+ * a plan is valid for the cu_seqlens values it was built from. Calls that
+ * use one plan must not overlap in time (they share its tile counters). */
+typedef struct attn_varlen_plan {
+  void* data;
+  size_t bytes;
+  int32_t batch, seqlen_q, seqlen_k, total_q, total_k, num_heads_q, num_heads_kv, head_dim,
+      causal;
+} attn_varlen_plan;
+
 typedef struct attn_params {
   int32_t batch;         /* fixed: B. varlen: number of packed sequences */
   int32_t seqlen_q;      /* fixed: Sq. varlen: max query length (upper bound) */
@@ -139,6 +158,8 @@ typedef struct attn_params {
                             once and are bit-identical either way; the fused
                             design orders its dQ additions when set */
   attn_options opt;      /* per-call design and tuning options (zero: defaults) */
+  const attn_varlen_plan* varlen_plan; /* varlen calls: the cached schedule (NULL: each
+                                          call computes it in its workspace) */
 } attn_params;
 
 /* "OK", "invalid argument", ... ; never NULL. */
@@ -170,6 +191,21 @@ size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen);
  * every sequence's key length; sequences beyond it drop stores rather than
  * write past the workspace). */
 int32_t attn_bwd_design(const attn_params* p, int32_t varlen);
+
+/* Bytes of device memory a varlen plan for these parameters needs (they
+ * depend on the sequence count only); (size_t)-1 for parameters the varlen
+ * calls would reject. */
+size_t attn_varlen_plan_size(const attn_params* p);
+
+/* Builds a varlen plan for the packed batch described by p and the device
+ * arrays cu_seqlens_q / cu_seqlens_k (as for attn_fwd_varlen): fills *plan
+ * (host) and enqueues one schedule kernel on `stream` that writes the tables
+ * into `data` (`bytes` >= attn_varlen_plan_size). Calls that then pass the
+ * plan in attn_params.varlen_plan launch no schedule pass of their own, and
+ * their workspaces hold no tables (the workspace sizes drop accordingly). */
+attn_status attn_varlen_plan_build(const attn_params* p, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, void* data, size_t bytes,
+                                   attn_varlen_plan* plan, hipStream_t stream);
 
 /* Forward, fixed length. lse may be NULL (the LSE is optional on the pages:
  * blog page, correction-warpgroup list, "optionally compute and store LSE"). */
@@ -242,6 +278,17 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* wo
  * No GPU is needed. */
 attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,
                             int64_t* count);
+
+/* Stored-dS layout, evaluated on the host with the kernels' arithmetic: the
+ * index of the 32 x 32 sub-tile (sub-row row32 = queries 32 row32 ..,
+ * sub-column col32 = keys 32 col32 ..) inside the region of one (sequence,
+ * query head) with p->seqlen_q queries and p->seqlen_k keys (p->causal), or
+ * -1 when the layout keeps no such sub-tile. The region holds
+ * *region_tiles sub-tiles (2 KiB each). Key-block major: each 256-key block
+ * keeps the sub-rows from the first one its dK/dV step writes, 8 sub-tiles
+ * per sub-row. No GPU is needed. */
+int64_t attn_bwd_ds_subtile(const attn_params* p, int32_t row32, int32_t col32,
+                            int64_t* region_tiles);
 
 /* Persistent launches (forward, dK/dV and dQ kernels): `grid` workgroups, as
  * many as fit on the device at once, loop over the `ntiles` positions of the

@@ -339,35 +339,98 @@ def _dq_reads(lq, lk, d, causal):
     return out
 
 
-def _ds_width(lq, lk, causal, r):
-    kb = -(-lk // 256)
-    if not causal:
-        return 8 * kb
-    shift = lk - lq
-    c = 1 + (-(-shift // 256))
-    return 8 * min(max(r // 8 + c, 0), kb)
-
-
 @pytest.mark.parametrize("lq,lk", [(300, 300), (8192, 8192), (1000, 1000), (64, 64), (1, 1),
                                    (256, 257), (700, 300), (300, 700), (17, 4096), (4096, 17),
-                                   (513, 1024), (1024, 513), (2000, 2000 + 255), (33, 33)])
+                                   (513, 1024), (1024, 513), (2000, 2000 + 255), (33, 33),
+                                   (5000, 4000), (4000, 5000), (640, 7000)])
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_stored_ds_layout_holds_every_write_and_read(lq, lk, d, causal):
-    """The visible-only layout (rows of whole 256-key blocks, widths constant
-    over 256-query groups) holds every sub-tile the dK/dV kernel writes, the
-    dQ kernel reads only written sub-tiles, and the library's area for B x Hq
-    regions equals the brute-force sum of the row widths."""
+    """The key-block-major layout (evaluated by the library on the host) gives
+    every sub-tile the dK/dV kernel writes its own index inside the region,
+    the dQ kernel reads only written sub-tiles, each key block's stored rows
+    are contiguous (16 KiB per sub-row, so the dK/dV kernel advances by a
+    constant per step), and the library's area for B x Hq regions equals the
+    region size."""
     writes = _dkdv_writes(lq, lk, d, causal)
     reads = _dq_reads(lq, lk, d, causal)
-    rows = -(-lq // 64) * 2
     assert reads <= writes
-    for r, k in writes:
-        assert r < rows and k < _ds_width(lq, lk, causal, r), (r, k)
-    region = sum(_ds_width(lq, lk, causal, r) for r in range(rows))
-    kw = dict(batch=2, seqlen_q=lq, seqlen_k=lk, heads_q=3, heads_kv=1, head_dim=d, causal=causal)
-    area = (ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=2, ds_budget=1 << 40)))
-            - ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=1))))
-    assert 2 * 3 * region * 2048 <= area < 2 * 3 * region * 2048 + 256
-    if causal and d == 128 and lq == lk and lq % 256 == 0:
-        assert len(writes) == region       # tight: nothing stored that is not written
+    p = _p(batch=2, seqlen_q=lq, seqlen_k=lk, heads_q=3, heads_kv=1, head_dim=d, causal=causal)
+    idx = {}
+    region = None
+    for r, k in sorted(writes):
+        i, region = ea.ds_subtile(p, r, k)
+        assert 0 <= i < region, (r, k, i, region)
+        idx[(r, k)] = i
+    assert len(set(idx.values())) == len(idx)               # one slot per written sub-tile
+    # contiguity: within a key block, sub-row r + 1 sits 8 sub-tiles after r
+    for (r, k), i in idx.items():
+        if (r + 1, k) in idx:
+            assert idx[(r + 1, k)] == i + 8
+    # unstored neighbours of the written set return -1
+    rows = -(-lq // 64) * 2
+    for r, k in list(writes)[:50]:
+        assert ea.ds_subtile(p, rows, k)[0] == -1 and ea.ds_subtile(p, r, -1)[0] == -1
+    if writes:
+        kw = dict(batch=2, seqlen_q=lq, seqlen_k=lk, heads_q=3, heads_kv=1, head_dim=d,
+                  causal=causal)
+        area = (ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=2, ds_budget=1 << 40)))
+                - ea.bwd_workspace_size(_p(**kw, options=dict(bwd_design=1))))
+        assert 2 * 3 * region * 2048 <= area < 2 * 3 * region * 2048 + 256
+        # the region is exactly the written set, rounded to whole 256-key
+        # blocks and to the 64-query rows of the longest dK/dV step
+        blocks = {}
+        for r, k in writes:
+            blocks.setdefault(k // 8, set()).add(r)
+        want = sum(8 * (rows - min(rs) // 2 * 2) for rs in blocks.values())
+        assert region == want
+
+
+def test_varlen_plan_validation():
+    """Plans are sized by the sequence count alone, shrink the varlen
+    workspaces (no tables there), and a call whose parameters differ from the
+    plan's in any recorded field is rejected before anything is enqueued."""
+    lib = ea.load()
+    kw = dict(batch=5, seqlen_q=700, seqlen_k=700, heads_q=4, heads_kv=2, head_dim=128,
+              causal=True, total_q=2000, total_k=2000)
+    p = _p(**kw)
+    n = lib.attn_varlen_plan_size(ctypes.byref(p))
+    assert 0 < n < 1 << 16
+    assert lib.attn_varlen_plan_size(ctypes.byref(_p(**dict(kw, batch=50)))) > n
+    plan = ea.AttnVarlenPlan()
+    # argument checks (no GPU needed): null cu, null data, small buffer
+    assert lib.attn_varlen_plan_build(ctypes.byref(p), None, FAKE, FAKE, n, ctypes.byref(plan),
+                                      None) == INVALID
+    assert lib.attn_varlen_plan_build(ctypes.byref(p), FAKE, FAKE, None, n, ctypes.byref(plan),
+                                      None) == INVALID
+    assert lib.attn_varlen_plan_build(ctypes.byref(p), FAKE, FAKE, FAKE, n - 1,
+                                      ctypes.byref(plan), None) == WS_SMALL
+    # a plan as the builder fills it (zero sequences: filled without a launch)
+    p0 = _p(**dict(kw, batch=0))
+    plan0 = ea.AttnVarlenPlan()
+    assert lib.attn_varlen_plan_build(ctypes.byref(p0), FAKE, FAKE, FAKE, 1 << 20,
+                                      ctypes.byref(plan0), None) == 0
+    assert (plan0.batch, plan0.num_heads_q, plan0.head_dim, plan0.causal) == (0, 4, 128, 1)
+    # a plan built for p: fields as recorded
+    good = ea.AttnVarlenPlan(FAKE, n, 5, 700, 700, 2000, 2000, 4, 2, 128, 1)
+    pp = _p(**kw)
+    pp.varlen_plan = ctypes.pointer(good)
+    assert ea.fwd_workspace_size(pp, True) == 0
+    assert ea.bwd_workspace_size(pp, True) < ea.bwd_workspace_size(p, True)
+    # a valid plan passes validation (the call then fails on the null q)
+    assert lib.attn_fwd_varlen(ctypes.byref(pp), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None,
+                               0, None) == INVALID
+    for field, val in (("batch", 4), ("seqlen_k", 701), ("total_q", 1999), ("num_heads_q", 8),
+                       ("num_heads_kv", 1), ("head_dim", 64), ("causal", 0), ("bytes", n - 1)):
+        bad = ea.AttnVarlenPlan(FAKE, n, 5, 700, 700, 2000, 2000, 4, 2, 128, 1)
+        setattr(bad, field, val)
+        q = _p(**kw)
+        q.varlen_plan = ctypes.pointer(bad)
+        args = [FAKE] * 7 + [None, FAKE, 1 << 20, None]
+        assert lib.attn_fwd_varlen(ctypes.byref(q), *args) == INVALID, field
+        bargs = [FAKE] * 11 + [FAKE, 1 << 30, None]
+        assert lib.attn_bwd_varlen(ctypes.byref(q), *bargs) == INVALID, field
+    # a plan on a fixed-length call
+    f = _p(batch=5, seqlen_q=700, seqlen_k=700, heads_q=4, heads_kv=2, head_dim=128, causal=True)
+    f.varlen_plan = ctypes.pointer(good)
+    assert lib.attn_fwd(ctypes.byref(f), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID

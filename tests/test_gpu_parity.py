@@ -344,3 +344,35 @@ def test_stored_ds_lengths_beyond_declared_maximum_stay_in_the_workspace(hq, hkv
                                     inp["cu_seqlens_q"], inp["cu_seqlens_k"])
     from parity import rel_l2
     assert rel_l2(dk, ref[1]) <= 2e-2 and rel_l2(dv, ref[2]) <= 2e-2
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_plan_gives_the_same_bits(causal, bwd_mode):
+    """A cached varlen plan (one schedule launch, reused by every call) gives
+    the bits of the calls that compute their own schedule, over three reuses
+    of the plan (its tile counters stay valid across launches); deterministic
+    mode so that every design's dQ is bitwise comparable."""
+    lengths = [3000, 17, 1200, 640, 2500, 1, 0, 777]
+    hq, hkv, d = 4, 2, 128
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=151, lengths=lengths)
+    g = _dev(inp)
+    mx = max(lengths)
+    cq, ck = g["cu_seqlens_q"], g["cu_seqlens_k"]
+    plan = ea.varlen_plan(cq, ck, mx, mx, sum(lengths), sum(lengths), hq, hkv, d, causal)
+
+    def run(pl):
+        o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], cq, ck, mx, mx, causal=causal, plan=pl)
+        grads = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, cq, ck, mx, mx,
+                              causal=causal, deterministic=True, options=bwd_mode, plan=pl)
+        torch.cuda.synchronize()
+        return (o, lse) + tuple(grads)
+
+    ref = run(None)
+    for _ in range(3):
+        got = run(plan)
+        for i, (x, y) in enumerate(zip(ref, got)):
+            assert torch.equal(x, y), i
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], 1 / math.sqrt(d),
+                                              causal, inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    check_o(got[0], o_ref, "plan")
+    check_lse(got[1], lse_ref, "plan")
