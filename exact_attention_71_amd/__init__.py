@@ -87,7 +87,7 @@ _vp = ctypes.c_void_p
 EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
-           "attn_persistent_tile", "attn_bwd_design",
+           "attn_persistent_tile", "attn_bwd_design", "attn_bwd_noalloc",
            "attn_bwd_ds_subtile", "attn_varlen_plan_size", "attn_varlen_plan_build"]
 
 
@@ -107,6 +107,7 @@ def _lib():
     lib.attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.attn_fwd_varlen.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.attn_bwd.argtypes = [_P] + [_vp] * 10 + [ctypes.c_size_t, _vp]
+    lib.attn_bwd_noalloc.argtypes = [_P] + [_vp] * 10
     lib.attn_bwd_varlen.argtypes = [_P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
     lib.attn_bwd_phases.argtypes = [_P, _vp, _vp, ctypes.c_int32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
     lib.attn_bwd_status.argtypes = [_P, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_int32), _vp]
@@ -280,6 +281,25 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float
     _check(_lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                            _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                            _stream()), "attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float] = None,
+                deterministic: bool = False, options: Optional[dict] = None):
+    """attn_bwd_noalloc: the recomputing backward on the library's static device
+    scratch (no workspace; the C call allocates nothing; dq, dk, dv are
+    allocated here by torch)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _expect(t, n)
+    _expect(lse, "lse", torch.float32)
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    p = make_params(b, sq, sk, hq, hkv, d, scale, causal, deterministic, options=options)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(_lib().attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                   _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _stream()),
+           "attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -489,6 +489,34 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   return ATTN_OK;
 }
 
+// ------------------------------------------------ allocation-free backward
+// Device scratch of attn_bwd_noalloc, for callers that cannot allocate
+// (graph capture, serving loops, harnesses that forbid allocation): the
+// recomputing backward's workspace (-D and LSE log2 e per (row, query head),
+// the ticket / status words) lives in this static array, which every GPU the
+// library runs on holds until the process ends. In host code the name is a
+// stand-in, not a device address: kernels and copies use the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch.
+__device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];
+
+attn_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (dev < 0 || dev >= 64) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ATTN_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -575,6 +603,28 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
                      void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
   return bwd_impl(p, nullptr, nullptr, ATTN_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, ws,
                   ws_bytes, stream);
+}
+
+attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse, void* dq,
+                             void* dk, void* dv, hipStream_t stream) {
+  attn_status st = check_params(p, false);
+  if (st != ATTN_OK) return st;
+  if (p->opt.bwd_design != ATTN_BWD_AUTO && p->opt.bwd_design != ATTN_BWD_RECOMPUTE)
+    return ATTN_ERR_UNSUPPORTED;
+  attn_params pr = *p;
+  pr.opt.bwd_design = ATTN_BWD_RECOMPUTE;
+  if (bwd_ws(&pr, false).total > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_UNSUPPORTED;
+  // every argument is checked before the first HIP call (the scratch lookup)
+  void* const placeholder = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  st = bwd_impl(&pr, nullptr, nullptr, ATTN_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, placeholder,
+                ATTN_NOALLOC_SCRATCH_BYTES, stream, /*launch=*/false);
+  if (st != ATTN_OK || p->batch == 0) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != ATTN_OK) return st;
+  return bwd_impl(&pr, nullptr, nullptr, ATTN_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, ws,
+                  ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,

@@ -229,6 +229,26 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Backward, fixed length, allocating nothing: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments and results as attn_bwd
+ * with the recomputing design (opt.bwd_design must be ATTN_BWD_AUTO or
+ * ATTN_BWD_RECOMPUTE, else ATTN_ERR_UNSUPPORTED), but no workspace argument:
+ * the workspace lives in a library-owned static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES, which each GPU the library runs on holds until
+ * the process ends. Calls whose workspace (attn_bwd_workspace_size with the
+ * recomputing design: 8 bytes per (query row, query head) plus a few
+ * hundred) exceeds it return ATTN_ERR_UNSUPPORTED before launching
+ * anything. The first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress); no call allocates or frees memory. All calls
+ * on one GPU share its array, and each call rewrites what it needs, so calls
+ * that overlap in time on one GPU (other streams, other host threads) race:
+ * serialize them. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32ll << 20)
+attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse, void* dq,
+                             void* dk, void* dv, hipStream_t stream);
+
 /* Backward, packed variable length (same conventions as attn_fwd_varlen). */
 attn_status attn_bwd_varlen(const attn_params* p, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_k, const void* q, const void* k,
