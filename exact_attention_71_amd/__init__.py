@@ -68,7 +68,12 @@ class AttnParams(ctypes.Structure):
                 ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
                 ("deterministic", ctypes.c_int32), ("opt", AttnOptions),
-                ("varlen_plan", ctypes.POINTER(AttnVarlenPlan))]
+                ("varlen_plan", ctypes.POINTER(AttnVarlenPlan)),
+                ("block_mask", ctypes.c_void_p), ("block_mask_stride_b", ctypes.c_int64),
+                ("block_mask_stride_h", ctypes.c_int64)]
+
+
+MASK_BLOCK = 128   # queries and keys per block-mask entry
 
 
 class VarlenPlan:
@@ -179,6 +184,38 @@ def make_params(batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, scale, c
     return p
 
 
+def prepare_block_mask(mask: Optional[torch.Tensor], batch: int, heads_q: int, seqlen_q: int,
+                       seqlen_k: int) -> Optional[torch.Tensor]:
+    """A block mask as the library reads it: uint8 (bool accepted), shape
+    [batch or 1, heads_q or 1, ceil(seqlen_q / 128), ceil(seqlen_k / 128)],
+    contiguous and 4-byte aligned on the GPU (copied if needed)."""
+    if mask is None:
+        return None
+    nqb, nkb = -(-seqlen_q // MASK_BLOCK), -(-seqlen_k // MASK_BLOCK)
+    if mask.dim() != 4 or tuple(mask.shape[2:]) != (nqb, nkb) or \
+            mask.shape[0] not in (1, batch) or mask.shape[1] not in (1, heads_q):
+        raise ValueError(f"block mask must be [{batch} or 1, {heads_q} or 1, {nqb}, {nkb}], "
+                         f"got {tuple(mask.shape)}")
+    if not mask.is_cuda:
+        raise ValueError("block mask must be on the GPU")
+    # the library reads whole 4-byte words: a 4-byte aligned buffer padded to a
+    # multiple of 4 bytes
+    m = mask.to(torch.uint8).contiguous()
+    n = m.numel()
+    buf = torch.zeros((n + 3) // 4 * 4, dtype=torch.uint8, device=m.device)
+    buf[:n].copy_(m.reshape(-1))
+    return buf[:n].view(m.shape)
+
+
+def set_block_mask(p: AttnParams, m: Optional[torch.Tensor]) -> None:
+    """Point the parameters at a prepared block mask (size-1 dims broadcast)."""
+    if m is None:
+        return
+    p.block_mask = m.data_ptr()
+    p.block_mask_stride_b = m.stride(0) if m.shape[0] > 1 else 0
+    p.block_mask_stride_h = m.stride(1) if m.shape[1] > 1 else 0
+
+
 def varlen_plan(cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                 total_q: int, total_k: int, heads_q: int, heads_kv: int, head_dim: int,
                 causal: bool) -> VarlenPlan:
@@ -221,8 +258,8 @@ def bwd_design(p: AttnParams, varlen: bool = False) -> int:
 # --------------------------------------------------------------------- forward
 def fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
         return_lse: bool = True, out: Optional[torch.Tensor] = None,
-        lse_out: Optional[torch.Tensor] = None,
-        options: Optional[dict] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        lse_out: Optional[torch.Tensor] = None, options: Optional[dict] = None,
+        block_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] bf16 -> (o [B, Sq, Hq, d], lse [B, Hq, Sq] fp32)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _expect(t, n)
@@ -230,6 +267,8 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
     sk, hkv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     p = make_params(b, sq, sk, hq, hkv, d, scale, causal, options=options)
+    bm = prepare_block_mask(block_mask, b, hq, sq, sk)
+    set_block_mask(p, bm)
     o = torch.empty_like(q) if out is None else out
     lse = None
     if return_lse:
@@ -267,7 +306,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
 # -------------------------------------------------------------------- backward
 def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float] = None,
         deterministic: bool = False, workspace: Optional[torch.Tensor] = None,
-        options: Optional[dict] = None):
+        options: Optional[dict] = None, block_mask: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of sum(do * o) for fixed-length BSHD inputs."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _expect(t, n)
@@ -276,6 +315,8 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale: Optional[float
     sk, hkv = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     p = make_params(b, sq, sk, hq, hkv, d, scale, causal, deterministic, options=options)
+    bm = prepare_block_mask(block_mask, b, hq, sq, sk)
+    set_block_mask(p, bm)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = workspace if workspace is not None else _workspace(bwd_workspace_size(p), q.device)
     _check(_lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),

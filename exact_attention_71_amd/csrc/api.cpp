@@ -50,6 +50,29 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------- validation
+// Bytes of a block-mask buffer: the span of the last (batch, head) block
+// table plus the strides, rounded up to whole 4-byte words (the kernels read
+// the mask a word at a time, and a word that ends past the buffer range reads
+// as zero).
+int64_t mask_bytes(const attn_params* p) {
+  const int64_t nqb = cdiv(p->seqlen_q, kMaskBlock), nkb = cdiv(p->seqlen_k, kMaskBlock);
+  if (p->batch <= 0 || nqb * nkb == 0) return 0;
+  const int64_t span = (int64_t)(p->batch - 1) * p->block_mask_stride_b +
+                       (int64_t)(p->num_heads_q - 1) * p->block_mask_stride_h + nqb * nkb;
+  return (span + 3) / 4 * 4;
+}
+MaskView mask_view(const attn_params* p) {
+  MaskView m;
+  std::memset(&m, 0, sizeof(m));
+  if (!p->block_mask) return m;
+  m.mask = p->block_mask;
+  m.sb = p->block_mask_stride_b;
+  m.sh = p->block_mask_stride_h;
+  m.nkb = cdiv(p->seqlen_k, kMaskBlock);
+  m.range = static_cast<int>(mask_bytes(p));
+  return m;
+}
+
 attn_status check_params(const attn_params* p, bool varlen) {
   if (!p) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return ATTN_ERR_UNSUPPORTED;
@@ -69,6 +92,12 @@ attn_status check_params(const attn_params* p, bool varlen) {
   if (!(o.tau == 0.0f || o.tau == -1.0f || (o.tau > 0.0f && o.tau <= 64.0f)))
     return ATTN_ERR_INVALID_ARGUMENT;
   if (o.spin_limit < 0 || o.ds_budget < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->block_mask) {
+    if (p->block_mask_stride_b < 0 || p->block_mask_stride_h < 0 ||
+        (reinterpret_cast<uintptr_t>(p->block_mask) & 3u))
+      return ATTN_ERR_INVALID_ARGUMENT;
+    if (varlen || o.exp_emulation != 0 || mask_bytes(p) > kMaxExtent) return ATTN_ERR_UNSUPPORTED;
+  }
   // one (sequence, head) slab must stay within 32-bit byte offsets
   const int64_t d = p->head_dim;
   const int64_t ext_q = (int64_t)p->seqlen_q * p->num_heads_q * d * 4;  // fp32 dQ accumulator
@@ -157,7 +186,8 @@ int64_t ds_area_bytes(const attn_params* p, bool varlen) {
 int bwd_design_of(const attn_params* p, bool varlen) {
   const Opts o = opts_of(p);
   if (o.bwd_design == ATTN_BWD_FUSED_DQ || o.bwd_design == ATTN_BWD_RECOMPUTE) return o.bwd_design;
-  const bool fits = ds_area_bytes(p, varlen) <= o.ds_budget &&
+  // stored dS needs the whole dS area within the budget (and no block mask)
+  const bool fits = ds_area_bytes(p, varlen) <= o.ds_budget && !p->block_mask &&
                     ds_geom(p->seqlen_q, p->seqlen_k, p->causal != 0).rows < kDsMaxRows;
   if (o.bwd_design == ATTN_BWD_STORED_DS) return fits ? ATTN_BWD_STORED_DS : -1;
   return (p->head_dim >= 128 && fits) ? ATTN_BWD_STORED_DS : ATTN_BWD_RECOMPUTE;
@@ -338,6 +368,7 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   fp.alpha = p->softmax_scale;
   fp.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   fp.tau = op.tau;
+  fp.mask = mask_view(p);
   const int pcus = launch_cus(op.persistent);
   if (varlen) {
     // the tables from a plan, or from a schedule pass into the workspace
@@ -429,6 +460,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.n_sem = fused ? wl.n_sem : 0;
   bp.zero_acc = fused ? 1 : 0;
   bp.spin_limit = op.spin_limit;
+  bp.mask = mask_view(p);
   const int bmq = use_ds ? DqDsCfg<128>::BM : dq_block_m(d);
   bp.nm_dq = cdiv(p->seqlen_q, bmq);
   if (use_ds) {

@@ -135,7 +135,7 @@ struct alignas(16) BwdSmem {
   int ticket;
 };
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool MASK>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   constexpr int BN = BwdCfg<D>::BN;     // 128 keys, 32 per wave
   constexpr int BM = BwdCfg<D>::BM;     // queries per step
@@ -188,6 +188,15 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
   const int m_first = causal ? causal_row_begin(n0, shift) / BM : 0;
   const int nlast_all = cdiv(lk, BN) - 1;   // last key block of this sequence
+  // block mask (MASK): the block's 128 keys form one mask column, each step's
+  // rows lie in one 128-row block
+  const rsrc_t mrs = raw_rsrc(p.mask.mask, MASK ? p.mask.range : 0);
+  uint32_t mcol = 0;
+  if constexpr (MASK) {
+    static_assert(BN == kMaskBlock, "one mask column per key block");
+    mcol = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        (int64_t)t.seq * p.mask.sb + n0 / kMaskBlock));
+  }
 
   // ---- K, V of this wave's keys as B operands; K^T of the block in LDS
   const int64_t kv_bytes = ((int64_t)(lk - 1) * kstride + D) * 2;
@@ -323,8 +332,13 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
         dp[qb] = mfma32(ao, vf[kk], dp[qb]);
       }
 
-    // P = 2^(S alpha log2e - LSE log2e), dS = P (dP - D) (the stored rows hold -D)
-    const bool need_mask = (n0 + BN > lk) || (causal && n0 + BN - 1 > mq0 + shift);
+    // P = 2^(S alpha log2e - LSE log2e), dS = P (dP - D) (the stored rows hold -D);
+    // a cleared mask block hides the whole step
+    bool hid = false;
+    if constexpr (MASK)
+      hid = !mask_set(mrs, mcol + static_cast<uint32_t>((int64_t)hq * p.mask.sh +
+                                                         (int64_t)(mq0 / kMaskBlock) * p.mask.nkb));
+    const bool need_mask = hid || (n0 + BN > lk) || (causal && n0 + BN - 1 > mq0 + shift);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
           float pv = fast_exp2(__builtin_fmaf(s[qb][i], sl2, -l4[r]));
           if (need_mask) {
             const int qrow = mq0 + q4 + r;
-            if (mykey >= lk || (causal && mykey > qrow + shift)) pv = 0.0f;
+            if (hid || mykey >= lk || (causal && mykey > qrow + shift)) pv = 0.0f;
           }
           s[qb][i] = pv;
           dp[qb][i] = pv * dp[qb][i];
@@ -479,15 +493,23 @@ hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool FUSED>
+void launch_main_dm(const BwdParams& p, int grid, hipStream_t stream) {
+  if (p.mask.mask)
+    hipLaunchKernelGGL((bwd_main_kernel<D, FUSED, true>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_main_kernel<D, FUSED, false>), dim3(grid), dim3(256), 0, stream, p);
+}
+
 hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   switch (d * 2 + (fused ? 1 : 0)) {
-    case 128: hipLaunchKernelGGL((bwd_main_kernel<64, false>), dim3(grid), dim3(256), 0, stream, p); break;
-    case 129: hipLaunchKernelGGL((bwd_main_kernel<64, true>), dim3(grid), dim3(256), 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((bwd_main_kernel<128, false>), dim3(grid), dim3(256), 0, stream, p); break;
-    case 257: hipLaunchKernelGGL((bwd_main_kernel<128, true>), dim3(grid), dim3(256), 0, stream, p); break;
-    case 512: hipLaunchKernelGGL((bwd_main_kernel<256, false>), dim3(grid), dim3(256), 0, stream, p); break;
-    case 513: hipLaunchKernelGGL((bwd_main_kernel<256, true>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 128: launch_main_dm<64, false>(p, grid, stream); break;
+    case 129: launch_main_dm<64, true>(p, grid, stream); break;
+    case 256: launch_main_dm<128, false>(p, grid, stream); break;
+    case 257: launch_main_dm<128, true>(p, grid, stream); break;
+    case 512: launch_main_dm<256, false>(p, grid, stream); break;
+    case 513: launch_main_dm<256, true>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -37,8 +37,9 @@ template <int D, int BM>
 constexpr int dkdv_smem_bytes() { return 2 * 3 * BM * 2 * D + 3 * 2 * BM * 4; }
 
 // One tile: the keys of key block t.block of (sequence t.seq, KV head t.head).
-template <int D, int KB, int BM, bool DS>
+template <int D, int KB, int BM, bool DS, bool MASK>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, char* smem) {
+  static_assert(!(DS && MASK), "block masks run with the recomputing dQ kernel");
   constexpr int NW = 4, NT = NW * 64;
   constexpr int KPW = 32 * KB;          // keys per wave
   constexpr int BN = NW * KPW;          // keys per workgroup
@@ -150,6 +151,17 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
                                                        ds_col_start(dsg, blk) * 2048));
     ds_soff = ds_soff0;
   }
+  // block mask (MASK): this wave's keys lie in one 128-key block; the byte of
+  // (query head kvh0 + c_h, query block mq0 / 128) sits at
+  // m_base + c_h * m_sh + (mq0 / 128) * m_nkb of the mask buffer
+  const rsrc_t mrs = raw_rsrc(p.mask.mask, MASK ? p.mask.range : 0);
+  uint32_t m_base = 0, m_sh = 0, m_nkb = 0;
+  if constexpr (MASK) {
+    m_base = keep_sgpr(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        (int64_t)t.seq * p.mask.sb + (int64_t)kvh0 * p.mask.sh + wk0 / kMaskBlock)));
+    m_sh = keep_sgpr(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p.mask.sh)));
+    m_nkb = keep_sgpr(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p.mask.nkb)));
+  }
   const int64_t q_tile = (qs * qstride + (int64_t)kvh0 * D) * 2;
   const char* const q_seq = keep_sgpr(static_cast<const char*>(p.q) + q_tile);
   const char* const do_seq = keep_sgpr(static_cast<const char*>(p.dout) + q_tile);
@@ -252,14 +264,14 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // the previous step), of the next step (slot offset nxt) on return.
   // has_next: a later step exists (mid-step sync); iss >= 0: the ring slot the
   // loads of step + 2 go to.
-  auto step_body = [&](int mq0, bool need_mask, bf16x8& f0, bf16x8& f1, bool has_next, int iss,
-                       int nxt) {
+  auto step_body = [&](int mq0, bool need_mask, bool hid, bf16x8& f0, bf16x8& f1, bool has_next,
+                       int iss, int nxt) {
     constexpr int OT = NS * TILE;   // dO tile offset from the Q tile
     int rel[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = wk0 + 32 * kb + c;
-      rel[kb] = key >= lk ? 0x7fffffff : (causal ? key - shift - mq0 - 4 * g : -1);
+      rel[kb] = (hid || key >= lk) ? 0x7fffffff : (causal ? key - shift - mq0 - 4 * g : -1);
     }
     // Hand schedule (one wave per SIMD: nothing else hides this wave's VALU
     // work, and issue is in order). The step reads one stream of LDS operand
@@ -425,11 +437,17 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   __builtin_amdgcn_s_barrier();
 
   int st = 0;   // ring slot of the step being computed (step % NS)
+  int c_h = 0;  // query head of the compute cursor, from kvh0
   bf16x8 f0 = fetch_first(0, 0), f1 = fetch_first(1, 0);
   for (int step = 0; step < n_steps; ++step) {
     const int mq0 = c_m * BM;
     const bool wrap = ++c_m == nm;
     if (wrap) c_m = m_first;
+    // a cleared mask block hides every pair of this wave's step (P = 0)
+    bool hid = false;
+    if constexpr (MASK)
+      hid = !mask_set(mrs, m_base + c_h * m_sh + static_cast<uint32_t>(mq0 / kMaskBlock) * m_nkb);
+    if (wrap) ++c_h;
     const bool has_next = step + 1 < n_steps;
     const int iss = step + NS - 1 < n_steps ? (st == 0 ? NS - 1 : st - 1) : -1;  // (step + 2) % NS
     const int nxt = st == NS - 1 ? -(NS - 1) * TILE : TILE;                      // next slot
@@ -437,8 +455,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     // anyway (masked to zero): skipping it would need a second path around
     // the mid-step barrier, and the register allocator answers such a split
     // of the AGPR accumulators with spills.
-    const bool need_mask = (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
-    step_body(mq0, need_mask, f0, f1, has_next, iss, nxt);
+    const bool need_mask = hid || (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
+    step_body(mq0, need_mask, hid, f0, f1, has_next, iss, nxt);
     if constexpr (DS) {   // the compute cursor's next sub-rows
       if (wrap) {
         ds_col = keep_sgpr(ds_col + ds_reg);
@@ -481,7 +499,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 
 // Persistent workgroups walk the tiles (schedule.hpp: persistent_index); a
 // one-shot grid (gridDim.x == ntiles) gives each workgroup one tile.
-template <int D, int KB, int BM, bool DS>
+template <int D, int KB, int BM, bool DS, bool MASK>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM>()];
   __shared__ int ticket;
@@ -499,22 +517,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
     } else {
       t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, false, p.nxcd, p.natural != 0);
     }
-    dkdv_tile<D, KB, BM, DS>(p, t, smem);
+    dkdv_tile<D, KB, BM, DS, MASK>(p, t, smem);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }
 
-template <int D, bool DS>
+template <int D, bool DS, bool MASK>
 hipError_t launch_dkdv_t(const BwdParams& p, int cus, hipStream_t stream) {
   using C = DkdvCfg<D>;
-  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM, DS>, 256);
+  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM, DS, MASK>, 256);
   const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM, DS>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM, DS, MASK>), dim3(grid), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 template <int D>
 hipError_t launch_dkdv_d(const BwdParams& p, int cus, hipStream_t stream) {
-  return p.ds ? launch_dkdv_t<D, true>(p, cus, stream) : launch_dkdv_t<D, false>(p, cus, stream);
+  if (p.mask.mask) {
+    if (p.ds) return hipErrorInvalidValue;   // the host never combines the two
+    return launch_dkdv_t<D, false, true>(p, cus, stream);
+  }
+  return p.ds ? launch_dkdv_t<D, true, false>(p, cus, stream)
+              : launch_dkdv_t<D, false, false>(p, cus, stream);
 }
 
 }  // namespace

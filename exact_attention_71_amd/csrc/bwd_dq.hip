@@ -31,7 +31,7 @@ template <int D, int BN>
 constexpr int dq_smem_bytes() { return 2 * 3 * BN * 2 * D; }
 
 // One tile: query block t.block of (sequence t.seq, query head t.head).
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, bool MASK>
 __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char* smem) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
@@ -77,6 +77,14 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
   const int myq = qw0 + c;
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const float sl2 = p.scale_log2;
+  // block mask (MASK): this wave's rows lie in one 128-row block, whose mask
+  // row starts at byte mrow of the mask buffer
+  const rsrc_t mrs = raw_rsrc(p.mask.mask, MASK ? p.mask.range : 0);
+  uint32_t mrow = 0;
+  if constexpr (MASK) {
+    mrow = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        (int64_t)t.seq * p.mask.sb + (int64_t)h * p.mask.sh + (int64_t)(qw0 / kMaskBlock) * p.mask.nkb));
+  }
 
   // ---- this lane's query row: Q and dO as B operands, LSE log2 e and D as scalars
   const int64_t qbytes = ((int64_t)(lq - 1) * qstride + D) * 2;
@@ -263,8 +271,10 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
     const int st = n % NS;
     if (n + NS - 1 < n_tiles) issue(n + NS - 1);
     const int k0 = n * BN;
-    // whole wave below the diagonal's start: no visible pair in this tile
-    const bool active = !(causal && k0 > qw0 + 31 + shift);
+    // whole wave below the diagonal's start, or a cleared mask block: no
+    // visible pair in this tile
+    bool active = !(causal && k0 > qw0 + 31 + shift);
+    if constexpr (MASK) active = active && mask_set(mrs, mrow + static_cast<uint32_t>(k0 / kMaskBlock));
     const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
     if (active) tile_body(k0, need_mask);
     advance_slot(st);
@@ -287,7 +297,7 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
 }
 
 // Persistent workgroups walk the query blocks (schedule.hpp: persistent_index).
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, bool MASK>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_smem_bytes<D, BN>()];
   __shared__ int ticket;
@@ -305,18 +315,23 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams) {
     } else {
       t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
     }
-    dq_tile<D, NW, BN>(p, t, smem);
+    dq_tile<D, NW, BN, MASK>(p, t, smem);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }
 
+template <int D, bool MASK>
+hipError_t launch_dq_t(const BwdParams& p, int cus, hipStream_t stream) {
+  using C = DqCfg<D>;
+  static const int occ = resident_per_cu(bwd_dq_kernel<D, C::NW, C::BN, MASK>, C::NW * 64);
+  const int grid = persistent_grid(p.ntiles_dq, cus * occ, p.nxcd);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, C::NW, C::BN, MASK>), dim3(grid), dim3(C::NW * 64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
 template <int D>
 hipError_t launch_dq_d(const BwdParams& p, int cus, hipStream_t stream) {
-  using C = DqCfg<D>;
-  static const int occ = resident_per_cu(bwd_dq_kernel<D, C::NW, C::BN>, C::NW * 64);
-  const int grid = persistent_grid(p.ntiles_dq, cus * occ, p.nxcd);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, C::NW, C::BN>), dim3(grid), dim3(C::NW * 64), 0, stream, p);
-  return hipGetLastError();
+  return p.mask.mask ? launch_dq_t<D, true>(p, cus, stream) : launch_dq_t<D, false>(p, cus, stream);
 }
 
 }  // namespace

@@ -288,6 +288,17 @@ __device__ __forceinline__ rsrc_t raw_rsrc(const void* base, int range) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, range, 0x00020000);
 }
 
+// One byte of a block mask (nonzero: the block is visible), read by the
+// scalar unit from the dword that holds it: a uniform value, waited for in
+// the same asm block (the wait also drains the LDS reads in flight). Offsets
+// past the resource's range read as zero: hidden.
+__device__ __forceinline__ bool mask_set(rsrc_t r, uint32_t byte_off) {
+  uint32_t w;
+  asm volatile("s_buffer_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(w) : "s"(r), "s"(byte_off & ~3u));
+  return ((w >> ((byte_off & 3u) * 8u)) & 0xffu) != 0u;
+}
+
 __device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, int voff, int soff) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return __builtin_bit_cast(bf16x8, x);

@@ -59,7 +59,7 @@ constexpr int fwd_smem_bytes() { return 2 * fwd_ring_depth<D, BN>() * BN * 2 * D
 // and the Q fragments of `nxt` (when has_nxt), so that the next tile starts
 // without waiting for them. `pre` says the previous tile did so for this one;
 // the return value says whether this one did for `nxt`.
-template <int D, int NW, int QB, int BN, int EMU>
+template <int D, int NW, int QB, int BN, int EMU, bool MASK>
 __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char* smem,
                                          bf16x8 (&qf)[QB][D / 16], int& s0, bool pre,
                                          Tile nxt, bool has_nxt) {
@@ -104,6 +104,14 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int qw0 = m0 + w * 32 * QB;     // first query row of this wave
+  // block mask (MASK): this wave's rows lie in one 128-row block, whose mask
+  // row starts at byte mrow of the mask buffer
+  const rsrc_t mrs = raw_rsrc(p.mask.mask, MASK ? p.mask.range : 0);
+  uint32_t mrow = 0;
+  if constexpr (MASK) {
+    mrow = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        (int64_t)t.seq * p.mask.sb + (int64_t)h * p.mask.sh + (int64_t)(qw0 / kMaskBlock) * p.mask.nkb));
+  }
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const float tau = keep_sgpr(p.tau);
   const bf16* __restrict__ qp = static_cast<const bf16*>(p.q);
@@ -255,7 +263,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       if (n + NS - 1 < n_tiles) issue(n + NS - 1);
     }
     const int k0 = n * BN;
-    const bool active = !(causal && k0 > qw0 + 32 * QB - 1 + shift);
+    bool active = !(causal && k0 > qw0 + 32 * QB - 1 + shift);
+    // a cleared mask block: this wave skips the tile (no visible key in it)
+    if constexpr (MASK) active = active && mask_set(mrs, mrow + static_cast<uint32_t>(k0 / kMaskBlock));
     f32x16 s[NKB][QB];   // S^T, then P^T in place
     if (active) {
       // S^T = K Q^T for this tile, key block by key block; the mask and the
@@ -443,7 +453,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
 // Persistent workgroups walk the query blocks (schedule.hpp: persistent_index).
 // The next tile is drawn before the current one runs, so that its first loads
 // can go out during the current tile's last key tile.
-template <int D, int NW, int QB, int BN, int EMU>
+template <int D, int NW, int QB, int BN, int EMU, bool MASK>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[fwd_smem_bytes<D, BN>()];
   __shared__ int ticket;
@@ -471,21 +481,31 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   while (have) {
     const bool have_next = draw(r, nxt);
     const FwdParams& p = kernel_args<FwdParams>();
-    pre = fwd_tile<D, NW, QB, BN, EMU>(p, cur, smem, qf, s0, pre, nxt, have_next);
+    pre = fwd_tile<D, NW, QB, BN, EMU, MASK>(p, cur, smem, qf, s0, pre, nxt, have_next);
     __syncthreads();   // the next tile's loads reuse the ring slots
     cur = nxt;
     have = have_next;
   }
 }
 
+template <int D, int EMU, bool MASK>
+hipError_t launch_dm(const FwdParams& p, int cus, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  static const int occ = resident_per_cu(fwd_kernel<D, C::NW, C::QB, C::BN, EMU, MASK>, C::NW * 64);
+  const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
+  hipLaunchKernelGGL((fwd_kernel<D, C::NW, C::QB, C::BN, EMU, MASK>), dim3(grid),
+                     dim3(C::NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+// block masks only with every exponential on v_exp_f32 (the host refuses the rest)
 template <int D, int EMU>
 hipError_t launch_d(const FwdParams& p, int cus, hipStream_t stream) {
-  using C = FwdCfg<D>;
-  static const int occ = resident_per_cu(fwd_kernel<D, C::NW, C::QB, C::BN, EMU>, C::NW * 64);
-  const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
-  hipLaunchKernelGGL((fwd_kernel<D, C::NW, C::QB, C::BN, EMU>), dim3(grid), dim3(C::NW * 64), 0,
-                     stream, p);
-  return hipGetLastError();
+  if constexpr (EMU == 0) {
+    if (p.mask.mask) return launch_dm<D, 0, true>(p, cus, stream);
+  } else {
+    if (p.mask.mask) return hipErrorInvalidValue;
+  }
+  return launch_dm<D, EMU, false>(p, cus, stream);
 }
 
 }  // namespace

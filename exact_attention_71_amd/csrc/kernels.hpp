@@ -18,6 +18,17 @@ struct SeqView {
   int total_q;            // rows of the packed q (varlen LSE stride)
 };
 
+// Block-sparse mask (fixed length): byte (b, h, i, j) at
+// b * sb + h * sh + i * nkb + j, one per 128 x 128 block of (query, key)
+// pairs; zero hides the block. mask == null: no mask.
+constexpr int kMaskBlock = 128;
+struct MaskView {
+  const uint8_t* mask;
+  int64_t sb, sh;       // bytes between batches / query heads (0: shared)
+  int nkb;              // entries per mask row: ceil(Sk / 128)
+  int range;            // bytes of the mask buffer
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -37,6 +48,7 @@ struct FwdParams {
   float alpha;            // softmax scale
   float scale_log2;       // alpha * log2(e)
   float tau;              // rescale threshold on the running-max jump, log2 units
+  MaskView mask;
 };
 
 struct BwdParams {
@@ -85,6 +97,7 @@ struct BwdParams {
   // the register order of the dK/dV kernel, holding only the sub-tiles that
   // kernel writes (DsGeom below); the regions of the heads of a sequence follow
   // each other, sequences in order.
+  MaskView mask;
   char* ds;
   const int64_t* ds_prefix;  // varlen: first sub-tile of each sequence, -1 for a
                              // sequence whose regions do not fit the area (its

@@ -160,6 +160,20 @@ typedef struct attn_params {
   attn_options opt;      /* per-call design and tuning options (zero: defaults) */
   const attn_varlen_plan* varlen_plan; /* varlen calls: the cached schedule (NULL: each
                                           call computes it in its workspace) */
+  /* Block-sparse mask (fixed length; NULL: none), the reading taken of the
+   * synthesis page's block-sparse attention on the FA4 framework: one byte
+   * per 128 x 128 block of (query, key) pairs, at byte
+   *   b * block_mask_stride_b + h * block_mask_stride_h + i * ceil(seqlen_k / 128) + j
+   * for batch b, query head h, query block i < ceil(seqlen_q / 128), key
+   * block j; 0 hides every pair of the block, ANDed with the causal rule.
+   * Rows that see no key get O = 0, LSE = -inf, dQ = 0. Strides may be 0 (one
+   * mask shared by the batches or heads). The pointer must be 4-byte aligned;
+   * the mask is read in 4-byte words, so the buffer must hold its span rounded
+   * up to a multiple of 4 bytes, at most 2^31 - 1; packed variable lengths, the
+   * stored-dS design (ATTN_BWD_AUTO then recomputes dQ) and exp_emulation are
+   * refused with a mask (ATTN_ERR_UNSUPPORTED). */
+  const uint8_t* block_mask;
+  int64_t block_mask_stride_b, block_mask_stride_h;
 } attn_params;
 
 /* "OK", "invalid argument", ... ; never NULL. */

@@ -434,3 +434,31 @@ def test_varlen_plan_validation():
     f = _p(batch=5, seqlen_q=700, seqlen_k=700, heads_q=4, heads_kv=2, head_dim=128, causal=True)
     f.varlen_plan = ctypes.pointer(good)
     assert lib.attn_fwd(ctypes.byref(f), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
+
+
+def test_block_mask_validation():
+    """Block masks: 4-byte aligned, non-negative strides, fixed length only,
+    no exp emulation, and no stored dS (the automatic design recomputes dQ)."""
+    lib = ea.load()
+    kw = dict(batch=2, seqlen_q=300, seqlen_k=300, heads_q=4, heads_kv=2, head_dim=128,
+              causal=True)
+
+    def pm(ptr=FAKE, sb=9, sh=9, **extra):
+        p = _p(**dict(kw, **extra))
+        p.block_mask, p.block_mask_stride_b, p.block_mask_stride_h = ptr, sb, sh
+        return p
+
+    args = [None, FAKE, FAKE, FAKE, None, None, 0, None]     # null q: fails after validation
+    assert lib.attn_fwd(ctypes.byref(pm()), *args) == INVALID
+    assert ea.bwd_design(pm()) == ea.BWD_RECOMPUTE                       # automatic: recompute
+    assert ea.bwd_design(_p(**kw)) == ea.BWD_STORED_DS                   # without a mask
+    assert ea.bwd_design(pm(options=dict(bwd_design=ea.BWD_STORED_DS))) == -1
+    assert ea.bwd_design(pm(options=dict(bwd_design=ea.BWD_FUSED_DQ))) == ea.BWD_FUSED_DQ
+    full = [FAKE] * 4 + [None, None, 0, None]
+    assert lib.attn_fwd(ctypes.byref(pm(ptr=FAKE + 2)), *full) == INVALID       # misaligned
+    assert lib.attn_fwd(ctypes.byref(pm(sb=-1)), *full) == INVALID
+    assert lib.attn_fwd(ctypes.byref(pm(options=dict(exp_emulation=2))), *full) == UNSUPPORTED
+    assert lib.attn_fwd(ctypes.byref(pm(sh=1 << 30)), *full) == UNSUPPORTED     # > 2^31 bytes
+    pv = pm(total_q=600, total_k=600)
+    assert lib.attn_fwd_varlen(ctypes.byref(pv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                               1 << 20, None) == UNSUPPORTED
