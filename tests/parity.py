@@ -3,6 +3,9 @@
 Criteria, from the stated pass bar for bf16 inputs:
   O    max-abs <= 1e-2 beyond the output's own bf16 rounding (half a bf16 ulp
        of the oracle value, which no bf16 output can avoid), mean-abs <= 1e-3;
+       and, where the bf16 spacing allows it (|O| < 2, spacing <= 2^-7), the
+       error against the oracle rounded to bf16 is <= 1e-2 as well (the
+       survey's proposal for the tolerance conflict of large outputs);
   LSE  max-abs <= 1e-3;
   dQ, dK, dV  relative L2 <= 2e-2.
 """
@@ -25,16 +28,20 @@ def o_errors(o_gpu, o_ref: np.ndarray) -> dict:
     err = np.abs(g - o_ref)
     half_ulp = 0.5 * oracle.bf16_ulp(o_ref)
     floor = np.abs(oracle.round_bf16(o_ref) - o_ref)
+    vs_rounded = np.abs(g - oracle.round_bf16(o_ref))
+    small = np.abs(o_ref) < 2.0
     return {"max_abs": float(err.max(initial=0.0)),
             "max_excess": float(np.max(err - half_ulp, initial=0.0)),
             "mean_abs": float(err.mean()) if err.size else 0.0,
-            "max_vs_rounded_ref": float(np.abs(g - oracle.round_bf16(o_ref)).max(initial=0.0)),
+            "max_vs_rounded_ref": float(vs_rounded.max(initial=0.0)),
+            "max_vs_rounded_ref_below2": float(vs_rounded[small].max(initial=0.0)),
             "bf16_floor": float(floor.max(initial=0.0))}
 
 
 def check_o(o_gpu, o_ref, what=""):
     e = o_errors(o_gpu, o_ref)
     assert e["max_excess"] <= O_MAX and e["mean_abs"] <= O_MEAN, (what, e)
+    assert e["max_vs_rounded_ref_below2"] <= O_MAX, (what, e)
     return e
 
 
