@@ -193,7 +193,7 @@ int bwd_design_of(const attn_params* p, bool varlen) {
   return (p->head_dim >= 128 && fits) ? ATTN_BWD_STORED_DS : ATTN_BWD_RECOMPUTE;
 }
 int64_t bwd_mblocks(const attn_params* p, bool varlen) {
-  const int bm = bwd_block_m(p->head_dim);
+  const int bm = fused_block_m(p->head_dim);
   return varlen ? (int64_t)cdiv(p->total_q, bm) + p->batch
                 : (int64_t)p->batch * cdiv(p->seqlen_q, bm);
 }
@@ -245,7 +245,7 @@ int dq_grid(const attn_params* p, bool varlen) {
   return p->batch * p->num_heads_q * cdiv(p->seqlen_q, bm);
 }
 int bwd_grid(const attn_params* p, bool varlen, bool fused) {
-  const int bn = fused ? bwd_block_n(p->head_dim) : dkdv_block_n(p->head_dim);
+  const int bn = fused ? fused_block_n(p->head_dim) : dkdv_block_n(p->head_dim);
   if (varlen) return (cdiv(p->total_k, bn) + p->batch) * p->num_heads_kv;
   return p->batch * p->num_heads_kv * cdiv(p->seqlen_k, bn);
 }
@@ -305,12 +305,12 @@ SchedSet make_set(const attn_params* p, int kind, const int32_t* cu_q, const int
   s.heads = qblocks ? p->num_heads_q : p->num_heads_kv;
   s.blk = kind == kSetFwd ? fwd_block_m(d)
         : kind == kSetDkdv ? dkdv_block_n(d)
-        : kind == kSetFused ? bwd_block_n(d)
+        : kind == kSetFused ? fused_block_n(d)
         : kind == kSetDq ? dq_block_m(d) : DqDsCfg<128>::BM;
   s.order = reinterpret_cast<int*>(base + m.order);
   s.tile_prefix = reinterpret_cast<int*>(base + m.tile_prefix);
   s.mb_prefix = m.mb ? reinterpret_cast<int*>(base + m.mb_prefix) : nullptr;
-  s.mb_blk = bwd_block_m(d);
+  s.mb_blk = fused_block_m(d);
   s.queue = reinterpret_cast<unsigned*>(base + m.queue);
   s.ds_prefix = m.ds ? reinterpret_cast<int64_t*>(base + m.ds_prefix) : nullptr;
   s.ds_heads = p->num_heads_q;
@@ -444,7 +444,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   const Opts op = opts_of(p);
   const bool fused = fused_mode;
   const bool use_ds = wl.design == ATTN_BWD_STORED_DS;
-  const int bn = fused ? bwd_block_n(d) : dkdv_block_n(d), bm = bwd_block_m(d);
+  const int bn = fused ? fused_block_n(d) : dkdv_block_n(d), bm = fused_block_m(d);
   bp.nn = cdiv(p->seqlen_k, bn);
   bp.nm = cdiv(p->seqlen_q, bm);
   bp.sec = section_width(2ll * bp.group * p->seqlen_q * d * 2);
@@ -461,6 +461,9 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.zero_acc = fused ? 1 : 0;
   bp.spin_limit = op.spin_limit;
   bp.mask = mask_view(p);
+  // fused design at head_dim 64 / 128: dQ inside the 256-key dK/dV kernel
+  const bool fused_dkdv = fused && fused_in_dkdv(d);
+  bp.dq_mode = fused_dkdv ? (p->deterministic ? 2 : 1) : 0;
   const int bmq = use_ds ? DqDsCfg<128>::BM : dq_block_m(d);
   bp.nm_dq = cdiv(p->seqlen_q, bmq);
   if (use_ds) {
@@ -503,13 +506,16 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     }
     if (p->varlen_plan) sched.nsets = 0;   // computed when the plan was built
   }
+  // The deterministic chain needs tiles started in the order of its turns:
+  // workgroups draw them from the ticket word the preprocess clears
+  if (bp.dq_mode == 2) bp.queue = reinterpret_cast<unsigned*>(bp.ticket);
   if (pre) {
     if (varlen && launch_varlen_schedule(sched, stream) != hipSuccess) return ATTN_ERR_HIP;
     if (launch_bwd_pre(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (main) {
-    const hipError_t e = fused ? launch_bwd_main(bp, d, bp.ntiles, true, stream)
-                               : launch_bwd_dkdv(bp, d, pcus, stream);
+    const hipError_t e = fused && !fused_dkdv ? launch_bwd_main(bp, d, bp.ntiles, stream)
+                                              : launch_bwd_dkdv(bp, d, pcus, stream);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   if (dqk) {
@@ -710,7 +716,7 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
     }
   } else {
     const bool fz = which == 2;   // 1: dK/dV kernel; 2: fused deterministic (ticket order)
-    const int nn = cdiv(p->seqlen_k, fz ? bwd_block_n(d) : dkdv_block_n(d));
+    const int nn = cdiv(p->seqlen_k, fz ? fused_block_n(d) : dkdv_block_n(d));
     const int grp = p->num_heads_q / p->num_heads_kv;
     const int sec = section_width(2ll * grp * p->seqlen_q * d * 2);
     const int n = bwd_grid(p, false, fz);

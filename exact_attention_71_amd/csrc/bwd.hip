@@ -14,9 +14,13 @@
 // Kernels:
 //   bwd_pre   D = rowsum(dO o O) and LSE * log2(e) (fp32), zero the dQ
 //             accumulator and the semaphores / ticket / status words;
-//   bwd_main  per (sequence, KV head, 128-key block): dK, dV in registers,
-//             dQ atomics; all query heads of the KV group are walked here so
-//             dK, dV need no cross-workgroup reduction;
+//   bwd_main  the fused design at head_dim 256, per (sequence, KV head,
+//             128-key block): dK, dV in registers, dQ atomics; all query
+//             heads of the KV group are walked here so dK, dV need no
+//             cross-workgroup reduction (at head_dim 64 and 128 the 256-key
+//             dK/dV kernel of bwd_dkdv.hip forms and adds dQ itself, one
+//             reduction per 256 keys; at 256 its Q / dO ring leaves no LDS
+//             for the K tile that needs);
 //   bwd_post  dQ = bf16(alpha * dQ_acc).
 //
 // gfx950 layout of bwd_main: 4 wavefronts, wave w owns keys 32w..32w+31 of
@@ -135,7 +139,7 @@ struct alignas(16) BwdSmem {
   int ticket;
 };
 
-template <int D, bool FUSED, bool MASK>
+template <int D, bool MASK>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   constexpr int BN = BwdCfg<D>::BN;     // 128 keys, 32 per wave
   constexpr int BM = BwdCfg<D>::BM;     // queries per step
@@ -153,9 +157,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
-  // Without the fused dQ there is no cross-workgroup reduction: every order
-  // gives the same bits, and the deterministic flag needs no ordering.
-  const bool det = FUSED && p.deterministic != 0;
+  const bool det = p.deterministic != 0;
   const bool causal = p.causal != 0;
 
   // ---- which key block (deterministic: ticket order = shortest first)
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       vf[kk] = buf_load16(vr, off + 32 * kk, 0);
     }
   }
-  if (FUSED) {
+  {
     constexpr int KU = (BN / 4) * CPR;
     for (int u = tid; u < KU; u += 256) {
       const int kg = u / CPR, dc = u % CPR;
@@ -376,14 +378,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
         }
       }
 
-    if (!FUSED) {
-      __syncthreads();          // every wave is done with this step's tiles
-      if (step + 1 < n_steps) {
-        store_step();
-        __syncthreads();
-      }
-      continue;
-    }
     // dS -> LDS as [query][key]
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
@@ -493,25 +487,13 @@ hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool FUSED>
-void launch_main_dm(const BwdParams& p, int grid, hipStream_t stream) {
-  if (p.mask.mask)
-    hipLaunchKernelGGL((bwd_main_kernel<D, FUSED, true>), dim3(grid), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((bwd_main_kernel<D, FUSED, false>), dim3(grid), dim3(256), 0, stream, p);
-}
-
-hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream) {
+hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  switch (d * 2 + (fused ? 1 : 0)) {
-    case 128: launch_main_dm<64, false>(p, grid, stream); break;
-    case 129: launch_main_dm<64, true>(p, grid, stream); break;
-    case 256: launch_main_dm<128, false>(p, grid, stream); break;
-    case 257: launch_main_dm<128, true>(p, grid, stream); break;
-    case 512: launch_main_dm<256, false>(p, grid, stream); break;
-    case 513: launch_main_dm<256, true>(p, grid, stream); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (d != 256) return hipErrorInvalidValue;   // 64, 128: the 256-key dK/dV kernel
+  if (p.mask.mask)
+    hipLaunchKernelGGL((bwd_main_kernel<256, true>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_main_kernel<256, false>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -24,6 +24,24 @@
 // With DS set the kernel also stores every dS it forms (bf16, the values its
 // dK^T product uses) for the dQ kernel of bwd_dq_ds.hip, which then runs
 // dQ = alpha dS K as its only GEMM instead of recomputing S and dP.
+//
+// With DQ set (the fused design, head_dim 64 and 128) the kernel runs the
+// fifth GEMM itself, dQ += dS K over all 256 keys of the workgroup, and adds
+// the result to the fp32 dQ accumulator once per step: one global reduction
+// per 256 keys, where a 128-key workgroup would need two (blog page, 2-CTA
+// backward section: dQ as an (M/2, 2N) x (2N, d) product halves the global
+// atomic reductions; here one workgroup covers the 2N keys, so no exchange
+// between workgroups is needed). Each wave writes its bf16 dS fragments
+// into an LDS image in the stored-dS sub-tile layout (two buffers, by step
+// parity); after the mid-step barrier wave w forms one 32 x 32 unit of dQ
+// (queries x dims) from that image and a row-major K tile held in LDS for
+// the whole work tile, both read with transposing reads, interleaved with
+// its dK^T MFMAs, then adds it with 16 coalesced fp32 buffer atomics. DQ = 2
+// is the deterministic mode (blog page, deterministic-mode section): the key
+// blocks of a (query block, query head) add in a fixed order, the last key
+// block first; a wavefront waits until every wavefront of the earlier key
+// blocks has counted its adds done in the pair's semaphore, and counts its
+// own after the next mid-step wait has seen them complete.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "schedule.hpp"
@@ -32,14 +50,22 @@ namespace attn71 {
 
 namespace {
 
-// LDS of one workgroup: [NS] Q tiles | [NS] dO tiles | [NS][LSE BM | D BM] fp32
+// LDS of one workgroup: [NS] Q tiles | [NS] dO tiles | [NS][LSE BM | D BM] fp32,
+// and with DQ (from a 1 KiB boundary) the K tile | [2] dS images
 template <int D, int BM>
-constexpr int dkdv_smem_bytes() { return 2 * 3 * BM * 2 * D + 3 * 2 * BM * 4; }
+constexpr int dkdv_ring_bytes() { return 2 * 3 * BM * 2 * D + 3 * 2 * BM * 4; }
+template <int D, int BM, int DQ>
+constexpr int dkdv_smem_bytes() {
+  return DQ ? (dkdv_ring_bytes<D, BM>() + 1023) / 1024 * 1024 + DkdvCfg<D>::BN * 2 * D +
+                  2 * BM * DkdvCfg<D>::BN * 2
+            : dkdv_ring_bytes<D, BM>();
+}
 
 // One tile: the keys of key block t.block of (sequence t.seq, KV head t.head).
-template <int D, int KB, int BM, bool DS, bool MASK>
+template <int D, int KB, int BM, bool DS, bool MASK, int DQ>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, char* smem) {
   static_assert(!(DS && MASK), "block masks run with the recomputing dQ kernel");
+  static_assert(!(DS && DQ), "stored dS feeds the dQ kernel; DQ forms dQ here");
   constexpr int NW = 4, NT = NW * 64;
   constexpr int KPW = 32 * KB;          // keys per wave
   constexpr int BN = NW * KPW;          // keys per workgroup
@@ -56,10 +82,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   static_assert(TILE % (16 * NT) == 0 && NLD <= NW, "tile split over the workgroup");
   constexpr int OPS = 2 * CH;           // dma per step by waves >= NLD (one more below)
   static_assert(OPS + 1 < 64, "vmcnt range");
-  static_assert(dkdv_smem_bytes<D, BM>() == 2 * NS * TILE + NS * 2 * BM * 4, "LDS layout");
+  static_assert(dkdv_ring_bytes<D, BM>() == 2 * NS * TILE + NS * 2 * BM * 4, "LDS layout");
   char* const qtile = smem;
-  char* const otile = smem + NS * TILE;
   float* const lsed = reinterpret_cast<float*>(smem + 2 * NS * TILE);
+  // DQ: K tile (BN rows of RB bytes, row swizzle dma_swz) and two dS images
+  // of BM x BN bf16: per 32-query block qb, 8 sub-tiles of 32 keys (2 KiB,
+  // the stored-dS sub-tile layout) in key order
+  constexpr int NKC = BN / 32;          // 32-key sub-columns of the workgroup
+  constexpr int KT = BN * RB;           // bytes of the K tile
+  constexpr int DSB = BM * BN * 2;      // bytes of one dS image
+  constexpr int RING = (dkdv_ring_bytes<D, BM>() + 1023) / 1024 * 1024;
+  constexpr int NJQ = BN / 16;          // k-steps of the dQ product
+  static_assert(!DQ || (dkdv_smem_bytes<D, BM, DQ>() == RING + KT + 2 * DSB &&
+                        NQB * NDB == NW && KT % (16 * NT) == 0),
+                "LDS layout; one 32 x 32 dQ unit per wavefront");
   static_assert(BN == DkdvCfg<D>::BN && BM == DkdvCfg<D>::BM, "host and kernel tiling agree");
 
   int64_t qs, ks0;
@@ -199,6 +235,21 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     }
     if (++i_m == nm) { i_m = m_first; ++i_h; }
   };
+  // DQ: the dQ adds of a step go out at its end, after the loads of step + 2,
+  // and stay in flight through the next step: vector memory operations
+  // retire in issue order, so the mid-step wait for the loads of step + 1
+  // leaves the last NAT (the previous step's adds) outstanding.
+  constexpr int NAT = DQ ? 16 : 0;
+  // DQ = 2: the step's semaphore, the count its turn needs and a snapshot of
+  // it read before the previous step's adds (complete at the mid-step wait);
+  // the semaphores of the two steps before, whose adds are counted once the
+  // wait has retired them (rel_a: adds two steps old, complete at that wait).
+  int* sem_cur = nullptr;
+  int sem_need = 0, sem_seen = 0;
+  int* rel_a = nullptr;
+  int* rel_b = nullptr;
+  int64_t mb0 = 0;
+  if constexpr (DQ == 2) mb0 = p.sv.cu_q ? (int64_t)p.mb_prefix[t.seq] : (int64_t)t.seq * p.nm;
   // Ring order. Step s reads slot s % NS. Between its dV^T and dK^T phases
   // every wave waits for its own loads of step s + 1 (the only ones in flight
   // then) and meets the others at a barrier: after it, slot (s + 1) % NS is
@@ -207,8 +258,34 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // barrier sits under a queue of dK^T MFMAs instead of in front of the next
   // step, and the next step's first fragments are read before that step begins.
   auto mid = [&]() {
-    wait_vm<0>();
+    wait_vm<NAT>();
+    if constexpr (DQ) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // dS image written
     __builtin_amdgcn_s_barrier();
+    if constexpr (DQ == 2) {
+      // The adds of two steps back have completed (the wait above retired
+      // everything but the previous step's adds: the L2 has acknowledged
+      // them), so counting them needs no cache fence: no value of the
+      // accumulator is read inside the kernel, and a later key block issues
+      // its adds only after it has seen the count.
+      if (rel_a && lane == 0)
+        __hip_atomic_fetch_add(rel_a, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      rel_a = rel_b;
+      // this step's turn: every wavefront of the earlier key blocks counted
+      int v = __builtin_amdgcn_readfirstlane(sem_seen), it = 0;
+      while (v < sem_need) {
+        if (++it > p.spin_limit) {   // bounded: report and stop waiting
+          if (lane == 0) atomicOr(p.status, 1);
+          break;
+        }
+        if ((it & 255) == 0 && __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                                   p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+          break;
+        __builtin_amdgcn_s_sleep(2);
+        v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(sem_cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+      rel_b = sem_cur;
+    }
   };
 
   // per-lane LDS addresses (byte offsets; see dma_swz)
@@ -246,6 +323,44 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   };
   static_assert(TILE % 8192 == 0 || TILE >= 2 * RB * 32, "slot offsets clear the XOR bits");
 
+  // ---- DQ: the K tile (once per work tile; keys past the sequence read as
+  // zero) and the per-lane addresses of the dQ product. Wave w owns dQ unit
+  // (query block qb_w, dims 32 db_w .. +31) of every step.
+  const int qb_w = DQ ? w / NDB : 0, db_w = DQ ? w % NDB : 0;
+  const uint32_t lds_k = lds_q + RING, lds_s = lds_k + KT;
+  if constexpr (DQ) {
+    const rsrc_t ktr = make_rsrc(static_cast<const bf16*>(p.k) + (ks0 + n0) * kstride + (int64_t)kvh * D,
+                                 ((int64_t)(lk - n0 - 1) * kstride + D) * 2);
+#pragma unroll
+    for (int i = 0; i < KT / (16 * NT); ++i) {
+      const int base = (i * NW + w) * 64;
+      const int slot = base + lane;
+      const int r = slot / SPR, pos = slot % SPR;
+      dma16(ktr, lds_k + base * 16, (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2);
+    }
+  }
+  // Per-lane addresses of the dQ path, recomputed where they are used from
+  // an opaque lane id (kept live across the step they would cost VGPRs the
+  // dP and dV^T phases need). dS image writes: this wave's sub-columns
+  // w KB .. w KB + KB - 1, lane slot L ^ 4 (L >= 32) as in the stored layout.
+  auto dq_write_addr = [&](uint32_t par) -> uint32_t {
+    const int ln = opaque_lane_id();
+    return lds_s + par + w * KB * 2048 + ((ln ^ ((ln >> 5) << 2)) << 4);
+  };
+  // dS as the A operand (query on the lane, keys 4g + j and 8 + 4g + j of a
+  // 16-key step): the transposing read of the stored sub-tiles; K as the B
+  // operand (dim on the lane, the same keys): transposing reads of the
+  // row-major K tile, as for Q^T above.
+  auto dq_read_addr = [&](uint32_t par, uint32_t& ra, uint32_t& k0, uint32_t& k1) {
+    const int ln = opaque_lane_id();
+    const int l16 = ln & 15, lh = (ln >> 4) & 1, lg = ln >> 5, sl = l16 & 1;
+    ra = lds_s + par + qb_w * NKC * 2048 + lh * 1024 +
+         (32 * sl + ((4 * lg + (l16 >> 2)) ^ (4 * sl))) * 16 + ((l16 >> 1) & 1) * 8;
+    const int lr = 4 * lg + (l16 >> 2), lc = 2 * lh + ((l16 & 3) >> 1);
+    const int lt = lr * RB + 16 * (lc ^ dma_swz<D>(lr)) + 8 * (l16 & 1);
+    k0 = lds_k + (lt ^ (64 * db_w));
+    k1 = lds_k + (lt ^ (64 * db_w + 32)) + 8 * RB;
+  };
   // Fragment j (0 or 1) of a step, the Q operands of its first S MFMAs, from
   // the slot at byte offset nxt from the current one.
   auto fetch_first = [&](int j, int nxt) -> bf16x8 {
@@ -264,9 +379,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // the previous step), of the next step (slot offset nxt) on return.
   // has_next: a later step exists (mid-step sync); iss >= 0: the ring slot the
   // loads of step + 2 go to.
+  // par: byte offset of this step's dS image (DQ); dqa: its dQ unit.
   auto step_body = [&](int mq0, bool need_mask, bool hid, bf16x8& f0, bf16x8& f1, bool has_next,
-                       int iss, int nxt) {
+                       int iss, int nxt, uint32_t par, f32x16& dqa) {
     constexpr int OT = NS * TILE;   // dO tile offset from the Q tile
+    uint32_t dsw = 0, dsr = 0, dk0 = 0, dk1 = 0;   // DQ: dS image and K tile addresses
     int rel[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -351,14 +468,35 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
         for (int k2 = 0; k2 < KB; ++k2) {
           sb[qb][k2][j >> 1] = pack_half(dp[qb][k2], j >> 1);
           pin8(sb[qb][k2][j >> 1]);
+          if constexpr (DQ)
+            lds_st16(dsw + qb * NKC * 2048 + k2 * 2048 + (j >> 1) * 1024, sb[qb][k2][j >> 1]);
         }
       }
+    };
+    // DQ: operands of dQ k-step jq (keys 16 jq .. +15), read two steps ahead
+    constexpr int NQ = NJQ / NG2;                  // dQ MFMAs per dK^T fragment
+    static_assert(!DQ || NQ * NG2 == NJQ, "even dQ slices");
+    bf16x8 qa[3], qk[3];
+    auto dq_fetch = [&](int jq) {
+      const int kc = jq >> 1, tt = jq & 1;
+      const uint32_t so = kc * 2048 + 256 * tt, ko = (kc * 32 + 16 * tt) * RB;
+      qa[jq % 3] = cat8(ds_read_tr(dsr + so), ds_read_tr(dsr + so + 128));
+      qk[jq % 3] = cat8(ds_read_tr(dk0 + ko), ds_read_tr(dk1 + ko));
     };
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if (f == 2 * NG1 + NG2) {                       // dV^T done: sync for step + 1
         mid();
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DQ) {
+          dq_read_addr(par, dsr, dk0, dk1);
+          dq_fetch(0);
+          dq_fetch(1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (DQ) {
+        if (f == 2 * NG1) dsw = dq_write_addr(par);   // dV^T phase: the dS image writes begin
       }
       const bf16x8 cur = f0;
       f0 = f1;
@@ -404,6 +542,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mfma32_agpr<false>(dk[kb][db], cur, sb[qb][kb][tt]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DQ) {   // dQ unit += dS (32 queries x 16 keys) K (16 keys x 32 dims)
+#pragma unroll
+          for (int e = 0; e < NQ; ++e) {
+            const int jq = x * NQ + e;
+            dqa = mfma32(qa[jq % 3], qk[jq % 3], jq == 0 ? f32x16{} : dqa);
+            if (jq + 2 < NJQ) dq_fetch(jq + 2);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (DS) {
           if (db == NDB - 1) {   // last read of sb[qb][*][tt]: store it (waited for a step later)
             const rsrc_t dr = raw_rsrc(ds_col, ds_rng);
@@ -426,6 +573,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     }
   };
 
+  // DQ = 2: semaphore and needed count of the step at query block mq0, head
+  // kvh0 + hh (the key blocks of the pair add from the last one down)
+  auto chain_pos = [&](int mq0, int hh) {
+    const int nkb = cdiv(lk, BN);
+    const int nlast = causal ? imin(nkb - 1, (mq0 + BM - 1 + shift) / BN) : nkb - 1;
+    sem_need = 4 * (nlast - t.block);
+    sem_cur = p.sem + (mb0 + mq0 / BM) * p.hq + (kvh0 + hh);
+    sem_seen = __hip_atomic_load(sem_cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
   // ---- prologue: fill NS - 1 ring slots. The full wait also retires the K / V
   // fragment loads: the compiler then knows them complete and places no wait
   // of its own inside the loop (where the outstanding ring loads, which it
@@ -433,14 +590,19 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < n_steps) issue(s);
+  if constexpr (DQ == 2) {
+    if (n_steps > 0) chain_pos(m_first * BM, 0);   // step 0's snapshot, retired below
+  }
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
 
   int st = 0;   // ring slot of the step being computed (step % NS)
   int c_h = 0;  // query head of the compute cursor, from kvh0
   bf16x8 f0 = fetch_first(0, 0), f1 = fetch_first(1, 0);
+  f32x16 dqa;   // DQ: this wave's dQ unit of the step (formed from zero each step)
   for (int step = 0; step < n_steps; ++step) {
     const int mq0 = c_m * BM;
+    const int h_step = c_h;
     const bool wrap = ++c_m == nm;
     if (wrap) c_m = m_first;
     // a cleared mask block hides every pair of this wave's step (P = 0)
@@ -456,7 +618,27 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     // the mid-step barrier, and the register allocator answers such a split
     // of the AGPR accumulators with spills.
     const bool need_mask = hid || (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
-    step_body(mq0, need_mask, hid, f0, f1, has_next, iss, nxt);
+    const uint32_t par = (step & 1) * DSB;   // DQ: dS image of this step
+    step_body(mq0, need_mask, hid, f0, f1, has_next, iss, nxt, par, dqa);
+    if constexpr (DQ) {
+      // rows mq0 + 32 qb_w + 8 (r / 4) + 4 g + r % 4 (register r), dims
+      // 32 db_w + c; rows past the sequence fall outside the buffer range
+      const int r0 = mq0 + 32 * qb_w;
+      const int hh = kvh0 + h_step;
+      // the next step's snapshot goes out before these adds (c_m, c_h: the next step)
+      if constexpr (DQ == 2) {
+        if (has_next) chain_pos(c_m * BM, c_h);
+      }
+      const rsrc_t ar = raw_rsrc(p.dq_acc + ((qs + r0) * qstride + (int64_t)hh * D + 32 * db_w),
+                                 clamp_range(((int64_t)(lq - r0 - 1) * qstride + 32) * 4));
+      const int qs4 = (int)qstride * 4;
+      const int ln = opaque_lane_id();
+      const int dq_lane = ((ln >> 5) * 4 * qs4) + (ln & 31) * 4;   // fp32 offset of (row 4g, dim c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dqa[r], ar,
+                                                        dq_lane + (8 * (r >> 2) + (r & 3)) * qs4, 0, 0);
+    }
     if constexpr (DS) {   // the compute cursor's next sub-rows
       if (wrap) {
         ds_col = keep_sgpr(ds_col + ds_reg);
@@ -467,6 +649,14 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
     }
     advance_slot(st);
     st = st == NS - 1 ? 0 : st + 1;
+  }
+
+  if constexpr (DQ == 2) {   // count the last two steps' adds once they have completed
+    wait_vm<0>();
+    if (rel_a && lane == 0) __hip_atomic_fetch_add(rel_a, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (rel_b) {
+      if (lane == 0) __hip_atomic_fetch_add(rel_b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // ---- dK = alpha dK^T, dV = dV^T for this wave's keys
@@ -499,9 +689,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
 
 // Persistent workgroups walk the tiles (schedule.hpp: persistent_index); a
 // one-shot grid (gridDim.x == ntiles) gives each workgroup one tile.
-template <int D, int KB, int BM, bool DS, bool MASK>
+template <int D, int KB, int BM, bool DS, bool MASK, int DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
-  __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM>()];
+  __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM, DQ>()];
   __shared__ int ticket;
   for (int r = 0;; ++r) {
     const BwdParams& p = kernel_args<BwdParams>();
@@ -509,36 +699,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
     if (i < 0) break;
     Tile t;
     if (p.sv.cu_q) {
-      t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/false);
+      // deterministic: shortest first, the order of the chain's turns
+      t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/DQ == 2);
       if (t.seq < 0) {
         if (p.queue) continue;   // a ticket past the last real tile
         break;
       }
     } else {
-      t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, false, p.nxcd, p.natural != 0);
+      t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, DQ == 2, p.nxcd, p.natural != 0);
     }
-    dkdv_tile<D, KB, BM, DS, MASK>(p, t, smem);
+    dkdv_tile<D, KB, BM, DS, MASK, DQ>(p, t, smem);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }
 
-template <int D, bool DS, bool MASK>
+template <int D, bool DS, bool MASK, int DQ>
 hipError_t launch_dkdv_t(const BwdParams& p, int cus, hipStream_t stream) {
   using C = DkdvCfg<D>;
-  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM, DS, MASK>, 256);
+  static const int occ = resident_per_cu(bwd_dkdv_kernel<D, C::KB, C::BM, DS, MASK, DQ>, 256);
   const int grid = persistent_grid(p.ntiles, cus * occ, p.nxcd);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM, DS, MASK>), dim3(grid), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::KB, C::BM, DS, MASK, DQ>), dim3(grid), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
+template <int D, int DQ>
+hipError_t launch_dkdv_q(const BwdParams& p, int cus, hipStream_t stream) {
+  return p.mask.mask ? launch_dkdv_t<D, false, true, DQ>(p, cus, stream)
+                     : launch_dkdv_t<D, false, false, DQ>(p, cus, stream);
+}
 template <int D>
 hipError_t launch_dkdv_d(const BwdParams& p, int cus, hipStream_t stream) {
-  if (p.mask.mask) {
-    if (p.ds) return hipErrorInvalidValue;   // the host never combines the two
-    return launch_dkdv_t<D, false, true>(p, cus, stream);
+  // the host never combines stored dS with a block mask or the fused dQ
+  if (p.ds && (p.mask.mask || p.dq_mode)) return hipErrorInvalidValue;
+  if constexpr (D <= 128) {
+    if (p.dq_mode == 1) return launch_dkdv_q<D, 1>(p, cus, stream);
+    if (p.dq_mode == 2) {
+      if (!p.queue) return hipErrorInvalidValue;   // the chain needs tickets in turn order
+      return launch_dkdv_q<D, 2>(p, cus, stream);
+    }
+  } else {
+    if (p.dq_mode) return hipErrorInvalidValue;
   }
-  return p.ds ? launch_dkdv_t<D, true, false>(p, cus, stream)
-              : launch_dkdv_t<D, false, false>(p, cus, stream);
+  if (p.ds) return launch_dkdv_t<D, true, false, 0>(p, cus, stream);
+  return launch_dkdv_q<D, 0>(p, cus, stream);
 }
 
 }  // namespace

@@ -396,6 +396,9 @@ __device__ __forceinline__ bf16x8 lds_ld16(uint32_t lds_byte) {
 __device__ __forceinline__ f32x4 lds_ldf4(uint32_t lds_byte) {
   return *(const lds_f32x4*)(lds_byte);
 }
+__device__ __forceinline__ void lds_st16(uint32_t lds_byte, const bf16x8& x) {
+  *(lds_bf16x8*)(lds_byte) = x;
+}
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_char*)(p);

@@ -103,6 +103,10 @@ struct BwdParams {
                              // sequence whose regions do not fit the area (its
                              // stores are dropped); null: fixed length
   int64_t ds_bytes;          // size of the dS area
+  // dQ inside the 256-key dK/dV kernel (fused design): 0 off, 1 fp32 atomics
+  // into dq_acc, 2 the same in the deterministic order (sem, in turns of
+  // four wavefront adds per key block)
+  int dq_mode;
 };
 
 // Stored-dS layout of one (sequence, query head) with lq queries and lk
@@ -212,8 +216,15 @@ inline int dkdv_block_n(int d) { return d <= 128 ? DkdvCfg<128>::BN : DkdvCfg<25
 inline int fwd_block_m(int d) {
   return d == 64 ? FwdCfg<64>::BM : d == 128 ? FwdCfg<128>::BM : FwdCfg<256>::BM;
 }
-inline int bwd_block_n(int) { return 128; }
-inline int bwd_block_m(int d) { return d <= 128 ? 64 : 32; }
+// The fused design (dQ reduced across key blocks by atomics or the
+// deterministic chain): at head_dim 64 and 128 inside the 256-key dK/dV
+// kernel (one global reduction per 256 keys); at 256, whose Q / dO ring
+// leaves no LDS for the K tile, in the 128-key kernel of bwd.hip.
+inline bool fused_in_dkdv(int d) { return d <= 128; }
+inline int fused_block_n(int d) { return fused_in_dkdv(d) ? dkdv_block_n(d) : BwdCfg<256>::BN; }
+inline int fused_block_m(int d) {
+  return d == 64 ? DkdvCfg<64>::BM : d == 128 ? DkdvCfg<128>::BM : BwdCfg<256>::BM;
+}
 
 // Workgroups of `kernel` (block of `threads`) that fit on one CU at once.
 template <typename K>
@@ -236,10 +247,11 @@ inline int persistent_grid(int ntiles, int resident, int nx) {
 // a one-shot grid of one workgroup per tile (p.ntiles).
 hipError_t launch_fwd(const FwdParams& p, int d, int cus, int exp_emulation, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
-// fused = true: dQ accumulated with fp32 atomics (or the deterministic
-// semaphore chain) inside the dK/dV kernel; false: dK/dV only.
-hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, bool fused, hipStream_t stream);
-// dK, dV only: one workgroup per DkdvCfg<d>::BN keys (see bwd_dkdv.hip).
+// Fused design at head_dim 256: dK, dV and the dQ atomics (or the
+// deterministic chain) in one 128-key kernel; one workgroup per tile.
+hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stream);
+// dK, dV: one workgroup per DkdvCfg<d>::BN keys (see bwd_dkdv.hip); with
+// p.dq_mode set (head_dim 64, 128) also dQ into p.dq_acc.
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int cus, hipStream_t stream);
 // dQ without atomics: one workgroup per query block (see bwd_dq.hip).
 hipError_t launch_bwd_dq(const BwdParams& p, int d, int cus, hipStream_t stream);

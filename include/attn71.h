@@ -88,9 +88,13 @@ typedef enum attn_status {
  *                        needs the dS area to fit opt.ds_budget
  *                        (ATTN_ERR_UNSUPPORTED otherwise);
  *   ATTN_BWD_FUSED_DQ    one key-block kernel for all five GEMMs that adds
- *                        each tile's dQ into an fp32 buffer with atomics, or,
- *                        with deterministic = 1, in a fixed order behind
- *                        per-block semaphores; a postprocess converts dQ. */
+ *                        each step's dQ into an fp32 buffer with atomics
+ *                        (head_dim 64, 128: once per 256 keys; 256: once per
+ *                        128), or, with deterministic = 1, in a fixed order
+ *                        (the last key block first) behind per-(query block,
+ *                        query head) semaphores; a postprocess converts dQ.
+ *                        Bound by the device's fp32 atomic rate, 2 bytes of
+ *                        adds per visible (query, key) pair at head_dim 128. */
 #define ATTN_BWD_AUTO 0
 #define ATTN_BWD_RECOMPUTE 1
 #define ATTN_BWD_STORED_DS 2
@@ -306,8 +310,9 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* wo
  * of the blog page: longest first, L2-sized batch-head sections; here also
  * one contiguous range per XCD). which = 0: forward, out[3*i..3*i+2] = (batch, query head,
  * query block) of workgroup i; which = 1: dK/dV (or fused) backward,
- * which = 2: fused deterministic backward in ticket order, (batch, KV head,
- * key block); which = 3: dQ kernel, (batch, query head, query block).
+ * which = 2: fused deterministic backward in ticket order (key blocks of
+ * 256 at head_dim 64 and 128, 128 at 256), (batch, KV head, key block);
+ * which = 3: dQ kernel, (batch, query head, query block).
  * *count receives the grid size; at most `capacity` triples are written.
  * No GPU is needed. */
 attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,

@@ -204,7 +204,8 @@ def test_backward_tile_orders(b, s, hq, hkv, d):
     lpt = ea.tile_order(p, 1)
     assert sorted(lpt) == sorted((bb, h, n) for bb in range(b) for h in range(hkv)
                                  for n in range(nn_dkdv))
-    nn = -(-s // 128)
+    # the fused design: 256-key blocks at head_dim 64 and 128 (the dK/dV kernel), 128 at 256
+    nn = nn_dkdv
     full = sorted((bb, h, n) for bb in range(b) for h in range(hkv) for n in range(nn))
     det = ea.tile_order(p, 2)
     assert sorted(det) == full
