@@ -350,7 +350,9 @@ def measure(torch, ea, w, args, opts, cpu_budget: float) -> dict:
     fused = r.design == ea.BWD_FUSED_DQ
     stored = r.design == ea.BWD_STORED_DS
     names = {"fwd": f"fwd_kernel<{w.head_dim}>",
-             "bwd_main": f"{'bwd_main' if fused else 'bwd_dkdv'}_kernel<{w.head_dim}>",
+             # the fused design runs in the dK/dV kernel at head_dim 64 and 128
+             "bwd_main": f"{'bwd_main' if fused and w.head_dim > 128 else 'bwd_dkdv'}"
+                         f"_kernel<{w.head_dim}>",
              "bwd_dq": f"bwd_dq_{'ds_' if stored else ''}kernel<{w.head_dim}>",
              "bwd_pre": "bwd_pre_kernel", "bwd_post": "bwd_post_kernel"}
     half = fl["fwd"] / 2.0
@@ -402,7 +404,10 @@ def ablations(torch, ea, args) -> dict:
         inp = make_inputs(2, 8192, 8192, 16, hkv, 128, seed=71003, device="cuda:0")
         fl = workload_flops(w)
         res = {}
-        for name, opts in (("lpt", {}), ("natural", {"tile_order": 1})):
+        cases = [("lpt", {}), ("natural", {"tile_order": 1})]
+        if hkv == 1:   # 64 key-block tiles: the automatic head split against none
+            cases.append(("lpt_no_head_split", {"head_split": 1}))
+        for name, opts in cases:
             r = Runner(torch, ea, w, opts, inputs=inp)
             ms, kms = r.timed_steps(args.warmup, args.steps)
             bms = sum(kms.get(n, 0.0) for n in ("bwd_pre", "bwd_main", "bwd_dq", "bwd_post"))
@@ -411,6 +416,11 @@ def ablations(torch, ea, args) -> dict:
             del r
         res["fwd_gain"] = round(res["lpt"]["fwd_tflops"] / res["natural"]["fwd_tflops"] - 1, 4)
         res["bwd_gain"] = round(res["lpt"]["bwd_tflops"] / res["natural"]["bwd_tflops"] - 1, 4)
+        if hkv == 1:
+            p = ea.make_params(2, 8192, 8192, 16, hkv, 128, 1 / 128 ** 0.5, True)
+            res["head_split"] = ea.bwd_head_split(p)
+            res["head_split_bwd_gain"] = round(res["lpt"]["bwd_tflops"]
+                                               / res["lpt_no_head_split"]["bwd_tflops"] - 1, 4)
         out[f"lpt_causal_{tag}"] = dict(res, workload=f"B2 Hq16 Hkv{hkv} S8192 d128 causal")
         print(f"[bench] ablation lpt {tag}: {out[f'lpt_causal_{tag}']}", file=sys.stderr, flush=True)
         del inp

@@ -49,7 +49,8 @@ class AttnOptions(ctypes.Structure):
     _fields_ = [("bwd_design", ctypes.c_int32), ("tile_order", ctypes.c_int32),
                 ("one_shot_grid", ctypes.c_int32), ("exp_emulation", ctypes.c_int32),
                 ("tau", ctypes.c_float), ("spin_limit", ctypes.c_int32),
-                ("ds_budget", ctypes.c_int64)]
+                ("ds_budget", ctypes.c_int64), ("head_split", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class AttnVarlenPlan(ctypes.Structure):
@@ -93,7 +94,8 @@ EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
            "attn_persistent_tile", "attn_bwd_design", "attn_bwd_noalloc",
-           "attn_bwd_ds_subtile", "attn_varlen_plan_size", "attn_varlen_plan_build"]
+           "attn_bwd_ds_subtile", "attn_varlen_plan_size", "attn_varlen_plan_build",
+           "attn_bwd_head_split"]
 
 
 def _lib():
@@ -121,6 +123,8 @@ def _lib():
     lib.attn_persistent_tile.argtypes = [ctypes.c_int32] * 5
     lib.attn_persistent_tile.restype = ctypes.c_int32
     lib.attn_bwd_design.argtypes = [_P, ctypes.c_int32]
+    lib.attn_bwd_head_split.argtypes = [_P, ctypes.c_int32]
+    lib.attn_bwd_head_split.restype = ctypes.c_int32
     lib.attn_varlen_plan_size.argtypes = [_P]
     lib.attn_varlen_plan_size.restype = ctypes.c_size_t
     lib.attn_varlen_plan_build.argtypes = [_P, _vp, _vp, _vp, ctypes.c_size_t,
@@ -253,6 +257,12 @@ def bwd_design(p: AttnParams, varlen: bool = False) -> int:
     """BWD_RECOMPUTE, BWD_STORED_DS or BWD_FUSED_DQ: the design a backward call
     with these parameters runs; -1: parameters the calls would reject."""
     return _lib().attn_bwd_design(ctypes.byref(p), int(varlen))
+
+
+def bwd_head_split(p: AttnParams, varlen: bool = False) -> int:
+    """Query-head parts per KV group of the backward's key-block kernel
+    (1: unsplit); -1: parameters the calls would reject."""
+    return _lib().attn_bwd_head_split(ctypes.byref(p), int(varlen))
 
 
 # --------------------------------------------------------------------- forward

@@ -92,6 +92,10 @@ attn_status check_params(const attn_params* p, bool varlen) {
   if (!(o.tau == 0.0f || o.tau == -1.0f || (o.tau > 0.0f && o.tau <= 64.0f)))
     return ATTN_ERR_INVALID_ARGUMENT;
   if (o.spin_limit < 0 || o.ds_budget < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (o.reserved != 0 || o.head_split < 0 ||
+      (o.head_split > 1 && ((p->num_heads_q / p->num_heads_kv) % o.head_split != 0 ||
+                            (o.bwd_design == ATTN_BWD_FUSED_DQ && !fused_in_dkdv(p->head_dim)))))
+    return ATTN_ERR_INVALID_ARGUMENT;
   if (p->block_mask) {
     if (p->block_mask_stride_b < 0 || p->block_mask_stride_h < 0 ||
         (reinterpret_cast<uintptr_t>(p->block_mask) & 3u))
@@ -156,7 +160,8 @@ PlanMap plan_map(const attn_params* p) {
 }
 
 struct BwdWs {
-  size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, ds = 0;
+  size_t dsum = 0, lse2 = 0, dq_acc = 0, sem = 0, misc = 0, ds = 0, part = 0;
+  int split = 1;          // query-head parts per KV group (dK / dV partials when > 1)
   SetMap main, dq;        // varlen tables of the key-block and dQ kernels (no plan)
   bool tables = false;
   size_t total = 0;
@@ -197,6 +202,34 @@ int64_t bwd_mblocks(const attn_params* p, bool varlen) {
   return varlen ? (int64_t)cdiv(p->total_q, bm) + p->batch
                 : (int64_t)p->batch * cdiv(p->seqlen_q, bm);
 }
+// Key-block tiles of the backward before any head split: (sequence, KV
+// head, block of fused_block_n or dkdv_block_n keys); for packed lengths the
+// bound from the totals.
+int bwd_base_tiles(const attn_params* p, bool varlen, bool fused) {
+  const int bn = fused ? fused_block_n(p->head_dim) : dkdv_block_n(p->head_dim);
+  if (varlen) return (cdiv(p->total_k, bn) + p->batch) * p->num_heads_kv;
+  return p->batch * p->num_heads_kv * cdiv(p->seqlen_k, bn);
+}
+// Query-head parts per KV group (opt.head_split; automatic: the largest
+// divisor of the group that keeps the tiles within ATTN_SPLIT_TARGET, when the
+// unsplit tiles fall below it). The 128-key fused kernel (head_dim 256)
+// walks whole groups.
+int head_split_of(const attn_params* p, bool varlen, int design) {
+  const int group = p->num_heads_q / p->num_heads_kv;
+  const bool fused = design == ATTN_BWD_FUSED_DQ;
+  if (fused && !fused_in_dkdv(p->head_dim)) return 1;
+  const int req = p->opt.head_split;
+  if (req >= 1) return req;
+  const int64_t base = bwd_base_tiles(p, varlen, fused);
+  int s = 1;
+  for (int c = 2; c <= group; ++c)
+    if (group % c == 0 && base * c <= ATTN_SPLIT_TARGET) s = c;
+  return s;
+}
+int64_t rows_k_of(const attn_params* p, bool varlen) {
+  return varlen ? p->total_k : (int64_t)p->batch * p->seqlen_k;
+}
+
 // Workspace regions (256-byte aligned): -D and LSE log2 e per (row, query
 // head); the fp32 dQ accumulator and the semaphores only for the fused
 // design; ticket / status / tile counters; the varlen schedule tables; the
@@ -214,6 +247,12 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
   w.n_sem = fused && p->deterministic ? bwd_mblocks(p, varlen) * p->num_heads_q : 0;
   w.sem = off; off = align_up(off + sizeof(int) * (size_t)w.n_sem);
   w.misc = off; off = align_up(off + 64);
+  w.split = w.design < 0 ? 1 : head_split_of(p, varlen, w.design);
+  if (w.split > 1) {   // fp32 dK and dV partials, [part][row][KV head][d] each
+    w.part = off;
+    off = align_up(off + 2 * sizeof(float) * (size_t)w.split *
+                             (size_t)(rows_k_of(p, varlen) * p->num_heads_kv * p->head_dim));
+  }
   if (varlen && !p->varlen_plan && w.design > 0) {
     w.tables = true;
     off = map_set(off, p->batch, main_kind(w.design), &w.main);
@@ -244,10 +283,8 @@ int dq_grid(const attn_params* p, bool varlen) {
   if (varlen) return (cdiv(p->total_q, bm) + p->batch) * p->num_heads_q;
   return p->batch * p->num_heads_q * cdiv(p->seqlen_q, bm);
 }
-int bwd_grid(const attn_params* p, bool varlen, bool fused) {
-  const int bn = fused ? fused_block_n(p->head_dim) : dkdv_block_n(p->head_dim);
-  if (varlen) return (cdiv(p->total_k, bn) + p->batch) * p->num_heads_kv;
-  return p->batch * p->num_heads_kv * cdiv(p->seqlen_k, bn);
+int bwd_grid(const attn_params* p, bool varlen, bool fused, int split) {
+  return bwd_base_tiles(p, varlen, fused) * split;
 }
 
 // ----------------------------------------------------------------- device
@@ -447,10 +484,11 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   const int bn = fused ? fused_block_n(d) : dkdv_block_n(d), bm = fused_block_m(d);
   bp.nn = cdiv(p->seqlen_k, bn);
   bp.nm = cdiv(p->seqlen_q, bm);
-  bp.sec = section_width(2ll * bp.group * p->seqlen_q * d * 2);
+  bp.hsplit = wl.split;
+  bp.sec = section_width(2ll * (bp.group / wl.split) * p->seqlen_q * d * 2);
   bp.nxcd = kNxcd;
   bp.natural = op.natural ? 1 : 0;
-  bp.ntiles = bwd_grid(p, varlen, fused);
+  bp.ntiles = bwd_grid(p, varlen, fused, wl.split);
   bp.ntiles_dq = dq_grid(p, varlen);
   bp.causal = p->causal;
   bp.deterministic = p->deterministic;
@@ -461,6 +499,11 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   bp.zero_acc = fused ? 1 : 0;
   bp.spin_limit = op.spin_limit;
   bp.mask = mask_view(p);
+  if (wl.split > 1) {
+    bp.dk_part = reinterpret_cast<float*>(base + wl.part);
+    bp.dv_part = bp.dk_part + (size_t)wl.split * rows_k_of(p, varlen) * p->num_heads_kv * d;
+    bp.rows_k = rows_k_of(p, varlen);
+  }
   // fused design at head_dim 64 / 128: dQ inside the 256-key dK/dV kernel
   const bool fused_dkdv = fused && fused_in_dkdv(d);
   bp.dq_mode = fused_dkdv ? (p->deterministic ? 2 : 1) : 0;
@@ -517,6 +560,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     const hipError_t e = fused && !fused_dkdv ? launch_bwd_main(bp, d, bp.ntiles, stream)
                                               : launch_bwd_dkdv(bp, d, pcus, stream);
     if (e != hipSuccess) return ATTN_ERR_HIP;
+    if (wl.split > 1 && launch_bwd_dkdv_reduce(bp, d, stream) != hipSuccess) return ATTN_ERR_HIP;
   }
   if (dqk) {
     const hipError_t e = use_ds ? launch_bwd_dq_ds(bp, d, pcus, stream)
@@ -652,6 +696,9 @@ attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k,
     return ATTN_ERR_UNSUPPORTED;
   attn_params pr = *p;
   pr.opt.bwd_design = ATTN_BWD_RECOMPUTE;
+  // an automatic head split whose dK / dV partials do not fit runs unsplit
+  if (pr.opt.head_split == 0 && bwd_ws(&pr, false).total > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    pr.opt.head_split = 1;
   if (bwd_ws(&pr, false).total > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_UNSUPPORTED;
   // every argument is checked before the first HIP call (the scratch lookup)
   void* const placeholder = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
@@ -718,16 +765,24 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
     const bool fz = which == 2;   // 1: dK/dV kernel; 2: fused deterministic (ticket order)
     const int nn = cdiv(p->seqlen_k, fz ? fused_block_n(d) : dkdv_block_n(d));
     const int grp = p->num_heads_q / p->num_heads_kv;
-    const int sec = section_width(2ll * grp * p->seqlen_q * d * 2);
-    const int n = bwd_grid(p, false, fz);
+    const int split = head_split_of(p, false, fz ? ATTN_BWD_FUSED_DQ : ATTN_BWD_RECOMPUTE);
+    const int sec = section_width(2ll * (grp / split) * p->seqlen_q * d * 2);
+    const int n = bwd_grid(p, false, fz, split);
     *count = n;
     for (int i = 0; i < n && i < capacity; ++i) {
-      const Tile t = bwd_tile_fixed(i, p->batch, p->num_heads_kv, nn, sec, which == 2, kNxcd,
-                                    p->opt.tile_order != 0);
+      // with a head split the head is KV head * split + part
+      const Tile t = bwd_tile_fixed(i, p->batch, p->num_heads_kv * split, nn, sec, which == 2,
+                                    kNxcd, p->opt.tile_order != 0);
       out[3 * i] = t.seq; out[3 * i + 1] = t.head; out[3 * i + 2] = t.block;
     }
   }
   return ATTN_OK;
+}
+
+int32_t attn_bwd_head_split(const attn_params* p, int32_t varlen) {
+  if (check_params(p, varlen != 0) != ATTN_OK) return -1;
+  const int design = bwd_design_of(p, varlen != 0);
+  return design < 0 ? -1 : head_split_of(p, varlen != 0, design);
 }
 
 int64_t attn_bwd_ds_subtile(const attn_params* p, int32_t row32, int32_t col32,

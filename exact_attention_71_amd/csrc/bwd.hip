@@ -120,6 +120,37 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// bwd_dkdv_reduce: with a head split, dK = bf16(alpha sum of the parts' dK
+// partials), dV = bf16(sum of the dV partials), parts added in order (the
+// same bits for every run), 8 elements per thread. Packed rows past the last
+// sequence (total_k above cu_seqlens_k[batch]) have no partials: untouched.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ dkp,
+                                                              const float* __restrict__ dvp,
+                                                              bf16* __restrict__ dk,
+                                                              bf16* __restrict__ dv, int64_t n8,
+                                                              int64_t part_stride, int parts,
+                                                              float alpha, const int* cu_k,
+                                                              int nseq, int64_t row8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  if (cu_k && i / row8 >= cu_k[nseq]) return;
+  f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+  for (int s = 0; s < parts; ++s) {
+    const int64_t o = s * part_stride + 8 * i;
+    k0 += *reinterpret_cast<const f32x4*>(dkp + o);
+    k1 += *reinterpret_cast<const f32x4*>(dkp + o + 4);
+    v0 += *reinterpret_cast<const f32x4*>(dvp + o);
+    v1 += *reinterpret_cast<const f32x4*>(dvp + o + 4);
+  }
+  *reinterpret_cast<bf16x8*>(dk + 8 * i) = pack8(k0[0] * alpha, k0[1] * alpha, k0[2] * alpha,
+                                                 k0[3] * alpha, k1[0] * alpha, k1[1] * alpha,
+                                                 k1[2] * alpha, k1[3] * alpha);
+  *reinterpret_cast<bf16x8*>(dv + 8 * i) = pack8(v0[0], v0[1], v0[2], v0[3], v1[0], v1[1],
+                                                 v1[2], v1[3]);
+}
+
+// ---------------------------------------------------------------------------
 // bwd_main
 // ---------------------------------------------------------------------------
 template <int D, int BM, int BN>
@@ -494,6 +525,18 @@ hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stre
     hipLaunchKernelGGL((bwd_main_kernel<256, true>), dim3(grid), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_main_kernel<256, false>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_reduce(const BwdParams& p, int d, hipStream_t stream) {
+  if (p.hsplit <= 1) return hipSuccess;
+  const int64_t per_part = p.rows_k * p.hkv * d;
+  const int64_t n8 = per_part / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int64_t blocks = (n8 + 255) / 256;
+  hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     p.dk_part, p.dv_part, static_cast<bf16*>(p.dk), static_cast<bf16*>(p.dv), n8,
+                     per_part, p.hsplit, p.alpha, p.sv.cu_k, p.sv.batch, (int64_t)p.hkv * d / 8);
   return hipGetLastError();
 }
 

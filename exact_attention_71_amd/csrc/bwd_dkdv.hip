@@ -61,9 +61,10 @@ constexpr int dkdv_smem_bytes() {
             : dkdv_ring_bytes<D, BM>();
 }
 
-// One tile: the keys of key block t.block of (sequence t.seq, KV head t.head).
+// One tile: the keys of key block t.block of (sequence t.seq, KV head t.head),
+// query heads of part `part` of the group (p.hsplit parts).
 template <int D, int KB, int BM, bool DS, bool MASK, int DQ>
-__device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, char* smem) {
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int part, char* smem) {
   static_assert(!(DS && MASK), "block masks run with the recomputing dQ kernel");
   static_assert(!(DS && DQ), "stored dS feeds the dQ kernel; DQ forms dQ here");
   constexpr int NW = 4, NT = NW * 64;
@@ -122,7 +123,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   const int shift = lk - lq;            // causal: row i sees keys j <= i + shift
   const int m_first = causal ? imin(causal_row_begin(n0, shift) / BM, nm) : 0;
   const int per_head = nm - m_first;
-  const int n_steps = p.group * per_head;
+  const int gs = p.group / p.hsplit;   // query heads of this part
+  const int n_steps = gs * per_head;
   const int wk0 = n0 + KPW * w;         // first key of this wave
 
   // ---- this wave's keys: K and V as B operands (key on the lane)
@@ -159,7 +161,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   // 32-bit offsets from per-tile bases: a step's loads then cost a few scalar
   // operations (one wave per SIMD issues every instruction of the step
   // itself). Within one sequence the Q / dO byte offsets stay below 2^31.
-  const int kvh0 = kvh * p.group;
+  const int kvh0 = kvh * p.group + part * gs;   // first query head of the part
   int i_h = 0;
   // Stored dS (DS): sub-tiles of 32 queries x 32 keys per (sequence, query
   // head), 2 KiB each, key-block major (DsGeom: this tile's keys lie in one
@@ -664,12 +666,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { agpr_fence(dk[kb][db]); agpr_fence(dv[kb][db]); }
+  // With a head split: fp32 partials of this part (the reduction scales dK).
+  // One loop serves both forms, branching on an opaque copy of the flag per
+  // store, so that the compiler keeps a single copy of the loop (two would
+  // hold the accumulators in VGPRs for both and spill).
   const float a = p.alpha;
+  const bool split = p.hsplit > 1;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = wk0 + 32 * kb + c;
     if (key < lk) {
       const int64_t ro = (ks0 + key) * kstride + (int64_t)kvh * D + 4 * g;
+      const int64_t rp = (int64_t)part * p.rows_k * kstride + ro;
       bf16* dkp = static_cast<bf16*>(p.dk) + ro;
       bf16* dvp = static_cast<bf16*>(p.dv) + ro;
 #pragma unroll
@@ -678,10 +686,17 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, cha
         for (int j = 0; j < 4; ++j) {
           const f32x16& x = dk[kb][db];
           const f32x16& y = dv[kb][db];
-          *reinterpret_cast<bf16x4*>(dkp + db * 32 + 8 * j) =
-              pack4(x[4 * j] * a, x[4 * j + 1] * a, x[4 * j + 2] * a, x[4 * j + 3] * a);
-          *reinterpret_cast<bf16x4*>(dvp + db * 32 + 8 * j) =
-              pack4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+          if (opaque_bool(split)) {
+            *reinterpret_cast<f32x4*>(p.dk_part + rp + db * 32 + 8 * j) =
+                f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+            *reinterpret_cast<f32x4*>(p.dv_part + rp + db * 32 + 8 * j) =
+                f32x4{y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]};
+          } else {
+            *reinterpret_cast<bf16x4*>(dkp + db * 32 + 8 * j) =
+                pack4(x[4 * j] * a, x[4 * j + 1] * a, x[4 * j + 2] * a, x[4 * j + 3] * a);
+            *reinterpret_cast<bf16x4*>(dvp + db * 32 + 8 * j) =
+                pack4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+          }
         }
     }
   }
@@ -698,17 +713,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
     const int i = next_tile(r, p.ntiles, p.nxcd, p.queue, &ticket);
     if (i < 0) break;
     Tile t;
+    int part = 0;
     if (p.sv.cu_q) {
+      // head split: ticket = base tile * hsplit + part (the tables count base tiles)
+      int ib = i;
+      if (p.hsplit > 1) {
+        ib = i / p.hsplit;
+        part = i - ib * p.hsplit;
+      }
       // deterministic: shortest first, the order of the chain's turns
-      t = varlen_tile(i, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/DQ == 2);
+      t = varlen_tile(ib, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/DQ == 2);
       if (t.seq < 0) {
         if (p.queue) continue;   // a ticket past the last real tile
         break;
       }
     } else {
-      t = bwd_tile_fixed(i, p.sv.batch, p.hkv, p.nn, p.sec, DQ == 2, p.nxcd, p.natural != 0);
+      // head split: (KV head, part) pairs are the scheduler's heads
+      t = bwd_tile_fixed(i, p.sv.batch, p.hkv * p.hsplit, p.nn, p.sec, DQ == 2, p.nxcd,
+                         p.natural != 0);
+      if (p.hsplit > 1) {
+        const int kv = t.head / p.hsplit;
+        part = t.head - kv * p.hsplit;
+        t.head = kv;
+      }
     }
-    dkdv_tile<D, KB, BM, DS, MASK, DQ>(p, t, smem);
+    dkdv_tile<D, KB, BM, DS, MASK, DQ>(p, t, part, smem);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }

@@ -252,6 +252,14 @@ __device__ __forceinline__ int opaque_lane_id() {
   return l;
 }
 
+// A wave-uniform flag through an opaque copy: a branch on it inside a loop
+// is not hoisted out (no second copy of the loop).
+__device__ __forceinline__ bool opaque_bool(bool b) {
+  int v = __builtin_amdgcn_readfirstlane(b ? 1 : 0);
+  asm volatile("" : "+s"(v));
+  return v != 0;
+}
+
 // threadIdx.x through an opaque copy: values derived from it inside a
 // persistent loop's tile body are then recomputed per tile rather than
 // hoisted in front of the loop and kept live (in VGPRs) across all tiles.

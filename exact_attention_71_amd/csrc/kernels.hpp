@@ -107,6 +107,15 @@ struct BwdParams {
   // into dq_acc, 2 the same in the deterministic order (sem, in turns of
   // four wavefront adds per key block)
   int dq_mode;
+  // Head split (hsplit > 1): tile head t.head = KV head * hsplit + part (fixed
+  // length) or ticket i = base tile * hsplit + part (packed lengths); part j
+  // walks query heads j group/hsplit .. of the group and writes fp32 dK
+  // (unscaled) and dV partials [part][row][KV head][d] of rows_k rows each,
+  // which launch_bwd_dkdv_reduce adds in part order.
+  int hsplit;
+  float* dk_part;
+  float* dv_part;
+  int64_t rows_k;
 };
 
 // Stored-dS layout of one (sequence, query head) with lq queries and lk
@@ -253,6 +262,9 @@ hipError_t launch_bwd_main(const BwdParams& p, int d, int grid, hipStream_t stre
 // dK, dV: one workgroup per DkdvCfg<d>::BN keys (see bwd_dkdv.hip); with
 // p.dq_mode set (head_dim 64, 128) also dQ into p.dq_acc.
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, int cus, hipStream_t stream);
+// dK = bf16(alpha sum of the dK partials), dV = bf16(sum of the dV
+// partials), parts in order (p.hsplit > 1).
+hipError_t launch_bwd_dkdv_reduce(const BwdParams& p, int d, hipStream_t stream);
 // dQ without atomics: one workgroup per query block (see bwd_dq.hip).
 hipError_t launch_bwd_dq(const BwdParams& p, int d, int cus, hipStream_t stream);
 // dQ = alpha dS K from the dS the dK/dV kernel stored (p.ds; see bwd_dq_ds.hip).

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ATTN71_VERSION 200 /* 0.2.0: per-call options, visible-only stored dS */
+#define ATTN71_VERSION 201 /* 0.2.1: + head_split option, fused dQ per 256 keys */
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -122,9 +122,22 @@ typedef struct attn_options {
                             the ordered dQ chain in polls (0: default 2^26) */
   int64_t ds_budget;     /* bytes of stored dS the backward may place in its
                             workspace (0: default ATTN_DS_BUDGET_DEFAULT) */
+  int32_t head_split;    /* backward key-block tiles: 0 (default) automatic:
+                            when the (sequence, KV head, key block) tiles
+                            would not fill the device (few KV heads, few or
+                            short sequences; fewer than ATTN_SPLIT_TARGET
+                            tiles), the query heads of each KV group are split
+                            over n workgroups (the largest divisor n of
+                            Hq / Hkv that keeps the tiles within the target),
+                            each writing fp32 dK / dV partials that a
+                            reduction adds in a fixed order; 1: never split;
+                            n >= 2: n parts (n must divide Hq / Hkv; not with
+                            the fused design at head_dim 256) */
+  int32_t reserved;      /* must be zero */
 } attn_options;
 
 #define ATTN_DS_BUDGET_DEFAULT (4ll << 30)
+#define ATTN_SPLIT_TARGET 512 /* key-block tiles the automatic head split aims at */
 
 /* A varlen plan: the schedule tables of one packed batch (the order of the
  * sequences longest first, tile and block prefix sums, stored-dS offsets,
@@ -209,6 +222,15 @@ size_t attn_bwd_workspace_size(const attn_params* p, int32_t varlen);
  * every sequence's key length; sequences beyond it drop stores rather than
  * write past the workspace). */
 int32_t attn_bwd_design(const attn_params* p, int32_t varlen);
+
+/* Query-head parts per KV group the backward's key-block kernel runs with
+ * (opt.head_split resolved; 1: unsplit), -1 if the parameters are invalid
+ * or the design request cannot be met. With n > 1 each (sequence, KV head,
+ * key block) tile becomes n workgroups, part j walking query heads
+ * j Hq/(Hkv n) .. (j+1) Hq/(Hkv n) - 1 of the group and writing fp32 dK / dV
+ * partials that a reduction kernel adds in part order (deterministic). Pure
+ * function of the arguments. */
+int32_t attn_bwd_head_split(const attn_params* p, int32_t varlen);
 
 /* Bytes of device memory a varlen plan for these parameters needs (they
  * depend on the sequence count only); (size_t)-1 for parameters the varlen
@@ -311,7 +333,9 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* wo
  * one contiguous range per XCD). which = 0: forward, out[3*i..3*i+2] = (batch, query head,
  * query block) of workgroup i; which = 1: dK/dV (or fused) backward,
  * which = 2: fused deterministic backward in ticket order (key blocks of
- * 256 at head_dim 64 and 128, 128 at 256), (batch, KV head, key block);
+ * 256 at head_dim 64 and 128, 128 at 256), (batch, KV head, key block),
+ * or with a head split of n (attn_bwd_head_split) (batch, KV head * n +
+ * part, key block);
  * which = 3: dQ kernel, (batch, query head, query block).
  * *count receives the grid size; at most `capacity` triples are written.
  * No GPU is needed. */

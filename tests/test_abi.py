@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ea.load()
-    assert ea.version() == 200
+    assert ea.version() == 201
     assert lib.attn_status_string(0) == b"OK"
     assert lib.attn_status_string(3) == b"workspace too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -114,17 +114,22 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_workspace_sizes():
-    rows, hq, d = 2 * 300, 4, 128
-    p = _p(options=dict(bwd_design=ea.BWD_RECOMPUTE))
+    rows, hq, hkv, d = 2 * 300, 4, 2, 128
+    p = _p(options=dict(bwd_design=ea.BWD_RECOMPUTE, head_split=1))
     assert ea.fwd_workspace_size(p) == 0
     need = ea.bwd_workspace_size(p)
     assert 2 * rows * hq * 4 <= need < 2 * rows * hq * 4 + 1024   # -D, LSE log2 e, counters
-    fused = ea.bwd_workspace_size(_p(options=dict(bwd_design=ea.BWD_FUSED_DQ)))
+    # a head split adds the fp32 dK and dV partials of its parts
+    split = ea.bwd_workspace_size(_p(options=dict(bwd_design=ea.BWD_RECOMPUTE, head_split=2)))
+    assert need + 2 * 2 * rows * hkv * d * 4 <= split < need + 2 * 2 * rows * hkv * d * 4 + 256
+    fused = ea.bwd_workspace_size(_p(options=dict(bwd_design=ea.BWD_FUSED_DQ, head_split=1)))
     assert fused >= need + rows * hq * d * 4                       # + the fp32 dQ accumulator
-    fused_det = ea.bwd_workspace_size(_p(deterministic=True, options=dict(bwd_design=3)))
+    fused_det = ea.bwd_workspace_size(_p(deterministic=True,
+                                         options=dict(bwd_design=3, head_split=1)))
     assert fused_det > fused                                       # + semaphores
     # deterministic costs nothing outside the fused design
-    assert ea.bwd_workspace_size(_p(deterministic=True, options=dict(bwd_design=1))) == need
+    assert ea.bwd_workspace_size(_p(deterministic=True,
+                                    options=dict(bwd_design=1, head_split=1))) == need
     pv = _p(total_q=1000, total_k=1000, batch=5)
     assert ea.fwd_workspace_size(pv, True) > 0
     assert ea.fwd_workspace_size(_p(head_dim=80)) == SIZE_MAX
@@ -135,7 +140,8 @@ def test_workspace_sizes():
                                  dict(one_shot_grid=-1), dict(exp_emulation=3),
                                  dict(exp_emulation=8), dict(tau=-2.0), dict(tau=65.0),
                                  dict(tau=float("nan")), dict(spin_limit=-1),
-                                 dict(ds_budget=-1)])
+                                 dict(ds_budget=-1), dict(head_split=-1), dict(head_split=3),
+                                 dict(head_split=4), dict(reserved=1)])
 def test_options_are_validated(opt):
     lib = ea.load()
     p = _p(options=opt)
@@ -153,6 +159,28 @@ def test_valid_options_pass_validation():
         # fails on the null q pointer, i.e. after the options were accepted
         assert lib.attn_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, 0, None) == INVALID
         assert ea.bwd_workspace_size(p) != SIZE_MAX
+
+
+def test_head_split_rule():
+    """Automatic head split: the largest divisor of the KV group that keeps the
+    key-block tiles within 512, only when the unsplit tiles fall below it."""
+    def hs(b, s, hq, hkv, d, varlen=False, **opt):
+        tot = b * s if varlen else 0
+        p = ea.make_params(b, s, s, hq, hkv, d, 0.088, True, total_q=tot, total_k=tot,
+                           options=opt or None)
+        return ea.bwd_head_split(p, varlen)
+    assert hs(2, 8192, 16, 1, 128) == 8        # MQA: 64 tiles -> 512
+    assert hs(2, 8192, 16, 16, 128) == 1       # MHA: no group to split
+    assert hs(1, 8192, 8, 2, 128) == 4         # 64 tiles, group 4 -> 256
+    assert hs(16, 4352, 32, 4, 128, varlen=True) == 1   # packed GQA: 1152 tiles
+    assert hs(1, 300, 8, 1, 64) == 8
+    assert hs(2, 8192, 16, 1, 128, head_split=1) == 1
+    assert hs(2, 8192, 16, 1, 128, head_split=4) == 4
+    # the fused design at head_dim 256 (the 128-key kernel) walks whole groups
+    assert hs(2, 8192, 16, 1, 256, bwd_design=ea.BWD_FUSED_DQ) == 1
+    p = ea.make_params(1, 300, 300, 8, 1, 256, 0.088, True,
+                       options=dict(bwd_design=ea.BWD_FUSED_DQ, head_split=2))
+    assert ea.bwd_workspace_size(p) == SIZE_MAX and ea.bwd_head_split(p) == -1
 
 
 def test_workspace_size_is_a_pure_function_of_the_parameters():
@@ -201,21 +229,26 @@ def test_forward_tile_order_is_a_permutation_longest_first(b, s, hq, hkv, d, cau
 def test_backward_tile_orders(b, s, hq, hkv, d):
     p = _p(batch=b, seqlen_q=s, seqlen_k=s, heads_q=hq, heads_kv=hkv, head_dim=d, causal=True)
     nn_dkdv = -(-s // (256 if d <= 128 else 128))
+    # a head split of n makes (KV head, part) the scheduler's heads
+    split = ea.bwd_head_split(p)
+    assert split >= 1 and (hq // hkv) % split == 0
+    if b * hkv * nn_dkdv >= 512:
+        assert split == 1   # enough tiles: no split
     lpt = ea.tile_order(p, 1)
-    assert sorted(lpt) == sorted((bb, h, n) for bb in range(b) for h in range(hkv)
+    assert sorted(lpt) == sorted((bb, h, n) for bb in range(b) for h in range(hkv * split)
                                  for n in range(nn_dkdv))
     # the fused design: 256-key blocks at head_dim 64 and 128 (the dK/dV kernel), 128 at 256
     nn = nn_dkdv
-    full = sorted((bb, h, n) for bb in range(b) for h in range(hkv) for n in range(nn))
+    full = sorted((bb, h, n) for bb in range(b) for h in range(hkv * split) for n in range(nn))
     det = ea.tile_order(p, 2)
     assert sorted(det) == full
-    # deterministic order: for each (batch, KV head) key blocks strictly descending, so every
-    # workgroup only ever waits on workgroups that took earlier tickets
+    # deterministic order: for each (batch, KV head, part) key blocks strictly descending, so
+    # every workgroup only ever waits on workgroups that took earlier tickets
     pos = {}
     for i, t in enumerate(det):
         pos[t] = i
     for bb in range(b):
-        for h in range(hkv):
+        for h in range(hkv * split):
             idx = [pos[(bb, h, n)] for n in range(nn)]
             assert all(idx[n] > idx[n + 1] for n in range(nn - 1))
 

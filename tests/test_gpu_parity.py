@@ -346,6 +346,51 @@ def test_stored_ds_lengths_beyond_declared_maximum_stay_in_the_workspace(hq, hkv
     assert rel_l2(dk, ref[1]) <= 2e-2 and rel_l2(dv, ref[2]) <= 2e-2
 
 
+@pytest.mark.parametrize("varlen", [False, True])
+def test_head_split_matches_oracle_and_is_reproducible(varlen, bwd_mode):
+    """The query heads of an MQA group split over 1, 2 and 8 key-block
+    workgroups: every split matches the oracle, and a split run gives the same
+    dK, dV bits twice (its fp32 partials are added in part order)."""
+    hq, hkv, d = 8, 1, 128
+    scale = 1.0 / math.sqrt(d)
+    if varlen:
+        lengths = [300, 0, 700, 129]
+        inp = make_inputs(0, 0, 0, hq, hkv, d, seed=801, lengths=lengths)
+    else:
+        inp = make_inputs(1, 700, 700, hq, hkv, d, seed=802)
+    g = _dev(inp)
+    if varlen:
+        mx = max(lengths)
+        cu = (g["cu_seqlens_q"], g["cu_seqlens_k"])
+        o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], *cu, mx, mx, causal=True,
+                               softmax_scale=scale)
+        ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True,
+                                        inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    else:
+        o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=scale)
+        ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True)
+
+    def run(split):
+        opts = dict(bwd_design_opts, head_split=split)
+        if varlen:
+            out = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, *cu, mx, mx, causal=True,
+                                softmax_scale=scale, options=opts)
+        else:
+            out = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True,
+                         softmax_scale=scale, options=opts)
+        torch.cuda.synchronize()
+        return out
+
+    bwd_design_opts = bwd_mode
+    for split in (1, 2, 8):
+        print(f"[head split] varlen={varlen} {bwd_mode} split={split}", flush=True)
+        grads = run(split)
+        check_grads(grads, ref, f"head split {split} varlen {varlen}")
+        if split == 8:
+            again = run(split)
+            assert torch.equal(grads[1], again[1]) and torch.equal(grads[2], again[2])
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_varlen_plan_gives_the_same_bits(causal, bwd_mode):
     """A cached varlen plan (one schedule launch, reused by every call) gives
