@@ -142,13 +142,12 @@ __device__ __forceinline__ float xor32(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
-// max of three floats in one instruction. Written as inline asm because the
-// compiler otherwise quiets every MFMA result (an extra v_max per element)
-// before fmaxf; MFMA never produces signalling NaNs, so that step is moot here.
+// max of three floats: the compiler folds the pair of fmaxf into one
+// v_max3_f32 (and, on MFMA results, adds no quieting step). Plain code rather
+// than inline asm, whose outputs the hazard recognizer guards with a wait
+// state before every dependent VALU instruction.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // Staging-unit mapping for tiles written to LDS both row-major and transposed.

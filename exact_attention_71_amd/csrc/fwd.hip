@@ -292,10 +292,16 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
             }
           }
         }
+        // a depth-3 tree of eight v_max3 per 32-key block (a chain would
+        // serialise eight dependent instructions)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) mx[qb] = max3f(mx[qb], s[kb][qb][i], s[kb][qb][i + 1]);
+        for (int qb = 0; qb < QB; ++qb) {
+          const f32x16& v = s[kb][qb];
+          const float t0 = max3f(v[0], v[1], v[2]), t1 = max3f(v[3], v[4], v[5]);
+          const float t2 = max3f(v[6], v[7], v[8]), t3 = max3f(v[9], v[10], v[11]);
+          const float t4 = max3f(v[12], v[13], v[14]);
+          mx[qb] = max3f(mx[qb], max3f(t0, t1, t2), max3f(t3, t4, v[15]));
+        }
       };
       constexpr int NSF = NKB * KS;                 // S^T MFMA fragments
       auto fetch_s = [&](int y) -> bf16x8 {
@@ -349,14 +355,18 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       // schedule: the P work of each 16-key half (8 elements) runs between
       // the NDB MFMAs of the previous half, whose V^T fragments stream two
       // ahead; only half 0 is computed up front.
-      float nb[QB], acc[QB];
+      // row sums in two accumulators (even and odd elements): two short
+      // dependency chains instead of one through the whole tile
+      float nb[QB], acc[QB][2];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         nb[qb] = (mref[qb] == neg_inf()) ? 0.0f : -mref[qb] * sl2;
-        acc[qb] = 0.0f;
+        acc[qb][0] = acc[qb][1] = 0.0f;
       }
       auto p_half = [&](int h, int j0, int nj) {   // elements j0 .. j0+nj-1 of half h
         const int kb = h / 2;
+        // the exponentials first, then the sums: no sum reads the result of
+        // the exponential just before it (a wait state after v_exp_f32)
 #pragma unroll
         for (int j = j0; j < j0 + nj; ++j) {
           const int i = 8 * (h % 2) + j;
@@ -366,8 +376,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
             float e = ((i & 7) < EMU) ? emu_exp2(x) : fast_exp2(x);
             pin(e);
             s[kb][qb][i] = e;
-            acc[qb] += e;
           }
+        }
+#pragma unroll
+        for (int j = j0; j < j0 + nj; ++j) {
+          const int i = 8 * (h % 2) + j;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][j & 1] += s[kb][qb][i];
         }
       };
       constexpr int NH = 2 * NKB, NPV = NH * NDB;   // halves, PV MFMAs
@@ -403,7 +418,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
         }
       }
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb];
+      for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb][0] + acc[qb][1];
     }
     advance_slot(st);
     if constexpr (!LAST) wait_next(n + NS - 1 < n_tiles);
