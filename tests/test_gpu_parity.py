@@ -391,6 +391,40 @@ def test_head_split_matches_oracle_and_is_reproducible(varlen, bwd_mode):
             assert torch.equal(grads[1], again[1]) and torch.equal(grads[2], again[2])
 
 
+def test_head_split_leaves_packed_rows_past_the_last_sequence_alone():
+    """Packed K / V with rows past the last sequence (total_k above
+    cu_seqlens_k[batch]): the split backward's reduction writes dK, dV of the
+    sequences' rows only (a canary survives in the rest), and those rows
+    match the unsplit run."""
+    lengths = [300, 129]
+    hq, hkv, d, pad = 8, 1, 128, 64
+    scale = 1.0 / math.sqrt(d)
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=811, lengths=lengths)
+    g = _dev(inp)
+    tk = g["k"].shape[0]
+    zeros = torch.zeros((pad, hkv, d), dtype=g["k"].dtype, device=DEV)
+    k = torch.cat([g["k"], zeros]).contiguous()
+    v = torch.cat([g["v"], zeros]).contiguous()
+    cu_q, cu_k = g["cu_seqlens_q"], g["cu_seqlens_k"]
+    mx = max(lengths)
+    o, lse = ea.fwd_varlen(g["q"], k, v, cu_q, cu_k, mx, mx, causal=True, softmax_scale=scale)
+    results = {}
+    for split in (1, 2):
+        p = ea.make_params(len(lengths), mx, mx, hq, hkv, d, scale, True, total_q=g["q"].shape[0],
+                           total_k=tk + pad, options=dict(head_split=split))
+        assert ea.bwd_head_split(p, True) == split
+        ws = torch.empty(ea.bwd_workspace_size(p, True), dtype=torch.uint8, device=DEV)
+        dq = torch.empty_like(g["q"])
+        dk = torch.full_like(k, 7.0)
+        dv = torch.full_like(v, 7.0)
+        ea.bwd_phases(p, ea.BWD_ALL, g["q"], k, v, o, g["do"], lse, dq, dk, dv, ws, cu_q, cu_k)
+        torch.cuda.synchronize()
+        assert torch.all(dk[tk:] == 7.0) and torch.all(dv[tk:] == 7.0), split
+        results[split] = (dk[:tk].float(), dv[:tk].float())
+    for a_, b_ in zip(results[1], results[2]):
+        assert torch.linalg.vector_norm(a_ - b_) <= 1e-2 * torch.linalg.vector_norm(a_)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_varlen_plan_gives_the_same_bits(causal, bwd_mode):
     """A cached varlen plan (one schedule launch, reused by every call) gives
