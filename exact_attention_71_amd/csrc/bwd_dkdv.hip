@@ -41,7 +41,8 @@
 // blocks of a (query block, query head) add in a fixed order, the last key
 // block first; a wavefront waits until every wavefront of the earlier key
 // blocks has counted its adds done in the pair's semaphore, and counts its
-// own after the next mid-step wait has seen them complete.
+// own once a later mid-step wait has retired them (two steps on; at the end
+// of the work tile, after a full wait).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "schedule.hpp"
