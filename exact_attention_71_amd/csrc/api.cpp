@@ -111,6 +111,11 @@ attn_status check_params(const attn_params* p, bool varlen) {
   const int64_t rows_k = varlen ? p->total_k : (int64_t)p->batch * p->seqlen_k;
   // grids stay below 2^31 workgroups and row indices in int32
   if (rows_q * p->num_heads_q > (1ll << 30) || rows_k > (1ll << 30)) return ATTN_ERR_UNSUPPORTED;
+  // key-block tiles (128-key blocks bound every backward design) times the
+  // largest head split (the group size) within int32
+  const int64_t kblocks = varlen ? rows_k / 128 + 1 + p->batch
+                                 : (int64_t)p->batch * ((p->seqlen_k + 127) / 128);
+  if (kblocks * p->num_heads_q > (1ll << 30)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

@@ -183,6 +183,15 @@ def test_head_split_rule():
     assert ea.bwd_workspace_size(p) == SIZE_MAX and ea.bwd_head_split(p) == -1
 
 
+def test_tile_counts_stay_within_int32():
+    """Key-block tiles times the largest head split must fit the kernels' int32
+    tile indices: 2^16 key blocks x 2^16 query heads is refused up front."""
+    p = ea.make_params(1, 16, 1 << 23, 1 << 16, 1, 64, 0.125, False)
+    assert ea.bwd_workspace_size(p) == SIZE_MAX and ea.bwd_head_split(p) == -1
+    ok = ea.make_params(1, 16, 1 << 20, 1 << 10, 1, 64, 0.125, False)
+    assert ea.bwd_workspace_size(ok) != SIZE_MAX
+
+
 def test_workspace_size_is_a_pure_function_of_the_parameters():
     """No process-wide state: sizes and designs depend on the parameters
     (options included) alone, whatever other calls ran in between."""
