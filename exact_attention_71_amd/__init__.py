@@ -14,6 +14,7 @@ Entry points mirror the C ABI in ``include/attn71.h``:
     bwd_phases(...)          the backward split into its launches
     bwd_design(params)       the backward design a call with these parameters runs
     tile_order(...)          the fixed-length tile schedule, evaluated on the host
+    varlen_key_order(...)    the packed-length key-block order, evaluated on the host
 
 Design and tuning choices are per call: ``options`` is a dict of
 ``attn_options`` fields (bwd_design, tile_order, one_shot_grid,
@@ -33,6 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn71.so")
 
 ATTN_OK = 0
+ATTN_ERR_UNSUPPORTED = 2
 BWD_PREPROCESS, BWD_MAIN, BWD_POSTPROCESS, BWD_DQ, BWD_ALL = 1, 2, 4, 8, 15
 
 
@@ -95,7 +97,7 @@ EXPORTS = ["attn_status_string", "attn_version", "attn_fwd_workspace_size",
            "attn_bwd_varlen", "attn_bwd_phases", "attn_bwd_status", "attn_tile_order",
            "attn_persistent_tile", "attn_bwd_design", "attn_bwd_noalloc",
            "attn_bwd_ds_subtile", "attn_varlen_plan_size", "attn_varlen_plan_build",
-           "attn_bwd_head_split"]
+           "attn_bwd_head_split", "attn_varlen_key_order"]
 
 
 def _lib():
@@ -120,6 +122,8 @@ def _lib():
     lib.attn_bwd_status.argtypes = [_P, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_int32), _vp]
     lib.attn_tile_order.argtypes = [_P, ctypes.c_int32, _vp, ctypes.c_int64,
                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.attn_varlen_key_order.argtypes = [_P, _vp, _vp, _vp, ctypes.c_int64,
+                                          ctypes.POINTER(ctypes.c_int64)]
     lib.attn_persistent_tile.argtypes = [ctypes.c_int32] * 5
     lib.attn_persistent_tile.restype = ctypes.c_int32
     lib.attn_bwd_design.argtypes = [_P, ctypes.c_int32]
@@ -392,6 +396,24 @@ def bwd_status(p: AttnParams, workspace: torch.Tensor, varlen: bool = False) -> 
     _check(_lib().attn_bwd_status(ctypes.byref(p), int(varlen), _ptr(workspace),
                                   ctypes.byref(val), _stream()), "attn_bwd_status")
     return val.value
+
+
+def varlen_key_order(p: AttnParams, cu_q, cu_k):
+    """[(sequence, key block)] in the order the packed-length dK/dV kernel takes
+    its key-block tiles (KV heads innermost), or None where it keeps the
+    per-sequence order. cu_q / cu_k: host int sequences of batch + 1 offsets."""
+    lib = _lib()
+    cq = (ctypes.c_int32 * len(cu_q))(*[int(x) for x in cu_q])
+    ck = (ctypes.c_int32 * len(cu_k))(*[int(x) for x in cu_k])
+    count = ctypes.c_int64(0)
+    st = lib.attn_varlen_key_order(ctypes.byref(p), cq, ck, None, 0, ctypes.byref(count))
+    if st == ATTN_ERR_UNSUPPORTED:
+        return None
+    _check(st, "attn_varlen_key_order")
+    buf = (ctypes.c_int32 * (2 * count.value))()
+    _check(lib.attn_varlen_key_order(ctypes.byref(p), cq, ck, buf, count.value,
+                                     ctypes.byref(count)), "attn_varlen_key_order")
+    return [tuple(buf[2 * i:2 * i + 2]) for i in range(count.value)]
 
 
 def tile_order(p: AttnParams, which: int):

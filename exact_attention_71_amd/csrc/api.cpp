@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "attn71.h"
 #include "kernels.hpp"
@@ -127,16 +128,33 @@ int64_t rows_q_of(const attn_params* p, bool varlen) {
 // Varlen schedule tables of one kernel (see SchedSet): offsets in a buffer.
 enum SetKind { kSetFwd = 0, kSetDkdv = 1, kSetFused = 2, kSetDq = 3, kSetDqDs = 4, kNumSets = 5 };
 struct SetMap {
-  size_t order = 0, tile_prefix = 0, mb_prefix = 0, ds_prefix = 0, queue = 0;
+  size_t order = 0, tile_prefix = 0, mb_prefix = 0, ds_prefix = 0, key_tiles = 0, queue = 0;
   bool mb = false, ds = false;
+  int key_cap = 0;        // entries of the key-tile list (0: none)
 };
-size_t map_set(size_t off, int64_t nseq, int kind, SetMap* m) {
+// The key-tile list (one longest-first order of all key blocks) of the
+// key-block kernels that run in the dK/dV kernel: entries bounded by
+// total_k / block + batch; ranking costs entries x batch steps of one
+// workgroup, so only up to 2^17 of them.
+int key_list_cap(const attn_params* p, int kind) {
+  const int d = p->head_dim;
+  if (kind != kSetDkdv && !(kind == kSetFused && fused_in_dkdv(d))) return 0;
+  const int64_t cap = (int64_t)p->total_k / dkdv_block_n(d) + 1 + p->batch;
+  return cap * p->batch <= (1ll << 17) ? (int)cap : 0;
+}
+size_t map_set(size_t off, const attn_params* p, int kind, SetMap* m) {
+  const int64_t nseq = p->batch;
   m->mb = kind == kSetDkdv || kind == kSetFused;
   m->ds = kind == kSetDkdv;
+  m->key_cap = key_list_cap(p, kind);
   m->order = off; off = align_up(off + sizeof(int) * (size_t)nseq);
   m->tile_prefix = off; off = align_up(off + sizeof(int) * ((size_t)nseq + 1));
   if (m->mb) { m->mb_prefix = off; off = align_up(off + sizeof(int) * ((size_t)nseq + 1)); }
   if (m->ds) { m->ds_prefix = off; off = align_up(off + sizeof(int64_t) * ((size_t)nseq + 1)); }
+  if (m->key_cap) {
+    m->key_tiles = off;
+    off = align_up(off + 2 * sizeof(int) * ((size_t)m->key_cap + 1));
+  }
   m->queue = off; off = align_up(off + sizeof(unsigned));
   return off;
 }
@@ -147,7 +165,7 @@ struct FwdWs {
 };
 FwdWs fwd_ws(const attn_params* p, bool varlen) {
   FwdWs w;
-  if (varlen && !p->varlen_plan) w.total = map_set(0, p->batch, kSetFwd, &w.set);
+  if (varlen && !p->varlen_plan) w.total = map_set(0, p, kSetFwd, &w.set);
   return w;
 }
 
@@ -159,7 +177,7 @@ struct PlanMap {
 PlanMap plan_map(const attn_params* p) {
   PlanMap m;
   size_t off = 0;
-  for (int k = 0; k < kNumSets; ++k) off = map_set(off, p->batch, k, &m.set[k]);
+  for (int k = 0; k < kNumSets; ++k) off = map_set(off, p, k, &m.set[k]);
   m.total = off;
   return m;
 }
@@ -260,8 +278,8 @@ BwdWs bwd_ws(const attn_params* p, bool varlen) {
   }
   if (varlen && !p->varlen_plan && w.design > 0) {
     w.tables = true;
-    off = map_set(off, p->batch, main_kind(w.design), &w.main);
-    if (!fused) off = map_set(off, p->batch, dq_kind(w.design), &w.dq);
+    off = map_set(off, p, main_kind(w.design), &w.main);
+    if (!fused) off = map_set(off, p, dq_kind(w.design), &w.dq);
   }
   if (w.design == ATTN_BWD_STORED_DS) {
     w.ds = off;
@@ -353,6 +371,11 @@ SchedSet make_set(const attn_params* p, int kind, const int32_t* cu_q, const int
   s.tile_prefix = reinterpret_cast<int*>(base + m.tile_prefix);
   s.mb_prefix = m.mb ? reinterpret_cast<int*>(base + m.mb_prefix) : nullptr;
   s.mb_blk = fused_block_m(d);
+  if (m.key_cap) {
+    s.key_tiles = reinterpret_cast<int*>(base + m.key_tiles);
+    s.key_cap = m.key_cap;
+    s.rank_bm = d == 64 ? DkdvCfg<64>::BM : DkdvCfg<128>::BM;   // query rows per dK/dV step
+  }
   s.queue = reinterpret_cast<unsigned*>(base + m.queue);
   s.ds_prefix = m.ds ? reinterpret_cast<int64_t*>(base + m.ds_prefix) : nullptr;
   s.ds_heads = p->num_heads_q;
@@ -544,6 +567,7 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
     bp.order = ms.order;
     bp.tile_prefix = ms.tile_prefix;
     bp.mb_prefix = ms.mb_prefix;
+    bp.key_tiles = ms.key_tiles;
     bp.queue = pcus ? ms.queue : nullptr;
     if (use_ds) bp.ds_prefix = ms.ds_prefix;
     if (!fused) {
@@ -780,6 +804,35 @@ attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, i
                                     kNxcd, p->opt.tile_order != 0);
       out[3 * i] = t.seq; out[3 * i + 1] = t.head; out[3 * i + 2] = t.block;
     }
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_varlen_key_order(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
+                                  int32_t* out, int64_t capacity, int64_t* count) {
+  if (!count || !cu_q || !cu_k || capacity < 0 || (capacity > 0 && !out))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  *count = 0;
+  attn_status st = check_params(p, true);
+  if (st != ATTN_OK) return st;
+  const int cap = key_list_cap(p, kSetDkdv);
+  const int d = p->head_dim, bn = dkdv_block_n(d);
+  const int bm = d == 64 ? DkdvCfg<64>::BM : DkdvCfg<128>::BM;
+  std::vector<int> lq(p->batch), lk(p->batch);
+  int nkb = 0;
+  for (int s = 0; s < p->batch; ++s) {
+    lq[s] = cu_q[s + 1] - cu_q[s];
+    lk[s] = cu_k[s + 1] - cu_k[s];
+    nkb += imax(0, cdiv(lk[s], bn));
+  }
+  *count = nkb;
+  if (cap == 0 || nkb > cap) return ATTN_ERR_UNSUPPORTED;
+  for (int e = 0; e < nkb; ++e) {
+    int s, b;
+    key_block_at(lk.data(), p->batch, bn, e, &s, &b);
+    const int r = key_block_rank(lq.data(), lk.data(), p->batch, bm, bn, p->causal != 0, s, b);
+    if (r < 0 || r >= nkb) return ATTN_ERR_INVALID_ARGUMENT;
+    if (r < capacity) { out[2 * r] = s; out[2 * r + 1] = b; }
   }
   return ATTN_OK;
 }

@@ -722,8 +722,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
         ib = i / p.hsplit;
         part = i - ib * p.hsplit;
       }
-      // deterministic: shortest first, the order of the chain's turns
-      t = varlen_tile(ib, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/DQ == 2);
+      if (DQ != 2 && p.key_tiles && p.key_tiles[0]) {
+        // one longest-first list of all key blocks, KV heads innermost
+        t.seq = -1;
+        if (ib < p.tile_prefix[p.sv.batch]) {
+          const int e = ib / p.hkv;
+          t.head = ib - e * p.hkv;
+          t.seq = __builtin_amdgcn_readfirstlane(p.key_tiles[2 + 2 * e]);
+          t.block = __builtin_amdgcn_readfirstlane(p.key_tiles[3 + 2 * e]);
+          if ((unsigned)t.seq >= (unsigned)p.sv.batch) t.seq = -1;
+        }
+      } else {
+        // deterministic: shortest first, the order of the chain's turns
+        t = varlen_tile(ib, p.order, p.tile_prefix, p.sv.batch, p.hkv, /*reverse=*/DQ == 2);
+      }
       if (t.seq < 0) {
         if (p.queue) continue;   // a ticket past the last real tile
         break;

@@ -72,6 +72,8 @@ struct BwdParams {
   const int* order;       // varlen: virtual -> actual sequence (by key length)
   const int* tile_prefix; // varlen: first tile of each virtual sequence
   const int* mb_prefix;   // varlen: query-block prefix per actual sequence
+  const int* key_tiles;   // varlen, optional: a SchedSet key-tile list (used when its
+                          // first word is set; else the per-sequence order)
   int hq, hkv, group;
   int nn;                 // fixed: key blocks per sequence
   int nm;                 // fixed: query blocks per sequence
@@ -287,6 +289,12 @@ struct SchedSet {
   int* tile_prefix;
   int* mb_prefix;
   int mb_blk;
+  // optional (key-block kinds): key_tiles[0] = 1 when the list below is
+  // written (0 when the blocks exceed key_cap), key_tiles[2 + 2 r], [3 + 2 r]
+  // = (sequence, key block) of rank r in the longest-first order of all key
+  // blocks (schedule.hpp: key_block_rank, steps of rank_bm query rows)
+  int* key_tiles;
+  int key_cap, rank_bm;
   unsigned* queue;
   int64_t* ds_prefix;
   int ds_heads, causal;

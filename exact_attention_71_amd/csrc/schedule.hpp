@@ -165,6 +165,57 @@ A71_HD Tile varlen_tile(int v, const int* order, const int* tile_prefix, int nse
   return t;
 }
 
+// Key-block tiles of packed sequences in one global longest-first order. The
+// work of key block b of a sequence (query rows lq, keys lk, query blocks of
+// bm rows, key blocks of bn keys) is its number of query-block steps: all of
+// them without a causal mask, those from the block's diagonal on with one
+// (bottom-right aligned).
+A71_HD int key_block_work(int lq, int lk, int bm, int bn, bool causal, int b) {
+  const int nm = cdiv(lq, bm);
+  if (!causal) return nm;
+  return nm - imin(causal_row_begin(b * bn, lk - lq) / bm, nm);
+}
+// Number of key blocks b < nkb with work >= w (work > w when strict). The
+// work never grows with b: under the causal mask, work >= w (1 <= w <= nm)
+// holds iff the block's first visible row, max(0, b bn - shift), lies below
+// (nm - w + 1) bm, i.e. iff b bn < (nm - w + 1) bm + shift.
+A71_HD int key_blocks_above(int lq, int lk, int bm, int bn, bool causal, int nkb, int w,
+                            bool strict) {
+  if (strict) ++w;
+  const int nm = cdiv(lq, bm);
+  if (w <= 0) return imax(nkb, 0);
+  if (w > nm) return 0;
+  if (!causal) return imax(nkb, 0);
+  const int n = cdiv((nm - w + 1) * bm + (lk - lq), bn);
+  return imax(0, imin(n, nkb));
+}
+// Position of key block b of sequence s in the longest-first order of all
+// blocks (ties: sequence, then block, ascending): the blocks with more work,
+// plus the blocks with equal work that come first. len_q / len_k: the
+// sequences' query and key lengths; a permutation of [0, total blocks).
+A71_HD int key_block_rank(const int* len_q, const int* len_k, int nseq, int bm, int bn,
+                          bool causal, int s, int b) {
+  const int w = key_block_work(len_q[s], len_k[s], bm, bn, causal, b);
+  int r = b;   // this sequence's earlier blocks (their work is >= w)
+  for (int t = 0; t < nseq; ++t) {
+    if (t == s) continue;
+    r += key_blocks_above(len_q[t], len_k[t], bm, bn, causal, cdiv(len_k[t], bn), w,
+                          /*strict=*/t > s);
+  }
+  return r;
+}
+
+// Key block e of the natural order (sequence-major, blocks of bn keys
+// ascending): *s = its sequence, *b = its block; *s = -1 past the last.
+A71_HD void key_block_at(const int* len_k, int nseq, int bn, int e, int* s, int* b) {
+  *s = -1; *b = 0;
+  for (int t = 0; t < nseq; ++t) {
+    const int n = cdiv(len_k[t], bn);
+    if (n > 0 && e < n) { *s = t; *b = e; return; }
+    if (n > 0) e -= n;
+  }
+}
+
 // Host/device reference of the varlen schedule pass (also run by the single
 // workgroup schedule kernel): sequences sorted by decreasing length (ties by
 // index), tile prefix over ceil(len / blk) * heads, and the per-sequence

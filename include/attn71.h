@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ATTN71_VERSION 201 /* 0.2.1: + head_split option, fused dQ per 256 keys */
+#define ATTN71_VERSION 202 /* 0.2.2: + longest-first packed key-block order */
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -341,6 +341,24 @@ attn_status attn_bwd_status(const attn_params* p, int32_t varlen, const void* wo
  * No GPU is needed. */
 attn_status attn_tile_order(const attn_params* p, int32_t which, int32_t* out, int64_t capacity,
                             int64_t* count);
+
+/* Packed lengths: the order in which the dK/dV kernel of the recomputing
+ * and stored-dS designs (and of the fused design at head_dim 64 and 128,
+ * unless deterministic) takes its key-block tiles. The FlashAttention-4 blog
+ * page (scheduling section) puts the longest tiles first; here every key
+ * block of every sequence is ranked by its work (the query-block steps it
+ * visits: all of them without a causal mask, those from its diagonal on
+ * with one), ties by sequence then block, and the KV heads of one key block
+ * follow each other. cu_q / cu_k: host copies of the packed offsets
+ * (batch + 1 entries each, non-decreasing). Writes (sequence, key block)
+ * pairs in that order to out[2 r], out[2 r + 1] for the first `capacity`
+ * ranks; *count receives the number of key blocks. ATTN_ERR_UNSUPPORTED
+ * when the call keeps the per-sequence order instead (the order of
+ * attn_tile_order's packed analogue: sequences longest first), which it
+ * does past 2^17 (key-block bound x batch) ranking steps. Evaluated on the
+ * host with the schedule pass's arithmetic; no GPU is needed. */
+attn_status attn_varlen_key_order(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
+                                  int32_t* out, int64_t capacity, int64_t* count);
 
 /* Stored-dS layout, evaluated on the host with the kernels' arithmetic: the
  * index of the 32 x 32 sub-tile (sub-row row32 = queries 32 row32 ..,

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = ea.load()
-    assert ea.version() == 201
+    assert ea.version() == 202
     assert lib.attn_status_string(0) == b"OK"
     assert lib.attn_status_string(3) == b"workspace too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -190,6 +190,50 @@ def test_tile_counts_stay_within_int32():
     assert ea.bwd_workspace_size(p) == SIZE_MAX and ea.bwd_head_split(p) == -1
     ok = ea.make_params(1, 16, 1 << 20, 1 << 10, 1, 64, 0.125, False)
     assert ea.bwd_workspace_size(ok) != SIZE_MAX
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, True), (256, True), (128, False)])
+def test_varlen_key_order_is_longest_first(d, causal):
+    """Packed key-block tiles: one order over all sequences, by decreasing
+    work (the query steps whose rows see some key of the block under the
+    bottom-right causal mask, every step without it), ties by sequence then
+    block. Brute force over the mask predicate itself."""
+    import numpy as np
+    rng = np.random.default_rng(7 + d)
+    lq = [int(x) for x in rng.integers(0, 3000, 9)] + [0, 1, 257]
+    # as many keys as queries, more keys, fewer keys (rows before the diagonal see none)
+    lk = [x if i % 3 == 2 else max(0, x + (1 if i % 3 == 0 else -1) * int(rng.integers(0, 600)))
+          for i, x in enumerate(lq)]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).tolist()
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).tolist()
+    bn = 256 if d <= 128 else 128
+    bm = 64 if d == 64 else 32
+    p = ea.make_params(len(lq), max(lq), max(lk), 8, 2, d, 0.1, causal,
+                       total_q=cu_q[-1], total_k=cu_k[-1])
+
+    def work(q, k, b):
+        steps = 0
+        for m in range(-(-q // bm)):
+            rows = range(m * bm, min(q, (m + 1) * bm))
+            keys = range(b * bn, min(k, (b + 1) * bn))
+            steps += any(j <= i + (k - q) for i in rows for j in keys) if causal else 1
+        return steps
+
+    entries = [(s, b) for s in range(len(lq)) for b in range(-(-lk[s] // bn))]
+    want = sorted(entries, key=lambda e: (-work(lq[e[0]], lk[e[0]], e[1]), e[0], e[1]))
+    got = ea.varlen_key_order(p, cu_q, cu_k)
+    assert got == want
+
+
+def test_varlen_key_order_falls_back_for_many_sequences():
+    """Ranking costs (key-block bound x batch) steps of one workgroup: past 2^17
+    the kernel keeps the per-sequence order."""
+    n = 1024
+    cu = [i * 512 for i in range(n + 1)]
+    p = ea.make_params(n, 512, 512, 8, 2, 128, 0.1, True, total_q=cu[-1], total_k=cu[-1])
+    assert ea.varlen_key_order(p, cu, cu) is None
+    small = ea.make_params(16, 512, 512, 8, 2, 128, 0.1, True, total_q=16 * 512, total_k=16 * 512)
+    assert len(ea.varlen_key_order(small, cu[:17], cu[:17])) == 32
 
 
 def test_workspace_size_is_a_pure_function_of_the_parameters():
