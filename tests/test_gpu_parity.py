@@ -128,6 +128,37 @@ def test_varlen_matches_oracle(causal, bwd_mode):
     check_grads((dq, dk, dv), ref, "varlen")
 
 
+@pytest.mark.parametrize("nseq,uses_list", [(250, True), (420, False)])
+def test_varlen_many_sequences(nseq, uses_list, bwd_mode):
+    """Many short packed sequences: up to the ranking bound the key-block
+    kernel walks one longest-first list over all key blocks; past it, the
+    per-sequence order. Both must match the oracle."""
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.integers(0, 100, nseq)]
+    hq, hkv, d = 2, 1, 64
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=47, lengths=lengths)
+    cu = inp["cu_seqlens_q"].tolist()
+    p = ea.make_params(nseq, max(lengths), max(lengths), hq, hkv, d, 0.125, True,
+                       total_q=cu[-1], total_k=cu[-1])
+    assert (ea.varlen_key_order(p, cu, cu) is not None) == uses_list
+    g = _dev(inp)
+    mx = max(lengths)
+    o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], mx, mx,
+                           causal=True, softmax_scale=0.125)
+    dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
+                               g["cu_seqlens_k"], mx, mx, causal=True, softmax_scale=0.125,
+                               options=bwd_mode)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], 0.125, True,
+                                              inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    what = f"varlen {nseq} sequences"
+    check_o(o, o_ref, what)
+    check_lse(lse, lse_ref, what)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], 0.125, True,
+                                    inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    check_grads((dq, dk, dv), ref, what)
+
+
 def test_varlen_non_causal_different_key_lengths(bwd_mode):
     lq, lk = [40, 300, 7], [260, 0, 90]
     hq, hkv, d = 2, 1, 64
