@@ -169,8 +169,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   // 256-key block, whose column holds 16 KiB per 32-query sub-row from its
   // first written row on): two 1 KiB fragments (16-row halves tt of the
   // sub-tile), each the 64 lanes' packed B operands of dK^T in lane order,
-  // except that lanes 32..63 swap 64-byte halves (slot L ^ 4), which makes
-  // the dQ kernel's transposing reads conflict-free. The column of the
+  // except that lanes 32..63 swap 64-byte halves (slot L ^ 4) and the second
+  // fragment swaps 128-byte halves (slot ^ 8): the dQ kernel's transposing
+  // reads then cover one 128-byte bank window per 16 lanes (L ^ 4) and, for
+  // the 16-lane groups serviced together, the two halves of a 256-byte bank
+  // line (^ 8), so they are conflict-free. The column of the
   // compute cursor's head starts at ds_col (ds_rng bytes; 0 for a packed
   // sequence whose regions did not fit the area, which drops its stores);
   // its step's sub-rows at byte ds_soff of it. The regions of the group's
@@ -345,7 +348,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   // Per-lane addresses of the dQ path, recomputed where they are used from
   // an opaque lane id (kept live across the step they would cost VGPRs the
   // dP and dV^T phases need). dS image writes: this wave's sub-columns
-  // w KB .. w KB + KB - 1, lane slot L ^ 4 (L >= 32) as in the stored layout.
+  // w KB .. w KB + KB - 1, in the stored layout (16-byte slot L ^ 4 (L >= 32)
+  // ^ 8 tt in half tt; the image's base is 256-byte aligned, so the slot's
+  // bit 3 is address bit 7).
   auto dq_write_addr = [&](uint32_t par) -> uint32_t {
     const int ln = opaque_lane_id();
     return lds_s + par + w * KB * 2048 + ((ln ^ ((ln >> 5) << 2)) << 4);
@@ -358,7 +363,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     const int ln = opaque_lane_id();
     const int l16 = ln & 15, lh = (ln >> 4) & 1, lg = ln >> 5, sl = l16 & 1;
     ra = lds_s + par + qb_w * NKC * 2048 + lh * 1024 +
-         (32 * sl + ((4 * lg + (l16 >> 2)) ^ (4 * sl))) * 16 + ((l16 >> 1) & 1) * 8;
+         (32 * sl + ((4 * lg + (l16 >> 2)) ^ (4 * sl)) + 8 * lh) * 16 + ((l16 >> 1) & 1) * 8;
     const int lr = 4 * lg + (l16 >> 2), lc = 2 * lh + ((l16 & 3) >> 1);
     const int lt = lr * RB + 16 * (lc ^ dma_swz<D>(lr)) + 8 * (l16 & 1);
     k0 = lds_k + (lt ^ (64 * db_w));
@@ -472,7 +477,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
           sb[qb][k2][j >> 1] = pack_half(dp[qb][k2], j >> 1);
           pin8(sb[qb][k2][j >> 1]);
           if constexpr (DQ)
-            lds_st16(dsw + qb * NKC * 2048 + k2 * 2048 + (j >> 1) * 1024, sb[qb][k2][j >> 1]);
+            lds_st16(((j >> 1) ? (dsw ^ 128) : dsw) + qb * NKC * 2048 + k2 * 2048 + (j >> 1) * 1024,
+                     sb[qb][k2][j >> 1]);
         }
       }
     };
@@ -483,7 +489,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     auto dq_fetch = [&](int jq) {
       const int kc = jq >> 1, tt = jq & 1;
       const uint32_t so = kc * 2048 + 256 * tt, ko = (kc * 32 + 16 * tt) * RB;
-      qa[jq % 3] = cat8(ds_read_tr(dsr + so), ds_read_tr(dsr + so + 128));
+      qa[jq % 3] = cat8(ds_read_tr(dsr + so), ds_read_tr((dsr ^ 128) + so));
       qk[jq % 3] = cat8(ds_read_tr(dk0 + ko), ds_read_tr(dk1 + ko));
     };
 #pragma unroll
@@ -561,7 +567,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
             // lane offset recomputed here from an opaque lane id: kept live
             // across the step it costs a VGPR
             const int ln = opaque_lane_id();
-            const int ds_voff = (ln ^ ((ln >> 5) << 2)) << 4;
+            const int ds_voff = ((ln ^ ((ln >> 5) << 2)) ^ (8 * tt)) << 4;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
               buf_store16_nt(dr, ds_voff, so + qb * 16384 + kb * 2048 + tt * 1024, sb[qb][kb][tt]);

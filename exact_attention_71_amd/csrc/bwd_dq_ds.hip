@@ -146,39 +146,57 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const Tile& t, cha
     at[db][1] = lds_k + (a_t ^ (64 * db + 32)) + 8 * RB;
   }
   // dS^T by transposing reads. In a stored sub-tile, 16-row half tt' holds at
-  // 16-byte slot L ^ (4 (L >= 32)) the chunks (queries 16tt' + 4g' + 0..3,
-  // then + 8) of key c' for lane L = c' + 32g'. The B operand wants, in lane
-  // (query 16dh + s16, g), keys 16tt + 4g + j (slots 0..3) and 16tt + 8 + 4g + j
-  // (slots 4..7), the k order of K^T above. So lane s16 of the group points at
-  // the chunk of key 16tt + 8hh + 4g + s16/4 and queries 16dh + 4(s16%4) .. +3:
-  // tt' = dh, chunk (s16 >> 1) & 1, g' = s16 & 1. Per 16-lane group the 16
-  // chunks cover one 128-byte bank window.
+  // 16-byte slot L ^ (4 (L >= 32)) ^ (8 tt') the chunks (queries 16tt' + 4g' +
+  // 0..3, then + 8) of key c' for lane L = c' + 32g'. The B operand wants, in
+  // lane (query 16dh + s16, g), keys 16tt + 4g + j (slots 0..3) and 16tt + 8 +
+  // 4g + j (slots 4..7), the k order of K^T above. So lane s16 of the group
+  // points at the chunk of key 16tt + 8hh + 4g + s16/4 and queries 16dh +
+  // 4(s16%4) .. +3: tt' = dh, chunk (s16 >> 1) & 1, g' = s16 & 1. Per 16-lane
+  // group the 16 chunks cover one 128-byte bank window, and the groups dh = 0
+  // and 1, which the transposing read services together, cover the two
+  // halves of a 256-byte bank line (the ^ 8 of half tt' = 1). The key group
+  // hh is slot bit 3 as well: bt reads hh = 0, bt ^ 128 reads hh = 1 (the
+  // region's base is 1 KiB aligned).
   const int sl = s16 & 1;
-  const int b_t = dh * 1024 + (32 * sl + ((4 * g + (s16 >> 2)) ^ (4 * sl))) * 16 + ((s16 >> 1) & 1) * 8;
-  const uint32_t bt = lds_s + w * DSW + b_t;
+  const int b_t = dh * 1024 + (32 * sl + ((4 * g + (s16 >> 2)) ^ (4 * sl)) + 8 * dh) * 16 +
+                  ((s16 >> 1) & 1) * 8;
+  const uint32_t bt = lds_s + w * DSW + b_t, bt1 = bt ^ 128;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   // Key tile in K ring slot st and dS ring slot sd, its first NV sub-tiles
-  // (the visible ones).
+  // (the visible ones): NV * 2 * NDB MFMAs x = ((sub-tile kb, 16-key half tt),
+  // dim block db). Operands stream ahead of use (LDS reads return in order):
+  // K^T two MFMAs ahead, dS^T one (kb, tt) group ahead, so each MFMA waits
+  // only for reads issued two MFMAs earlier.
   auto body = [&](int st, int sd, auto nv) {
     constexpr int NV = decltype(nv)::value;
+    constexpr int NX = NV * 2 * NDB;
     const uint32_t ko = st * TILE, so = sd * NW * DSW;
+    auto fetch_a = [&](int x) -> bf16x8 {   // K^T of MFMA x
+      const int y = x / NDB, db = x % NDB;
+      const uint32_t off = ko + ((y >> 1) * 32 + 16 * (y & 1)) * RB;
+      return cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
+    };
+    auto fetch_b = [&](int y) -> bf16x8 {   // dS^T of group y = 2 kb + tt
+      const uint32_t bo = so + (y >> 1) * 2048 + 256 * (y & 1);
+      return cat8(ds_read_tr(bt + bo), ds_read_tr(bt1 + bo));
+    };
+    bf16x8 b = fetch_b(0), bn = b;
+    bf16x8 a0 = fetch_a(0), a1 = fetch_a(1);
 #pragma unroll
-    for (int kb = 0; kb < NV; ++kb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint32_t bo = so + kb * 2048 + 256 * tt;
-        const bf16x8 b = cat8(ds_read_tr(bt + bo), ds_read_tr(bt + bo + 128));
-        const uint32_t off = ko + (kb * 32 + 16 * tt) * RB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
-          acc[db] = mfma32(a, b, acc[db]);
-        }
-      }
+    for (int x = 0; x < NX; ++x) {
+      const int y = x / NDB, db = x % NDB;
+      const bf16x8 a = a0;
+      a0 = a1;
+      if (x + 2 < NX) a1 = fetch_a(x + 2);
+      if (db == 0 && y + 1 < 2 * NV) bn = fetch_b(y + 1);
+      acc[db] = mfma32(a, b, acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (db == NDB - 1) b = bn;
+    }
   };
   // ---- prologue, in issue order: dS of tiles 0 .. NSD - 2, K of tiles 0
   // and 1; wait for K of tile 0 (and so for everything issued before it).

@@ -4,14 +4,17 @@ The dK/dV kernel stores each 32-query x 32-key dS sub-tile as two 1 KiB
 fragments (16-query halves tt'): lane L = key c' + 32 g' writes its packed
 dK^T B operand, 8 bf16 whose element e is query 16 tt' + 8 (e // 4) + 4 g' +
 e % 4 (register 8 tt' + e of the S accumulator: row 8 (i // 4) + 4 g + i % 4),
-at 16-byte slot L ^ 4 (L >= 32). The dQ kernel reads it back with
+at 16-byte slot L ^ 4 (L >= 32) ^ 8 tt'. The dQ kernel reads it back with
 ds_read_b64_tr_b16, which gives lane i of each 16-lane group element i % 4 of
 the 8 bytes addressed by lanes 4 j + i // 4, as its element j. These tests
 replay both sides in numpy and check that every lane of every dQ^T B operand
 receives dS[query][key] for its own query (16 dh + lane % 16) and the keys the
 K^T A operand holds in the same k slots (16 tt + 4 g + j, then + 8), and that
-the 16 addresses of each 16-lane group fall in distinct 8-byte slots of one
-128-byte bank window. No GPU is used.
+the reads are free of bank conflicts: LDS has 64 banks of 4 bytes, and a
+64-bit read is serviced 32 lanes at a time, so the 32 addresses of each half
+of the wavefront must fall in distinct 8-byte slots of one 256-byte line (the
+K^T reads of the same kernels are laid out that way, and measure no
+conflicts). No GPU is used.
 """
 import numpy as np
 
@@ -22,7 +25,7 @@ def _store_subtile(ds):
     for tt in range(2):
         for lane in range(64):
             key, g = lane % 32, lane // 32
-            slot = lane ^ (4 if lane >= 32 else 0)
+            slot = lane ^ (4 if lane >= 32 else 0) ^ (8 * tt)
             for e in range(8):
                 q = 16 * tt + 8 * (e // 4) + 4 * g + e % 4
                 words[(tt * 1024 + slot * 16 + 2 * e) // 2] = ds[q, key]
@@ -42,14 +45,27 @@ def _tr_read(words, addr):
 
 def _read_addresses(tt, hh):
     """Byte addresses the dQ kernel's lanes give the transposing read of
-    16-key half tt, key group hh (0: slots 0..3, 1: slots 4..7)."""
+    16-key half tt, key group hh (0: slots 0..3, 1: slots 4..7): bt, or
+    bt ^ 128 for hh = 1, plus 256 tt."""
     addr = []
     for lane in range(64):
         s16, dh, g = lane & 15, (lane >> 4) & 1, lane >> 5
         sl = s16 & 1
-        b_t = dh * 1024 + (32 * sl + ((4 * g + (s16 >> 2)) ^ (4 * sl))) * 16 + ((s16 >> 1) & 1) * 8
-        addr.append(b_t + (16 * tt + 8 * hh) * 16)
+        b_t = dh * 1024 + (32 * sl + ((4 * g + (s16 >> 2)) ^ (4 * sl)) + 8 * dh) * 16 + \
+            ((s16 >> 1) & 1) * 8
+        addr.append((b_t ^ (128 * hh)) + 256 * tt)
     return addr
+
+
+def _ways(addr):
+    """Most distinct 8-byte words one bank pair serves in one 32-lane pass."""
+    worst = 0
+    for half in (addr[:32], addr[32:]):
+        per = {}
+        for a in half:
+            per.setdefault((a % 256) // 8, set()).add(a // 8)
+        worst = max(worst, max(len(v) for v in per.values()))
+    return worst
 
 
 def test_every_stored_element_lands_once():
@@ -88,14 +104,33 @@ def test_k_operand_uses_the_same_k_order():
                             [16 * tt + 8 + 4 * g + j for j in range(4)]
 
 
-def test_reads_are_bank_conflict_free_per_16_lanes():
+def test_reads_are_bank_conflict_free():
     for tt in range(2):
         for hh in range(2):
             addr = _read_addresses(tt, hh)
+            assert all(x % 8 == 0 for x in addr)
             for grp in range(4):
                 a = addr[16 * grp:16 * grp + 16]
-                assert all(x % 8 == 0 for x in a)
                 assert len({(x % 128) // 8 for x in a}) == 16, (tt, hh, grp)
+            for half in (addr[:32], addr[32:]):
+                assert len({(x % 256) // 8 for x in half}) == 32, (tt, hh)
+            assert _ways(addr) == 1
+
+
+def test_without_the_half_swap_the_32_lane_passes_conflict():
+    """The ^ 8 of the second 16-row half is what puts the dh = 0 and dh = 1
+    groups of one 32-lane pass on different 128-byte halves of the bank
+    line: read at the unswapped addresses every bank pair serves two words."""
+    for tt in range(2):
+        for hh in range(2):
+            addr = []
+            for lane in range(64):
+                s16, dh, g = lane & 15, (lane >> 4) & 1, lane >> 5
+                sl = s16 & 1
+                b_t = dh * 1024 + (32 * sl + ((4 * g + (s16 >> 2)) ^ (4 * sl))) * 16 + \
+                    ((s16 >> 1) & 1) * 8
+                addr.append(b_t + 128 * hh + 256 * tt)
+            assert _ways(addr) == 2
 
 
 def test_without_the_lane_swap_the_reads_conflict():

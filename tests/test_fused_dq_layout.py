@@ -4,7 +4,7 @@ checked on the CPU.
 Each wave writes the bf16 dS fragments it packs for dK^T (lane L = key
 c + 32 g of its 32-key sub-column holds queries 16 tt + 4 g + 0..3 and
 16 tt + 8 + 4 g + 0..3) into an LDS image: per 32-query block qb, 8 sub-tiles
-of 32 keys (2 KiB, halves tt of 1 KiB), lane slot L ^ 4 (L >= 32). The K
+of 32 keys (2 KiB, halves tt of 1 KiB), lane slot L ^ 4 (L >= 32) ^ 8 tt. The K
 tile sits row-major in LDS with the row swizzle dma_swz (16-byte slot pos of
 row r holds logical chunk pos ^ dma_swz(r)). Wave w then forms the 32 x 32
 dQ unit (query block w // (d / 32), dim block w % (d / 32)) as sixteen
@@ -13,7 +13,8 @@ from ds_read_b64_tr_b16 at the lane addresses the kernel computes. The test
 replays the writes and the reads in numpy, with the MFMA's operand layout
 (lane l: A[l % 32][8 (l // 32) + e], B[8 (l // 32) + e][l % 32]), and checks
 every unit equals dS K; it also checks that every LDS access stays inside
-its region. No GPU is used.
+its region and that the dS reads are free of bank conflicts (64 banks of 4
+bytes, a 64-bit read serviced 32 lanes at a time). No GPU is used.
 """
 import numpy as np
 import pytest
@@ -67,8 +68,8 @@ def test_fused_dq_units_equal_ds_times_k(d, bm):
                         key, g = 32 * (w * kb_per_wave + kb) + ln % 32, ln // 32
                         rows = [16 * tt + 4 * g + r for r in range(4)] + \
                                [16 * tt + 8 + 4 * g + r for r in range(4)]
-                        a = (lds_s + par + w * kb_per_wave * 2048 + ((ln ^ ((ln >> 5) << 2)) << 4)
-                             + qb * nkc * 2048 + kb * 2048 + tt * 1024)
+                        dsw = lds_s + par + w * kb_per_wave * 2048 + ((ln ^ ((ln >> 5) << 2)) << 4)
+                        a = (dsw ^ (128 * tt)) + qb * nkc * 2048 + kb * 2048 + tt * 1024
                         assert lds_s + par <= a and a + 16 <= lds_s + par + dsb
                         lds[a // 2: a // 2 + 8] = [ds[32 * qb + q, key] for q in rows]
     assert not np.isnan(lds[:kt // 2]).any()
@@ -81,7 +82,8 @@ def test_fused_dq_units_equal_ds_times_k(d, bm):
             l16, lh, lg = ln & 15, (ln >> 4) & 1, ln >> 5
             sl = l16 & 1
             ra.append(lds_s + par + qb_w * nkc * 2048 + lh * 1024
-                      + (32 * sl + ((4 * lg + (l16 >> 2)) ^ (4 * sl))) * 16 + ((l16 >> 1) & 1) * 8)
+                      + (32 * sl + ((4 * lg + (l16 >> 2)) ^ (4 * sl)) + 8 * lh) * 16
+                      + ((l16 >> 1) & 1) * 8)
             lr, lc = 4 * lg + (l16 >> 2), 2 * lh + ((l16 & 3) >> 1)
             lt = lr * rb + 16 * (lc ^ _dma_swz(d, lr)) + 8 * (l16 & 1)
             k0.append(lds_k + (lt ^ (64 * db_w)))
@@ -91,8 +93,11 @@ def test_fused_dq_units_equal_ds_times_k(d, bm):
             kc, tt = jq >> 1, jq & 1
             so, ko = kc * 2048 + 256 * tt, (kc * 32 + 16 * tt) * rb
             img = (lds_s + par, lds_s + par + dsb)
-            a_op = np.concatenate([_tr_read(lds, [x + so for x in ra], *img),
-                                   _tr_read(lds, [x + so + 128 for x in ra], *img)], 1)
+            a0, a1 = [x + so for x in ra], [(x ^ 128) + so for x in ra]
+            for addr in (a0, a1):   # one 256-byte bank line per 32-lane pass
+                for half in (addr[:32], addr[32:]):
+                    assert len({(x % 256) // 8 for x in half}) == 32
+            a_op = np.concatenate([_tr_read(lds, a0, *img), _tr_read(lds, a1, *img)], 1)
             b_op = np.concatenate([_tr_read(lds, [x + ko for x in k0], lds_k, lds_k + kt),
                                    _tr_read(lds, [x + ko for x in k1], lds_k, lds_k + kt)], 1)
             am, bmat = np.zeros((32, 16)), np.zeros((16, 32))
