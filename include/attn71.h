@@ -141,6 +141,7 @@ typedef struct attn_options {
 
 /* A varlen plan: the schedule tables of one packed batch (the order of the
  * sequences longest first, tile and block prefix sums, stored-dS offsets,
+ * the longest-first list of all key blocks (attn_varlen_key_order),
  * tile-ticket counters) for every kernel, built once by
  * attn_varlen_plan_build and reused by any number of attn_fwd_varlen /
  * attn_bwd_varlen / attn_bwd_phases calls on the same sequences (blog page,
@@ -233,8 +234,8 @@ int32_t attn_bwd_design(const attn_params* p, int32_t varlen);
 int32_t attn_bwd_head_split(const attn_params* p, int32_t varlen);
 
 /* Bytes of device memory a varlen plan for these parameters needs (they
- * depend on the sequence count only); (size_t)-1 for parameters the varlen
- * calls would reject. */
+ * depend on the sequence count, and through the key-block list on total_k
+ * and head_dim); (size_t)-1 for parameters the varlen calls would reject. */
 size_t attn_varlen_plan_size(const attn_params* p);
 
 /* Builds a varlen plan for the packed batch described by p and the device
