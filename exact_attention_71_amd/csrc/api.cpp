@@ -404,7 +404,9 @@ attn_status fwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   attn_status st = check_params(p, varlen);
   if (st != ATTN_OK) return st;
   if (varlen && !cu_k) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARGUMENT;
+  // a tensor with no elements may be a null pointer (no kernel touches it)
+  const bool has_q = rows_q_of(p, varlen) > 0, has_k = rows_k_of(p, varlen) > 0;
+  if (has_q && (!q || !o || (has_k && (!k || !v)))) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARGUMENT;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARGUMENT;
   st = check_plan(p, varlen);
@@ -479,16 +481,23 @@ attn_status bwd_impl(const attn_params* p, const int32_t* cu_q, const int32_t* c
   const bool pre = phases & ATTN_BWD_PREPROCESS, main = phases & ATTN_BWD_MAIN,
              post = (phases & ATTN_BWD_POSTPROCESS) && fused_mode,
              dqk = (phases & ATTN_BWD_DQ) && !fused_mode;
-  if (pre && (!o || !dout || !aligned16(o) || !aligned16(dout))) return ATTN_ERR_INVALID_ARGUMENT;
-  if ((main || dqk) && (!q || !k || !v || !dout || !lse)) return ATTN_ERR_INVALID_ARGUMENT;
+  // a tensor with no elements may be a null pointer: with no query rows no
+  // kernel reads Q, O, dO or LSE or writes dQ, with no keys none reads K, V
+  // or writes dK, dV
+  const bool has_q = rows_q_of(p, varlen) > 0, has_k = rows_k_of(p, varlen) > 0;
+  if (pre && has_q && (!o || !dout)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (pre && (!aligned16(o) || !aligned16(dout))) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((main || dqk) && ((has_q && (!q || !dout || !lse)) || (has_k && (!k || !v))))
+    return ATTN_ERR_INVALID_ARGUMENT;
   if ((main || dqk) && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
                         (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_INVALID_ARGUMENT;
-  if (main && (!dk || !dv || !aligned16(dk) || !aligned16(dv))) return ATTN_ERR_INVALID_ARGUMENT;
-  if ((post || dqk) && (!dq || !aligned16(dq))) return ATTN_ERR_INVALID_ARGUMENT;
+  if (main && ((has_k && (!dk || !dv)) || !aligned16(dk) || !aligned16(dv)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if ((post || dqk) && ((has_q && !dq) || !aligned16(dq))) return ATTN_ERR_INVALID_ARGUMENT;
   if (ws_bytes < wl.total) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!ws) return ATTN_ERR_INVALID_ARGUMENT;
-  if (p->batch == 0 || !launch) return ATTN_OK;
+  if (p->batch == 0 || (!has_q && !has_k) || !launch) return ATTN_OK;
   st = check_device();
   if (st != ATTN_OK) return st;
 

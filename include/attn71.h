@@ -16,7 +16,10 @@
  *
  * Conventions shared by every call
  *   - q, k, v, o, dout, dq, dk, dv are bfloat16, contiguous, head dim
- *     innermost, 16-byte aligned device pointers.
+ *     innermost, 16-byte aligned device pointers. A tensor with no elements
+ *     (no query rows: q, o, dout, dq, lse; no keys: k, v, dk, dv) may be
+ *     null: no kernel touches it. Rows that see no key get O = 0, LSE =
+ *     -inf and dQ = 0; keys that no row sees get dK = dV = 0.
  *     Fixed length: BSHD, q/o/dout/dq [batch, seqlen_q, num_heads_q, head_dim],
  *     k/v/dk/dv [batch, seqlen_k, num_heads_kv, head_dim].
  *     Packed variable length (the *_varlen calls): THD, q [total_q, Hq, d],

@@ -113,6 +113,20 @@ def test_empty_batch_is_a_no_op():
     assert lib.attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 0
 
 
+def test_tensors_with_no_elements_may_be_null():
+    """No query rows and no keys: every data pointer may be null (PyTorch hands
+    out null for tensors with no elements) and the calls are no-ops."""
+    lib = ea.load()
+    p = _p(seqlen_q=0, seqlen_k=0)
+    ws = (ctypes.c_uint8 * 4096)()
+    assert lib.attn_fwd(ctypes.byref(p), None, None, None, None, None, None, 0, None) == 0
+    assert lib.attn_bwd(ctypes.byref(p), *([None] * 9), ws, 4096, None) == 0
+    # query rows present: Q and O must be given
+    q_only = _p(seqlen_k=0)
+    assert lib.attn_fwd(ctypes.byref(q_only), None, None, None, None, None, None, 0,
+                        None) == INVALID
+
+
 def test_workspace_sizes():
     rows, hq, hkv, d = 2 * 300, 4, 2, 128
     p = _p(options=dict(bwd_design=ea.BWD_RECOMPUTE, head_split=1))

@@ -159,6 +159,27 @@ def test_varlen_many_sequences(nseq, uses_list, bwd_mode):
     check_grads((dq, dk, dv), ref, what)
 
 
+@pytest.mark.parametrize("lq,lk", [([0, 0, 0], [0, 0, 0]), ([5, 300, 0], [0, 0, 0]),
+                                   ([0, 0, 0], [70, 0, 260])])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_with_no_queries_or_no_keys(lq, lk, causal, bwd_mode):
+    """Packed batches whose queries or keys are all empty (tensors with no
+    elements, null data pointers): rows that see no key give O = 0, LSE = -inf
+    and dQ = 0; keys that no query sees give dK = dV = 0."""
+    hq, hkv, d = 4, 2, 128
+    inp = make_inputs(0, 0, 0, hq, hkv, d, seed=53, lengths=lq, lengths_k=lk)
+    g = _dev(inp)
+    o, lse = ea.fwd_varlen(g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+                           max(lq), max(lk), causal=causal, softmax_scale=0.1)
+    dq, dk, dv = ea.bwd_varlen(g["q"], g["k"], g["v"], o, g["do"], lse, g["cu_seqlens_q"],
+                               g["cu_seqlens_k"], max(lq), max(lk), causal=causal,
+                               softmax_scale=0.1, options=bwd_mode)
+    torch.cuda.synchronize()
+    assert o.shape == g["q"].shape and dk.shape == g["k"].shape
+    assert torch.all(o == 0) and torch.all(dq == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
 def test_varlen_non_causal_different_key_lengths(bwd_mode):
     lq, lk = [40, 300, 7], [260, 0, 90]
     hq, hkv, d = 2, 1, 64
