@@ -180,6 +180,20 @@ def test_varlen_with_no_queries_or_no_keys(lq, lk, causal, bwd_mode):
     assert torch.all(dk == 0) and torch.all(dv == 0)
 
 
+@pytest.mark.parametrize("sq,sk", [(200, 0), (0, 200), (0, 0)])
+def test_fixed_length_with_no_queries_or_no_keys(sq, sk, bwd_mode):
+    b, hq, hkv, d = 2, 4, 2, 64
+    inp = make_inputs(b, sq, sk, hq, hkv, d, seed=57)
+    g = _dev(inp)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=True, softmax_scale=0.1)
+    dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=True,
+                        softmax_scale=0.1, options=bwd_mode)
+    torch.cuda.synchronize()
+    assert o.shape == (b, sq, hq, d) and dk.shape == (b, sk, hkv, d)
+    assert torch.all(o == 0) and torch.all(dq == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
 def test_varlen_non_causal_different_key_lengths(bwd_mode):
     lq, lk = [40, 300, 7], [260, 0, 90]
     hq, hkv, d = 2, 1, 64
