@@ -18,8 +18,11 @@ Entry points mirror the C ABI in ``include/attn71.h``:
 
 Design and tuning choices are per call: ``options`` is a dict of
 ``attn_options`` fields (bwd_design, tile_order, one_shot_grid,
-exp_emulation, tau, spin_limit, ds_budget); missing fields take the
-library's defaults. Nothing is process-global.
+exp_emulation, tau, spin_limit, ds_budget, head_split); missing fields take
+the library's defaults. Nothing is process-global. A packed batch's
+schedule can be built once with ``varlen_plan`` and passed to every varlen
+call (``plan=``); ``bwd_noalloc`` runs the backward on the library's own
+device scratch for callers that cannot allocate.
 """
 from __future__ import annotations
 
