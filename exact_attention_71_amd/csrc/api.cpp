@@ -101,7 +101,9 @@ attn_status check_params(const attn_params* p, bool varlen) {
     if (p->block_mask_stride_b < 0 || p->block_mask_stride_h < 0 ||
         (reinterpret_cast<uintptr_t>(p->block_mask) & 3u))
       return ATTN_ERR_INVALID_ARGUMENT;
-    if (varlen || o.exp_emulation != 0 || mask_bytes(p) > kMaxExtent) return ATTN_ERR_UNSUPPORTED;
+    if (varlen || o.exp_emulation != 0 || mask_bytes(p) > kMaxExtent ||
+        cdiv(p->seqlen_k, 64) > kMaxMaskTiles)   // the kernels' visible-tile lists
+      return ATTN_ERR_UNSUPPORTED;
   }
   // one (sequence, head) slab must stay within 32-bit byte offsets
   const int64_t d = p->head_dim;

@@ -32,7 +32,8 @@ constexpr int dq_smem_bytes() { return 2 * 3 * BN * 2 * D; }
 
 // One tile: query block t.block of (sequence t.seq, query head t.head).
 template <int D, int NW, int BN, bool MASK>
-__device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char* smem) {
+__device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char* smem,
+                                        uint16_t* vis, int* vis_n) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;            // k-steps of S^T and dP^T
@@ -85,6 +86,25 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
     mrow = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
         (int64_t)t.seq * p.mask.sb + (int64_t)h * p.mask.sh + (int64_t)(qw0 / kMaskBlock) * p.mask.nkb));
   }
+  // block mask: the key tiles with a set block in some mask row of this
+  // workgroup's rows, listed by wave 0 (mask_list_tiles); the loop walks only
+  // those, and a wave still skips a listed tile its own rows do not see
+  int nv = n_tiles;
+  if constexpr (MASK) {
+    if (w == 0) {
+      const int r0 = m0 / kMaskBlock, r1 = (imin(m0 + BM, lq) - 1) / kMaskBlock;
+      const uint32_t mb0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          (int64_t)t.seq * p.mask.sb + (int64_t)h * p.mask.sh + (int64_t)r0 * p.mask.nkb));
+      const int cnt = mask_list_tiles(mrs, mb0, p.mask.nkb, r0, r1, n_tiles, BN, kMaskBlock, vis);
+      if (lane == 0) *vis_n = cnt;
+    }
+    __syncthreads();
+    nv = __builtin_amdgcn_readfirstlane(*vis_n);
+  }
+  auto tile_of = [&](int j) -> int {   // key tile of loop position j
+    if constexpr (MASK) return __builtin_amdgcn_readfirstlane(static_cast<int>(vis[j]));
+    return j;
+  };
 
   // ---- this lane's query row: Q and dO as B operands, LSE log2 e and D as scalars
   const int64_t qbytes = ((int64_t)(lq - 1) * qstride + D) * 2;
@@ -119,11 +139,11 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
     const int r = slot / SPR, pos = slot % SPR;
     voffs[i] = (r * (int)kstride + (pos ^ dma_swz<D>(r)) * 8) * 2;
   }
-  auto issue = [&](int n) {
-    const int64_t t0 = (int64_t)n * BN * kstride;
+  auto issue = [&](int j) {   // loop position j into ring slot j % NS
+    const int64_t t0 = (int64_t)tile_of(j) * BN * kstride;
     const rsrc_t kr = make_rsrc(kbase + t0, kv_bytes - 2 * t0);
     const rsrc_t vr = make_rsrc(vbase + t0, kv_bytes - 2 * t0);
-    const int st = n % NS;
+    const int st = j % NS;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const uint32_t dst = lds_k + st * TILE + (i * NW + w) * 1024;
@@ -263,14 +283,14 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
   // (where the ring loads, which it cannot see, would make it stall).
 #pragma unroll
   for (int n = 0; n < NS - 1; ++n)
-    if (n < n_tiles) issue(n);
+    if (n < nv) issue(n);
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int st = n % NS;
-    if (n + NS - 1 < n_tiles) issue(n + NS - 1);
-    const int k0 = n * BN;
+  for (int j = 0; j < nv; ++j) {
+    const int st = j % NS;
+    if (j + NS - 1 < nv) issue(j + NS - 1);
+    const int k0 = tile_of(j) * BN;
     // whole wave below the diagonal's start, or a cleared mask block: no
     // visible pair in this tile
     bool active = !(causal && k0 > qw0 + 31 + shift);
@@ -278,7 +298,7 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, const Tile& t, char*
     const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + shift);
     if (active) tile_body(k0, need_mask);
     advance_slot(st);
-    if (n + 1 < n_tiles) wait_next(n + NS - 1 < n_tiles);
+    if (j + 1 < nv) wait_next(j + NS - 1 < nv);
   }
 
   // ---- dQ = alpha * dQ^T, bf16, this lane's query row
@@ -301,6 +321,8 @@ template <int D, int NW, int BN, bool MASK>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_smem_bytes<D, BN>()];
   __shared__ int ticket;
+  __shared__ uint16_t vis[MASK ? kMaxMaskTiles : 1];   // block mask: visible key tiles
+  __shared__ int vis_n;
   for (int r = 0;; ++r) {
     const BwdParams& p = kernel_args<BwdParams>();
     const int i = next_tile(r, p.ntiles_dq, p.nxcd, p.queue_dq, &ticket);
@@ -315,7 +337,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams) {
     } else {
       t = fwd_tile_fixed(i, p.sv.batch, p.hq, p.nm_dq, p.sec_dq, p.nxcd, p.natural != 0);
     }
-    dq_tile<D, NW, BN, MASK>(p, t, smem);
+    dq_tile<D, NW, BN, MASK>(p, t, smem, vis, &vis_n);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }

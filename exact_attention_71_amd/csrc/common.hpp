@@ -306,6 +306,32 @@ __device__ __forceinline__ bool mask_set(rsrc_t r, uint32_t byte_off) {
   return ((w >> ((byte_off & 3u) * 8u)) & 0xffu) != 0u;
 }
 
+// Block mask, one wavefront: the key tiles (bn keys each, tile n in mask
+// column n bn / mblk) in [0, n_tiles) whose block is set in any of the mask
+// rows r0 .. r1 (row r0 at byte mb0 of the mask buffer, rows stride bytes
+// apart), in ascending order into vis[]; returns their count (every lane).
+// Each lane tests one tile per round of 64; a ballot and a count of the
+// lower lanes place it. Bytes past the buffer's range read as zero.
+__device__ __forceinline__ int mask_list_tiles(rsrc_t r, uint32_t mb0, int stride, int r0, int r1,
+                                               int n_tiles, int bn, int mblk, uint16_t* vis) {
+  const int lane = static_cast<int>(__lane_id());
+  int base = 0;
+  for (int c0 = 0; c0 < n_tiles; c0 += 64) {
+    const int n = c0 + lane;
+    bool v = false;
+    if (n < n_tiles) {
+      const int col = n * bn / mblk;
+      for (int row = r0; row <= r1; ++row)
+        v = v || __builtin_amdgcn_raw_buffer_load_b8(
+                     r, static_cast<int>(mb0 + (row - r0) * stride + col), 0, 0) != 0;
+    }
+    const uint64_t bal = __ballot(v);
+    if (v) vis[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = static_cast<uint16_t>(n);
+    base += __builtin_popcountll(bal);
+  }
+  return base;
+}
+
 __device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, int voff, int soff) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return __builtin_bit_cast(bf16x8, x);

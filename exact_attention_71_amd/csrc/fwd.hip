@@ -62,10 +62,11 @@ constexpr int fwd_smem_bytes() { return 2 * fwd_ring_depth<D, BN>() * BN * 2 * D
 template <int D, int NW, int QB, int BN, int EMU, bool MASK>
 __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char* smem,
                                          bf16x8 (&qf)[QB][D / 16], int& s0, bool pre,
-                                         Tile nxt, bool has_nxt) {
-  // not at head_dim 256, whose scalar registers are already short: there every
-  // tile starts its ring at slot 0 and loads its own first tiles
-  constexpr bool XT = D <= 128;
+                                         Tile nxt, bool has_nxt, uint16_t* vis, int* vis_n) {
+  // not at head_dim 256, whose scalar registers are already short, and not
+  // with a block mask, whose tiles first list their visible key tiles: there
+  // every tile starts its ring at slot 0 and loads its own first tiles
+  constexpr bool XT = D <= 128 && !MASK;
   if constexpr (!XT) {
     s0 = 0;
     has_nxt = false;
@@ -112,6 +113,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
     mrow = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
         (int64_t)t.seq * p.mask.sb + (int64_t)h * p.mask.sh + (int64_t)(qw0 / kMaskBlock) * p.mask.nkb));
   }
+  // block mask: the key tiles with a set block in some mask row of this
+  // workgroup's rows, listed in ascending order by wave 0 (mask_list_tiles);
+  // the loop below walks only those. Waves still skip a listed tile whose
+  // block their own rows do not see.
+  int nv = n_tiles;
+  if constexpr (MASK) {
+    if (w == 0) {
+      const int r0 = m0 / kMaskBlock, r1 = (imin(m0 + BM, lq) - 1) / kMaskBlock;
+      const uint32_t mb0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          (int64_t)t.seq * p.mask.sb + (int64_t)h * p.mask.sh + (int64_t)r0 * p.mask.nkb));
+      const int cnt = mask_list_tiles(mrs, mb0, p.mask.nkb, r0, r1, n_tiles, BN, kMaskBlock, vis);
+      if (lane == 0) *vis_n = cnt;
+    }
+    __syncthreads();
+    nv = __builtin_amdgcn_readfirstlane(*vis_n);
+  }
+  // key tile of loop position j (the visible list with a mask)
+  auto tile_of = [&](int j) -> int {
+    if constexpr (MASK) return __builtin_amdgcn_readfirstlane(static_cast<int>(vis[j]));
+    return j;
+  };
   const int64_t qstride = (int64_t)p.hq * D, kstride = (int64_t)p.hkv * D;
   const float tau = keep_sgpr(p.tau);
   const bf16* __restrict__ qp = static_cast<const bf16*>(p.q);
@@ -159,7 +181,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       dma16(vr, dst + VT, voffs[i]);
     }
   };
-  auto issue = [&](int n) { issue_at(kbase, vbase, kv_bytes, n, (s0 + n) % NS); };
+  // loop position j: its key tile into ring slot (s0 + j) % NS
+  auto issue = [&](int j) { issue_at(kbase, vbase, kv_bytes, tile_of(j), (s0 + j) % NS); };
   // The next tile: its first key tile goes to slot (s0 + n_tiles) % NS, whose
   // last reader (this tile's key tile n_tiles - NS, or an earlier tile) has
   // passed a workgroup barrier by the start of this tile's last key tile; its
@@ -242,27 +265,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
     load_q(qs, lq, h, m0);
 #pragma unroll
     for (int n = 0; n < NS - 1; ++n)
-      if (n < n_tiles) issue(n);
+      if (n < nv) issue(n);
     wait_vm<0>();
   } else {
 #pragma unroll
     for (int n = 1; n < NS - 1; ++n)
-      if (n < n_tiles) issue(n);
+      if (n < nv) issue(n);
   }
   __builtin_amdgcn_s_barrier();
 
   // key tile n; the last one is a separate copy (LAST) that also loads the
   // next tile's first key tile and Q fragments, so that those loads sit
   // outside the loop and the compiler tracks no loop-carried load
-  auto k_tile = [&](int n, auto last_c) {
+  auto k_tile = [&](int j, auto last_c) {
     constexpr bool LAST = decltype(last_c)::value;
-    const int st = (s0 + n) % NS;
+    const int st = (s0 + j) % NS;
     if constexpr (LAST) {
       prefetch_kv();
     } else {
-      if (n + NS - 1 < n_tiles) issue(n + NS - 1);
+      if (j + NS - 1 < nv) issue(j + NS - 1);
     }
-    const int k0 = n * BN;
+    const int k0 = tile_of(j) * BN;
     bool active = !(causal && k0 > qw0 + 32 * QB - 1 + shift);
     // a cleared mask block: this wave skips the tile (no visible key in it)
     if constexpr (MASK) active = active && mask_set(mrs, mrow + static_cast<uint32_t>(k0 / kMaskBlock));
@@ -421,11 +444,11 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb][0] + acc[qb][1];
     }
     advance_slot(st);
-    if constexpr (!LAST) wait_next(n + NS - 1 < n_tiles);
+    if constexpr (!LAST) wait_next(j + NS - 1 < nv);
   };
-  for (int n = 0; n + 1 < n_tiles; ++n) k_tile(n, std::false_type{});
-  if (n_tiles > 0) k_tile(n_tiles - 1, std::true_type{});
-  if (n_tiles == 0) {
+  for (int j = 0; j + 1 < nv; ++j) k_tile(j, std::false_type{});
+  if (nv > 0) k_tile(nv - 1, std::true_type{});
+  if (nv == 0) {
     prefetch_kv();
     if (nxt_ok) load_q(nqs, nlq, nh, nm0);
   }
@@ -461,7 +484,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       }
     }
   }
-  s0 = XT ? (s0 + n_tiles) % NS : 0;
+  s0 = XT ? (s0 + nv) % NS : 0;
   return nxt_ok;
 }
 
@@ -472,6 +495,8 @@ template <int D, int NW, int QB, int BN, int EMU, bool MASK>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[fwd_smem_bytes<D, BN>()];
   __shared__ int ticket;
+  __shared__ uint16_t vis[MASK ? kMaxMaskTiles : 1];   // block mask: visible key tiles
+  __shared__ int vis_n;
   auto draw = [&](int& r, Tile& t) -> bool {   // every thread calls it (barriers)
     for (;;) {
       const FwdParams& p = kernel_args<FwdParams>();
@@ -496,7 +521,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdParams) {
   while (have) {
     const bool have_next = draw(r, nxt);
     const FwdParams& p = kernel_args<FwdParams>();
-    pre = fwd_tile<D, NW, QB, BN, EMU, MASK>(p, cur, smem, qf, s0, pre, nxt, have_next);
+    pre = fwd_tile<D, NW, QB, BN, EMU, MASK>(p, cur, smem, qf, s0, pre, nxt, have_next, vis,
+                                             &vis_n);
     __syncthreads();   // the next tile's loads reuse the ring slots
     cur = nxt;
     have = have_next;

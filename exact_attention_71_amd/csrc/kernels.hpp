@@ -22,6 +22,9 @@ struct SeqView {
 // b * sb + h * sh + i * nkb + j, one per 128 x 128 block of (query, key)
 // pairs; zero hides the block. mask == null: no mask.
 constexpr int kMaskBlock = 128;
+// key tiles a masked forward or dQ workgroup lists (its visible ones): the
+// host refuses masks over more than kMaxMaskTiles 64-key tiles
+constexpr int kMaxMaskTiles = 4096;
 struct MaskView {
   const uint8_t* mask;
   int64_t sb, sh;       // bytes between batches / query heads (0: shared)

@@ -191,8 +191,11 @@ typedef struct attn_params {
    * mask shared by the batches or heads). The pointer must be 4-byte aligned;
    * the mask is read in 4-byte words, so the buffer must hold its span rounded
    * up to a multiple of 4 bytes, at most 2^31 - 1; packed variable lengths, the
-   * stored-dS design (ATTN_BWD_AUTO then recomputes dQ) and exp_emulation are
-   * refused with a mask (ATTN_ERR_UNSUPPORTED). */
+   * stored-dS design (ATTN_BWD_AUTO then recomputes dQ), exp_emulation and
+   * seqlen_k above 4096 * 64 keys (the length of the visible-tile lists the
+   * forward and dQ kernels keep) are refused with a mask
+   * (ATTN_ERR_UNSUPPORTED). The forward and dQ kernels skip hidden key tiles
+   * entirely; the dK/dV kernel steps through them (masked to zero). */
   const uint8_t* block_mask;
   int64_t block_mask_stride_b, block_mask_stride_h;
 } attn_params;

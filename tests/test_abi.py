@@ -563,3 +563,7 @@ def test_block_mask_validation():
     pv = pm(total_q=600, total_k=600)
     assert lib.attn_fwd_varlen(ctypes.byref(pv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                1 << 20, None) == UNSUPPORTED
+    # the kernels list up to 4096 visible 64-key tiles per workgroup
+    # (null q: the first case passes the mask checks and fails on the pointer)
+    assert lib.attn_fwd(ctypes.byref(pm(seqlen_k=4096 * 64, sb=0, sh=0)), *args) == INVALID
+    assert lib.attn_fwd(ctypes.byref(pm(seqlen_k=4096 * 64 + 1, sb=0, sh=0)), *args) == UNSUPPORTED

@@ -59,6 +59,40 @@ def test_block_mask_matches_oracle(b, sq, sk, hq, hkv, d, causal, design):
         assert torch.all(dq.cpu().transpose(1, 2)[dead] == 0)
 
 
+@pytest.mark.parametrize("design", ["recompute", "fused"])
+@pytest.mark.parametrize("sq,sk,hkv,d,causal,window", [
+    (300, 9000, 2, 128, False, None), (300, 9000, 1, 256, False, None),
+    (600, 12000, 2, 64, False, None), (4096, 4096, 2, 128, True, 3)])
+def test_block_mask_over_many_key_tiles(sq, sk, hkv, d, causal, window, design):
+    """More key tiles than a wavefront has lanes (the kernels list the visible
+    ones 64 at a time), a sparse random mask or a band of blocks around the
+    diagonal (sliding window)."""
+    b, hq = 1, 2
+    inp = make_inputs(b, sq, sk, hq, hkv, d, seed=700 + sk + d)
+    if window is None:
+        m = _mask(b, hq, sq, sk, seed=sk + d, density=0.3)
+    else:
+        i = torch.arange(-(-sq // 128))[:, None]
+        j = torch.arange(-(-sk // 128))[None, :]
+        m = ((i - j).abs() <= window).expand(b, hq, -1, -1).contiguous()
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    scale = 1.0 / math.sqrt(d)
+    what = f"mask s{sq}/{sk} hkv{hkv} d{d} causal{causal} window{window} {design}"
+    print(f"[block mask] {what}", flush=True)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=causal, softmax_scale=scale,
+                    block_mask=m.to(DEV))
+    dq, dk, dv = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=causal,
+                        softmax_scale=scale, options=DESIGNS[design], block_mask=m.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal,
+                                              block_mask=m)
+    check_o(o, o_ref, what)
+    check_lse(lse, lse_ref, what)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal,
+                                    block_mask=m)
+    check_grads((dq, dk, dv), ref, what)
+
+
 def test_shared_mask_broadcasts_over_batches_and_heads():
     """A [1, 1, nqb, nkb] mask applies to every (batch, head) (strides 0)."""
     b, s, hq, d = 2, 640, 4, 128
