@@ -437,6 +437,39 @@ def measure(torch, ea, w, args, opts, cpu_budget: float) -> dict:
     return rec
 
 
+def ablation_block_sparse(torch, ea, args) -> dict:
+    """Block-sparse masks (synthesis page: block-sparse attention on the FA4
+    framework): the forward and the recomputing dQ kernel walk only the
+    visible key tiles, the dK/dV kernel only the (query head, mask row) pairs
+    with a visible block in its keys."""
+    from workloads import Workload, make_inputs
+    w = Workload("sparse", 3, 2, 16, 16, 8192, 128, True, "fwd+bwd")
+    inp = make_inputs(2, 8192, 8192, 16, 16, 128, seed=71005, device="cuda:0")
+    nb = 8192 // 128
+    i, j = torch.arange(nb)[:, None], torch.arange(nb)[None, :]
+    gen = torch.Generator().manual_seed(71005)
+    masks = {"none": None, "all_set": torch.ones(nb, nb, dtype=torch.bool),
+             "window4": (i - j).abs() <= 4,
+             "random30": torch.rand((nb, nb), generator=gen) < 0.3}
+    res = {}
+    causal_blocks = (j <= i)
+    for name, m in masks.items():
+        r = Runner(torch, ea, w, {"bwd_design": ea.BWD_RECOMPUTE}, inputs=inp)
+        if m is not None:
+            md = ea.prepare_block_mask(m[None, None].to("cuda:0"), 2, 16, 8192, 8192)
+            ea.set_block_mask(r.p, md)
+            r.mask_keep = md
+        ms, kms = r.timed_steps(args.warmup, args.steps)
+        vis = 1.0 if m is None else float((m & causal_blocks).sum() / causal_blocks.sum())
+        res[name] = {"visible_fraction": round(vis, 4), "fwd_ms": round(kms["fwd"], 4),
+                     "dkdv_ms": round(kms["bwd_main"], 4), "dq_ms": round(kms["bwd_dq"], 4)}
+        del r
+    out = dict(res, workload="B2 H16 S8192 d128 causal, recomputing dQ, "
+                             "one mask shared by batches and heads")
+    print(f"[bench] ablation block sparse: {out}", file=sys.stderr, flush=True)
+    return out
+
+
 def ablations(torch, ea, args) -> dict:
     """Schedule and design ablations the pages report for their own hardware."""
     from workloads import Workload, make_inputs, workload_flops, WORKLOADS
@@ -490,35 +523,7 @@ def ablations(torch, ea, args) -> dict:
     out["deterministic_vs_atomic"] = dict(res, workload="B1 H8 S16384 d128 causal")
     print(f"[bench] ablation det: {out['deterministic_vs_atomic']}", file=sys.stderr, flush=True)
     del inp
-    # block-sparse masks (synthesis page: block-sparse attention on the FA4
-    # framework): the forward and the recomputing dQ kernel walk only the
-    # visible key tiles; the dK/dV kernel still steps through hidden blocks
-    # (masked to zero)
-    w = Workload("sparse", 3, 2, 16, 16, 8192, 128, True, "fwd+bwd")
-    inp = make_inputs(2, 8192, 8192, 16, 16, 128, seed=71005, device="cuda:0")
-    nb = 8192 // 128
-    i, j = torch.arange(nb)[:, None], torch.arange(nb)[None, :]
-    gen = torch.Generator().manual_seed(71005)
-    masks = {"none": None, "all_set": torch.ones(nb, nb, dtype=torch.bool),
-             "window4": (i - j).abs() <= 4,
-             "random30": torch.rand((nb, nb), generator=gen) < 0.3}
-    res = {}
-    causal_blocks = (j <= i)
-    for name, m in masks.items():
-        r = Runner(torch, ea, w, {"bwd_design": ea.BWD_RECOMPUTE}, inputs=inp)
-        if m is not None:
-            md = ea.prepare_block_mask(m[None, None].to("cuda:0"), 2, 16, 8192, 8192)
-            ea.set_block_mask(r.p, md)
-            r.mask_keep = md
-        ms, kms = r.timed_steps(args.warmup, args.steps)
-        vis = 1.0 if m is None else float((m & causal_blocks).sum() / causal_blocks.sum())
-        res[name] = {"visible_fraction": round(vis, 4), "fwd_ms": round(kms["fwd"], 4),
-                     "dkdv_ms": round(kms["bwd_main"], 4), "dq_ms": round(kms["bwd_dq"], 4)}
-        del r
-    out["block_sparse"] = dict(res, workload="B2 H16 S8192 d128 causal, recomputing dQ, "
-                                             "one mask shared by batches and heads")
-    print(f"[bench] ablation block sparse: {out['block_sparse']}", file=sys.stderr, flush=True)
-    del inp
+    out["block_sparse"] = ablation_block_sparse(torch, ea, args)
     # forward sequence-length sweep, non-causal H16 d128, 16k tokens per batch
     # (digest page, sequence-length benchmark table: 1k .. 32k)
     sweep = {}

@@ -64,8 +64,43 @@ constexpr int dkdv_smem_bytes() {
 
 // One tile: the keys of key block t.block of (sequence t.seq, KV head t.head),
 // query heads of part `part` of the group (p.hsplit parts).
+// Block mask: the (query head h < gs, mask row r0 + rr < r0 + nrows) pairs
+// whose byte is set in one of the workgroup's ncols key columns (first byte
+// at mb0 + h sh + row nkb), head-major, as h << 16 | rr, written to rows[];
+// wave-uniform. Each lane tests one pair per round of 64; a ballot and a
+// count of the lower lanes place it. Returns the count; *n_first / *n_last:
+// listed pairs in row r0 / in row last_row.
+__device__ __forceinline__ int mask_list_rows(rsrc_t r, uint32_t mb0, uint32_t sh, uint32_t nkb,
+                                              int gs, int r0, int nrows, int ncols, int last_row,
+                                              int* rows, int* n_first, int* n_last) {
+  const int lane = static_cast<int>(__lane_id());
+  const int total = gs * nrows;
+  int base = 0, nf = 0, nl = 0;
+  for (int e0 = 0; e0 < total; e0 += 64) {
+    const int e = e0 + lane;
+    bool v = false;
+    int h = 0, rr = 0;
+    if (e < total) {
+      h = e / nrows;
+      rr = e - h * nrows;
+      const int off = static_cast<int>(mb0 + h * sh + (r0 + rr) * nkb);
+      v = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0) != 0 ||
+          (ncols > 1 && __builtin_amdgcn_raw_buffer_load_b8(r, off + 1, 0, 0) != 0);
+    }
+    const uint64_t bal = __ballot(v);
+    if (v) rows[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = h << 16 | rr;
+    base += __builtin_popcountll(bal);
+    nf += __builtin_popcountll(__ballot(v && rr == 0));
+    nl += __builtin_popcountll(__ballot(v && r0 + rr == last_row));
+  }
+  *n_first = nf;
+  *n_last = nl;
+  return base;
+}
+
 template <int D, int KB, int BM, bool DS, bool MASK, int DQ>
-__device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int part, char* smem) {
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int part, char* smem,
+                                          int* mrows, int* mstat) {
   static_assert(!(DS && MASK), "block masks run with the recomputing dQ kernel");
   static_assert(!(DS && DQ), "stored dS feeds the dQ kernel; DQ forms dQ here");
   constexpr int NW = 4, NT = NW * 64;
@@ -125,7 +160,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   const int m_first = causal ? imin(causal_row_begin(n0, shift) / BM, nm) : 0;
   const int per_head = nm - m_first;
   const int gs = p.group / p.hsplit;   // query heads of this part
-  const int n_steps = gs * per_head;
+  int n_steps = gs * per_head;
   const int wk0 = n0 + KPW * w;         // first key of this wave
 
   // ---- this wave's keys: K and V as B operands (key on the lane)
@@ -164,6 +199,32 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   // itself). Within one sequence the Q / dO byte offsets stay below 2^31.
   const int kvh0 = kvh * p.group + part * gs;   // first query head of the part
   int i_h = 0;
+  int c_h = 0;                                  // query head of the compute cursor, from kvh0
+  // CMP (block mask, no chain): the cursors walk the listed (query head,
+  // mask row) pairs, pair i_e / c_e; dense (more pairs than the list holds):
+  // pair e is query head e, all its steps
+  constexpr bool CMP = MASK && DQ != 2;
+  constexpr int RPB = kMaskBlock / BM;          // query blocks per mask row
+  static_assert(kMaskBlock % BM == 0 && (RPB & (RPB - 1)) == 0 && (!MASK || kMaskBlock % KPW == 0),
+                "mask rows hold whole steps");
+  int i_e = 0, c_e = 0, n_ent = 0, m_row0 = 0;  // m_row0: first query block of the first row
+  bool m_dense = true;
+  // advance a cursor (pair e, query block m, query head h) by one step
+  auto walk = [&](int& e, int& m, int& h) {
+    ++m;
+    if (m == nm || (!m_dense && (m & (RPB - 1)) == 0)) {
+      if (++e < n_ent) {
+        if (m_dense) {
+          h = e;
+          m = m_first;
+        } else {
+          const int v = __builtin_amdgcn_readfirstlane(mrows[e]);
+          h = v >> 16;
+          m = imax(m_row0 + (v & 0xffff) * RPB, m_first);
+        }
+      }
+    }
+  };
   // Stored dS (DS): sub-tiles of 32 queries x 32 keys per (sequence, query
   // head), 2 KiB each, key-block major (DsGeom: this tile's keys lie in one
   // 256-key block, whose column holds 16 KiB per 32-query sub-row from its
@@ -239,7 +300,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
       const int r = imin(i_m * BM + (l_idx & (BM - 1)), lq - 1);
       dma4(l_src + (i_h * l_step + r), lds_l + (st * 2 * BM + 64 * w) * 4);
     }
-    if (++i_m == nm) { i_m = m_first; ++i_h; }
+    if constexpr (CMP) {
+      walk(i_e, i_m, i_h);
+    } else if (++i_m == nm) {
+      i_m = m_first;
+      ++i_h;
+    }
   };
   // DQ: the dQ adds of a step go out at its end, after the loads of step + 2,
   // and stay in flight through the next step: vector memory operations
@@ -592,6 +658,44 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     sem_seen = __hip_atomic_load(sem_cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
+  // Block mask without the deterministic chain (whose turns count every key
+  // block at every step): the walk visits only the (query head, mask row)
+  // pairs where one of the workgroup's mask bytes is set; in a listed row a
+  // wave whose own byte is clear still computes, with P = 0 (hid). Pairs in
+  // list order; the steps of pair (h, row) are the query blocks of the row
+  // from m_first on. More pairs than the list holds: every pair, in order.
+  if constexpr (CMP) {
+    if (n_steps > 0) {
+      const int r0 = m_first / RPB, nmr = cdiv(nm, RPB), nrows = nmr - r0;
+      const bool dense = (int64_t)gs * nrows > kMaxMaskRows;
+      if (!dense && w == 0) {
+        int nf, nl;
+        // wave 0's column is the workgroup's first
+        const int n = mask_list_rows(mrs, m_base, m_sh, m_nkb,
+                                     gs, r0, nrows, (BN > kMaskBlock && n0 + kMaskBlock < lk) ? 2 : 1,
+                                     nmr - 1, mrows, &nf, &nl);
+        if (lane == 0) {
+          mstat[0] = n;
+          mstat[1] = RPB * n - nf * (m_first - r0 * RPB) - nl * (nmr * RPB - nm);
+        }
+      }
+      __syncthreads();
+      m_dense = dense;
+      if (!dense) {
+        m_row0 = r0 * RPB;
+        n_ent = __builtin_amdgcn_readfirstlane(mstat[0]);
+        n_steps = __builtin_amdgcn_readfirstlane(mstat[1]);
+        if (n_steps > 0) {
+          const int v = __builtin_amdgcn_readfirstlane(mrows[0]);
+          i_h = c_h = v >> 16;
+          i_m = c_m = imax(m_row0 + (v & 0xffff) * RPB, m_first);
+        }
+      } else {
+        n_ent = gs;   // cursors start at (head 0, m_first) as set above
+      }
+    }
+  }
+
   // ---- prologue: fill NS - 1 ring slots. The full wait also retires the K / V
   // fragment loads: the compiler then knows them complete and places no wait
   // of its own inside the loop (where the outstanding ring loads, which it
@@ -606,18 +710,22 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   __builtin_amdgcn_s_barrier();
 
   int st = 0;   // ring slot of the step being computed (step % NS)
-  int c_h = 0;  // query head of the compute cursor, from kvh0
   bf16x8 f0 = fetch_first(0, 0), f1 = fetch_first(1, 0);
   f32x16 dqa;   // DQ: this wave's dQ unit of the step (formed from zero each step)
   for (int step = 0; step < n_steps; ++step) {
     const int mq0 = c_m * BM;
     const int h_step = c_h;
-    const bool wrap = ++c_m == nm;
-    if (wrap) c_m = m_first;
+    bool wrap = false;
+    if constexpr (CMP) {
+      walk(c_e, c_m, c_h);
+    } else {
+      wrap = ++c_m == nm;
+      if (wrap) c_m = m_first;
+    }
     // a cleared mask block hides every pair of this wave's step (P = 0)
     bool hid = false;
     if constexpr (MASK)
-      hid = !mask_set(mrs, m_base + c_h * m_sh + static_cast<uint32_t>(mq0 / kMaskBlock) * m_nkb);
+      hid = !mask_set(mrs, m_base + h_step * m_sh + static_cast<uint32_t>(mq0 / kMaskBlock) * m_nkb);
     if (wrap) ++c_h;
     const bool has_next = step + 1 < n_steps;
     const int iss = step + NS - 1 < n_steps ? (st == 0 ? NS - 1 : st - 1) : -1;  // (step + 2) % NS
@@ -715,6 +823,8 @@ template <int D, int KB, int BM, bool DS, bool MASK, int DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
   __shared__ __attribute__((aligned(1024))) char smem[dkdv_smem_bytes<D, BM, DQ>()];
   __shared__ int ticket;
+  __shared__ int mrows[MASK && DQ != 2 ? kMaxMaskRows : 1];   // listed mask pairs
+  __shared__ int mstat[2];                                     // their count, their steps
   for (int r = 0;; ++r) {
     const BwdParams& p = kernel_args<BwdParams>();
     const int i = next_tile(r, p.ntiles, p.nxcd, p.queue, &ticket);
@@ -756,7 +866,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams) {
         t.head = kv;
       }
     }
-    dkdv_tile<D, KB, BM, DS, MASK, DQ>(p, t, part, smem);
+    dkdv_tile<D, KB, BM, DS, MASK, DQ>(p, t, part, smem, mrows, mstat);
     __syncthreads();   // the next tile's loads reuse the ring slots
   }
 }

@@ -25,6 +25,9 @@ constexpr int kMaskBlock = 128;
 // key tiles a masked forward or dQ workgroup lists (its visible ones): the
 // host refuses masks over more than kMaxMaskTiles 64-key tiles
 constexpr int kMaxMaskTiles = 4096;
+// (query head, 128-row mask row) pairs a masked dK/dV workgroup lists (its
+// visible ones); a workgroup with more pairs walks every step instead
+constexpr int kMaxMaskRows = 2048;
 struct MaskView {
   const uint8_t* mask;
   int64_t sb, sh;       // bytes between batches / query heads (0: shared)

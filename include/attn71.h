@@ -194,8 +194,10 @@ typedef struct attn_params {
    * stored-dS design (ATTN_BWD_AUTO then recomputes dQ), exp_emulation and
    * seqlen_k above 4096 * 64 keys (the length of the visible-tile lists the
    * forward and dQ kernels keep) are refused with a mask
-   * (ATTN_ERR_UNSUPPORTED). The forward and dQ kernels skip hidden key tiles
-   * entirely; the dK/dV kernel steps through them (masked to zero). */
+   * (ATTN_ERR_UNSUPPORTED). The forward and dQ kernels skip hidden key tiles;
+   * the dK/dV kernel skips the (query head, 128-row block) pairs hidden for
+   * all of its keys, except in the deterministic fused design, whose ordered
+   * dQ chain steps through them (masked to zero). */
   const uint8_t* block_mask;
   int64_t block_mask_stride_b, block_mask_stride_h;
 } attn_params;

@@ -93,6 +93,52 @@ def test_block_mask_over_many_key_tiles(sq, sk, hkv, d, causal, window, design):
     check_grads((dq, dk, dv), ref, what)
 
 
+def _masked_case(b, sq, sk, hq, hkv, d, causal, m, what, deterministic=False, options=None):
+    inp = make_inputs(b, sq, sk, hq, hkv, d, seed=800 + sq + sk + d)
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    md = m.to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[block mask] {what}", flush=True)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], causal=causal, softmax_scale=scale, block_mask=md)
+    grads = ea.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=causal, softmax_scale=scale,
+                   deterministic=deterministic, options=options, block_mask=md)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal,
+                                              block_mask=m)
+    check_o(o, o_ref, what)
+    check_lse(lse, lse_ref, what)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal,
+                                    block_mask=m)
+    check_grads(grads, ref, what)
+
+
+@pytest.mark.parametrize("design", ["recompute", "fused", "deterministic"])
+@pytest.mark.parametrize("sq,sk,hq,hkv,d", [
+    (650, 700, 4, 2, 128), (550, 700, 2, 1, 64), (450, 520, 2, 2, 256)])
+def test_block_mask_rows_cut_by_the_causal_diagonal(sq, sk, hq, hkv, d, design):
+    """Causal, with lengths whose diagonal makes a key block's first visible
+    query block fall inside a 128-row mask row, and whose last mask row is
+    partial: the dK/dV walk over the listed mask rows starts and ends inside
+    a row. The deterministic design walks every step (its semaphore chain
+    counts each key block at each query block)."""
+    m = _mask(1, hq, sq, sk, seed=sq + sk + d, density=0.4)
+    det = design == "deterministic"
+    opts = DESIGNS["fused" if det else design]
+    _masked_case(1, sq, sk, hq, hkv, d, True, m,
+                 f"mask cut s{sq}/{sk} hq{hq} hkv{hkv} d{d} {design}", det, opts)
+
+
+@pytest.mark.parametrize("design", ["recompute", "fused"])
+def test_block_mask_with_more_mask_rows_than_a_workgroup_lists(design):
+    """16 query heads per KV head (no head split) over 131 mask rows: 2096
+    (head, row) pairs per key block, more than the dK/dV kernel lists, so it
+    walks every step and skips none; the result is still the oracle's."""
+    b, sq, sk, hq, hkv, d = 1, 16700, 300, 16, 1, 64
+    m = _mask(b, hq, sq, sk, seed=31, density=0.3)
+    _masked_case(b, sq, sk, hq, hkv, d, False, m, f"mask dense walk {design}",
+                 options=dict(DESIGNS[design], head_split=1))
+
+
 def test_shared_mask_broadcasts_over_batches_and_heads():
     """A [1, 1, nqb, nkb] mask applies to every (batch, head) (strides 0)."""
     b, s, hq, d = 2, 640, 4, 128
