@@ -51,6 +51,10 @@ namespace attn71 {
 
 namespace {
 
+// A ring slot as a compile-time constant (the step loop runs one copy of the
+// step per slot, so slot offsets are immediates of the LDS reads)
+template <int N> struct Slot { static constexpr int value = N; };
+
 // LDS of one workgroup: [NS] Q tiles | [NS] dO tiles | [NS][LSE BM | D BM] fp32,
 // and with DQ (from a 1 KiB boundary) the K tile | [2] dS images
 template <int D, int BM>
@@ -371,10 +375,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   // Row rq + 8 has dma_swz(rq) ^ 2 (rq < 8), so the k slots 4..7 read at
   // (a_t ^ 32) + 8 RB.
   const int a_t = rq * RB + 16 * (cl ^ dma_swz<D>(rq)) + 8 * (s16 & 1);
-  // Absolute LDS addresses of the Q tile of the current ring slot (dO at
-  // + NS * TILE): ar[kk] for the S / dP operands, at[db][h] for the two
-  // transposing reads. They move by one slot per step; slot offsets are
-  // multiples of TILE, above every bit the XORs touch.
+  // Absolute LDS addresses in the Q tile of a ring slot (dO at + NS * TILE):
+  // ar[kk] for the S / dP operands, at[db][h] for the two transposing reads.
+  // UNR: the step loop holds one copy of the step per ring slot, whose reads
+  // add the slot's offset (from slot 0) as an immediate, with no per-step
+  // address updates (17 VALU adds fewer per step: dK/dV 2-3 % faster at
+  // head_dim 128); otherwise the addresses move by one slot per step (the
+  // copies would spill registers of the mask, fused-dQ and head_dim-256
+  // variants). Slot offsets are multiples of TILE, above every bit the XORs
+  // touch.
+  constexpr bool UNR = D <= 128 && !MASK && !DQ;
   uint32_t ar[KS], at[NDB][2];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_q + (a_rm ^ (32 * kk));
@@ -436,10 +446,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     k1 = lds_k + (lt ^ (64 * db_w + 32)) + 8 * RB;
   };
   // Fragment j (0 or 1) of a step, the Q operands of its first S MFMAs, from
-  // the slot at byte offset nxt from the current one.
-  auto fetch_first = [&](int j, int nxt) -> bf16x8 {
+  // the slot at byte offset so from the addresses' slot.
+  auto fetch_first = [&](int j, int so) -> bf16x8 {
     const int kk = j / NQB, qb = j % NQB;
-    return lds_ld16(ar[kk] + nxt + qb * 32 * RB);
+    return lds_ld16(ar[kk] + so + qb * 32 * RB);
   };
 
   // One step for query block mq0. Masking (causal diagonal, key tail) sets
@@ -449,13 +459,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   // (rel = INT_MAX for keys past the sequence, -1 where nothing is hidden).
   // Only S crosses that branch; a second copy of the whole body would split
   // the AGPR accumulators over two paths (the allocator answers with spills).
-  // f0, f1: the first two operand fragments of this step on entry (read by
-  // the previous step), of the next step (slot offset nxt) on return.
-  // has_next: a later step exists (mid-step sync); iss >= 0: the ring slot the
-  // loads of step + 2 go to.
-  // par: byte offset of this step's dS image (DQ); dqa: its dQ unit.
-  auto step_body = [&](int mq0, bool need_mask, bool hid, bf16x8& f0, bf16x8& f1, bool has_next,
-                       int iss, int nxt, uint32_t par, f32x16& dqa) {
+  // slot: Slot<s>, the step's offset from the addresses' ring slot in slots
+  // (UNR: its ring slot; else 0). f0, f1: the first two operand fragments of
+  // this step on entry (read by the previous step), of the next step (byte
+  // offset nxt from the addresses' slot) on return. has_next: a later step
+  // exists (mid-step sync); iss >= 0: the ring slot the loads of step + 2
+  // go to. par: byte offset of this step's dS image (DQ); dqa: its dQ unit.
+  auto step_body = [&](auto slot, int mq0, bool need_mask, bool hid, bf16x8& f0, bf16x8& f1,
+                       bool has_next, int iss, int nxt, uint32_t par, f32x16& dqa) {
+    constexpr int SO = decltype(slot)::value * TILE;           // Q tile offset
+    constexpr int SL = decltype(slot)::value * 2 * BM * 4;     // LSE / D offset
     constexpr int OT = NS * TILE;   // dO tile offset from the Q tile
     uint32_t dsw = 0, dsr = 0, dk0 = 0, dk1 = 0;   // DQ: dS image and K tile addresses
     int rel[KB];
@@ -478,11 +491,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     auto fetch = [&](int f) -> bf16x8 {
       if (f < 2 * NG1) {   // Q (then dO): fragment (kk, qb)
         const int x = f % NG1, kk = x / NQB, qb = x % NQB;
-        return lds_ld16(ar[kk] + (f < NG1 ? 0 : OT) + qb * 32 * RB);
+        return lds_ld16(ar[kk] + SO + (f < NG1 ? 0 : OT) + qb * 32 * RB);
       }
       const int x = (f - 2 * NG1) % NG2;           // dO^T (then Q^T): (qb, tt, db)
       const int qb = x / (2 * NDB), tt = (x / NDB) % 2, db = x % NDB;
-      const int off = (f < 2 * NG1 + NG2 ? OT : 0) + (qb * 32 + 16 * tt) * RB;
+      const int off = SO + (f < 2 * NG1 + NG2 ? OT : 0) + (qb * 32 + 16 * tt) * RB;
       return cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
     };
     f32x16 s[NQB][KB], dp[NQB][KB];
@@ -495,7 +508,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 v = lds_ldf4(al + 4 * (BM + qb * 32 + 8 * j));
+        const f32x4 v = lds_ldf4(al + SL + 4 * (BM + qb * 32 + 8 * j));
 #pragma unroll
         for (int r = 0; r < 4; ++r) nd[qb][4 * j + r] = v[r];
       }
@@ -509,7 +522,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
     // wait drain the operand fragments prefetched after it.
     constexpr int NJ = 4 * NQB;
     auto row_read = [&](int b) {   // LSE block b
-      return lds_ldf4(al + 4 * ((b / 4) * 32 + 8 * (b % 4)));
+      return lds_ldf4(al + SL + 4 * ((b / 4) * 32 + 8 * (b % 4)));
     };
     f32x4 rv_cur = {}, rv_next = row_read(0);
     auto row_block = [&](int b) {  // entering block b: rotate and prefetch b + 1
@@ -641,7 +654,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
           }
         }
         if (x == 1 && iss >= 0) {
-          issue(__builtin_amdgcn_readfirstlane(iss));
+          issue(UNR ? iss : __builtin_amdgcn_readfirstlane(iss));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -709,10 +722,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
 
-  int st = 0;   // ring slot of the step being computed (step % NS)
   bf16x8 f0 = fetch_first(0, 0), f1 = fetch_first(1, 0);
   f32x16 dqa;   // DQ: this wave's dQ unit of the step (formed from zero each step)
-  for (int step = 0; step < n_steps; ++step) {
+  int st = 0;   // !UNR: ring slot of the step being computed (step % NS)
+  // step `step`; UNR: in ring slot `slot` (= step % NS)
+  auto one_step = [&](auto slot, int step) {
     const int mq0 = c_m * BM;
     const int h_step = c_h;
     bool wrap = false;
@@ -728,15 +742,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
       hid = !mask_set(mrs, m_base + h_step * m_sh + static_cast<uint32_t>(mq0 / kMaskBlock) * m_nkb);
     if (wrap) ++c_h;
     const bool has_next = step + 1 < n_steps;
-    const int iss = step + NS - 1 < n_steps ? (st == 0 ? NS - 1 : st - 1) : -1;  // (step + 2) % NS
-    const int nxt = st == NS - 1 ? -(NS - 1) * TILE : TILE;                      // next slot
+    constexpr int ST = decltype(slot)::value;
+    const int is_slot = UNR ? (ST + NS - 1) % NS : (st == 0 ? NS - 1 : st - 1);  // (step + 2) % NS
+    const int iss = step + NS - 1 < n_steps ? is_slot : -1;
+    // the next step's slot, from the addresses' slot
+    const int nxt = UNR ? (ST + 1) % NS * TILE : (st == NS - 1 ? -(NS - 1) * TILE : TILE);
     // A wave whose keys all lie above this block's rows computes the step
     // anyway (masked to zero): skipping it would need a second path around
     // the mid-step barrier, and the register allocator answers such a split
     // of the AGPR accumulators with spills.
     const bool need_mask = hid || (wk0 + KPW > lk) || (causal && wk0 + KPW - 1 > mq0 + shift);
     const uint32_t par = (step & 1) * DSB;   // DQ: dS image of this step
-    step_body(mq0, need_mask, hid, f0, f1, has_next, iss, nxt, par, dqa);
+    step_body(slot, mq0, need_mask, hid, f0, f1, has_next, iss, nxt, par, dqa);
     if constexpr (DQ) {
       // rows mq0 + 32 qb_w + 8 (r / 4) + 4 g + r % 4 (register r), dims
       // 32 db_w + c; rows past the sequence fall outside the buffer range
@@ -764,8 +781,19 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
         ds_soff += NQB * 16384;
       }
     }
-    advance_slot(st);
-    st = st == NS - 1 ? 0 : st + 1;
+  };
+  if constexpr (UNR) {
+    for (int step = 0; step < n_steps; step += NS) {
+      one_step(Slot<0>{}, step);
+      if (step + 1 < n_steps) one_step(Slot<1>{}, step + 1);
+      if (step + 2 < n_steps) one_step(Slot<2>{}, step + 2);
+    }
+  } else {
+    for (int step = 0; step < n_steps; ++step) {
+      one_step(Slot<0>{}, step);
+      advance_slot(st);
+      st = st == NS - 1 ? 0 : st + 1;
+    }
   }
 
   if constexpr (DQ == 2) {   // count the last two steps' adds once they have completed
