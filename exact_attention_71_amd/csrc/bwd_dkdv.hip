@@ -51,10 +51,6 @@ namespace attn71 {
 
 namespace {
 
-// A ring slot as a compile-time constant (the step loop runs one copy of the
-// step per slot, so slot offsets are immediates of the LDS reads)
-template <int N> struct Slot { static constexpr int value = N; };
-
 // LDS of one workgroup: [NS] Q tiles | [NS] dO tiles | [NS][LSE BM | D BM] fp32,
 // and with DQ (from a 1 KiB boundary) the K tile | [2] dS images
 template <int D, int BM>

@@ -423,6 +423,10 @@ __device__ __forceinline__ bf16x4 ds_read_tr(uint32_t lds_byte) {
 }
 
 // Reads at a 32-bit LDS byte address (no generic-pointer conversion).
+// A ring slot as a compile-time constant: loops that run one copy of their
+// body per slot of an LDS ring read each slot at immediate offsets.
+template <int N> struct Slot { static constexpr int value = N; };
+
 __device__ __forceinline__ bf16x8 lds_ld16(uint32_t lds_byte) {
   return *(const lds_bf16x8*)(lds_byte);
 }
