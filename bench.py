@@ -52,14 +52,22 @@ METRIC = "attention fwd/bwd TFLOPs/s at hdim128 bf16; % of MI355X BF16 MFMA peak
 
 
 def sources_sha() -> str:
-    """Hash of the kernel sources and build flags (identifies the measured build)."""
+    """Hash of the kernel sources' code (comments and blank space removed, so an
+    edit of a comment keeps it) and of the build script with its flags:
+    identifies the measured build."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "exact_attention_71_amd")
-    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))):
+        with open(f, encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(os.path.basename(f).encode())
+        h.update(" ".join(code.split()).encode())
+    with open(os.path.join(pkg, "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -62,8 +62,6 @@ constexpr int dkdv_smem_bytes() {
             : dkdv_ring_bytes<D, BM>();
 }
 
-// One tile: the keys of key block t.block of (sequence t.seq, KV head t.head),
-// query heads of part `part` of the group (p.hsplit parts).
 // Block mask: the (query head h < gs, mask row r0 + rr < r0 + nrows) pairs
 // whose byte is set in one of the workgroup's ncols key columns (first byte
 // at mb0 + h sh + row nkb), head-major, as h << 16 | rr, written to rows[];
@@ -98,6 +96,9 @@ __device__ __forceinline__ int mask_list_rows(rsrc_t r, uint32_t mb0, uint32_t s
   return base;
 }
 
+// One tile: the keys of key block t.block of (sequence t.seq, KV head t.head),
+// query heads of part `part` of the group (p.hsplit parts). mrows, mstat: LDS
+// for the listed mask pairs (kMaxMaskRows) and their count and steps.
 template <int D, int KB, int BM, bool DS, bool MASK, int DQ>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int part, char* smem,
                                           int* mrows, int* mstat) {
