@@ -237,6 +237,20 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
     at[db][0] = lds_s0 + VT + (a_t ^ (64 * db));
     at[db][1] = lds_s0 + VT + (a_t ^ (64 * db + 32)) + 8 * RB;
   }
+  // UNR (no ring continued across tiles: s0 = 0): the key-tile loop holds one
+  // copy of the tile per ring slot, whose LDS reads add the slot's offset as
+  // an immediate instead of moving the addresses (2 KS VALU adds per tile at
+  // head_dim 256, where one wave per SIMD issues every instruction itself).
+  // The addresses go through an empty asm so that the compiler keeps them
+  // whole: split into a base and a constant, the V tile's offsets of the
+  // second slot exceed the 16-bit immediate and cost an add per read.
+  constexpr bool UNR = !XT;
+  if constexpr (UNR) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(ar[kk]));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(at[db][0]), "+v"(at[db][1]));
+  }
   auto advance_slot = [&](int st) {
     const int dq = st == NS - 1 ? -(NS - 1) * TILE : TILE;
 #pragma unroll
@@ -277,7 +291,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
   // key tile n; the last one is a separate copy (LAST) that also loads the
   // next tile's first key tile and Q fragments, so that those loads sit
   // outside the loop and the compiler tracks no loop-carried load
-  auto k_tile = [&](int j, auto last_c) {
+  // so: byte offset of the tile's ring slot from the addresses' slot (UNR;
+  // else 0, the addresses move instead)
+  auto k_tile = [&](int j, auto last_c, int so) {
     constexpr bool LAST = decltype(last_c)::value;
     const int st = (s0 + j) % NS;
     if constexpr (LAST) {
@@ -329,7 +345,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       constexpr int NSF = NKB * KS;                 // S^T MFMA fragments
       auto fetch_s = [&](int y) -> bf16x8 {
         const int kb = y / KS, kk = y % KS;
-        return lds_ld16(ar[kk] + kb * 32 * RB);
+        return lds_ld16(ar[kk] + so + kb * 32 * RB);
       };
       bf16x8 k0f = fetch_s(0), k1f = fetch_s(1);
 #pragma unroll
@@ -413,7 +429,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
       static_assert(PE * NDB == 8, "even P slices");
       auto fetch_pv = [&](int x) -> bf16x8 {
         const int h = x / NDB, db = x % NDB;
-        const int off = (h / 2 * 32 + 16 * (h % 2)) * RB;
+        const int off = so + (h / 2 * 32 + 16 * (h % 2)) * RB;
         return cat8(ds_read_tr(at[db][0] + off), ds_read_tr(at[db][1] + off));
       };
       bf16x8 v0 = fetch_pv(0), v1 = fetch_pv(1);
@@ -443,11 +459,23 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb][0] + acc[qb][1];
     }
-    advance_slot(st);
+    if constexpr (!UNR) advance_slot(st);
     if constexpr (!LAST) wait_next(j + NS - 1 < nv);
   };
-  for (int j = 0; j + 1 < nv; ++j) k_tile(j, std::false_type{});
-  if (nv > 0) k_tile(nv - 1, std::true_type{});
+  if constexpr (UNR) {
+    static_assert(NS == 2 || NS == 3, "one copy per ring slot");
+    for (int j = 0; j + 1 < nv; j += NS) {   // tiles j .. j + NS - 1 in slots 0 .. NS - 1
+      k_tile(j, std::false_type{}, 0);
+      if (j + 2 < nv) k_tile(j + 1, std::false_type{}, TILE);
+      if constexpr (NS == 3) {
+        if (j + 3 < nv) k_tile(j + 2, std::false_type{}, 2 * TILE);
+      }
+    }
+    if (nv > 0) k_tile(nv - 1, std::true_type{}, (nv - 1) % NS * TILE);
+  } else {
+    for (int j = 0; j + 1 < nv; ++j) k_tile(j, std::false_type{}, 0);
+    if (nv > 0) k_tile(nv - 1, std::true_type{}, 0);
+  }
   if (nv == 0) {
     prefetch_kv();
     if (nxt_ok) load_q(nqs, nlq, nh, nm0);
