@@ -217,7 +217,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
     __builtin_amdgcn_s_barrier();
   };
 
-  // per-lane LDS addresses of the current slot (see dma_swz): ar[kk] for the A
+  // per-lane LDS addresses in ring slot 0 (see dma_swz): ar[kk] for the A
   // operand of S^T (key row c of each 32-key block, logical chunk 2kk + g),
   // at[db][h] for the transposing reads of V^T (16-lane group (g, dh), lane
   // s16 reads key row 4g + s16/4 (+8 for k slots 4..7), dims
@@ -228,36 +228,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
   const int rq = 4 * g + (s16 >> 2);
   const int cl = 2 * dh + ((s16 & 3) >> 1);
   const int a_t = rq * RB + 16 * (cl ^ dma_swz<D>(rq)) + 8 * (s16 & 1);
+  // The addresses are those of ring slot 0: the key-tile loop holds one copy
+  // of the tile per ring slot, whose LDS reads add the slot's offset as an
+  // immediate instead of moving the addresses (2 KS VALU adds per tile: the
+  // d = 256 forward, one wave per SIMD, 3 % faster, the others 1 %); tiles
+  // before the continued ring wraps to slot 0, and the last tile, take their
+  // offset at run time. The addresses go through an empty asm so that the
+  // compiler keeps them whole: split into a base and a constant, the V tile's
+  // offsets of the second slot exceed the 16-bit immediate and cost an add
+  // per read.
   uint32_t ar[KS], at[NDB][2];
-  const uint32_t lds_s0 = lds_k + s0 * TILE;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_s0 + (a_rm ^ (32 * kk));
+  for (int kk = 0; kk < KS; ++kk) {
+    ar[kk] = lds_k + (a_rm ^ (32 * kk));
+    asm volatile("" : "+v"(ar[kk]));
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    at[db][0] = lds_s0 + VT + (a_t ^ (64 * db));
-    at[db][1] = lds_s0 + VT + (a_t ^ (64 * db + 32)) + 8 * RB;
+    at[db][0] = lds_k + VT + (a_t ^ (64 * db));
+    at[db][1] = lds_k + VT + (a_t ^ (64 * db + 32)) + 8 * RB;
+    asm volatile("" : "+v"(at[db][0]), "+v"(at[db][1]));
   }
-  // UNR (no ring continued across tiles: s0 = 0): the key-tile loop holds one
-  // copy of the tile per ring slot, whose LDS reads add the slot's offset as
-  // an immediate instead of moving the addresses (2 KS VALU adds per tile at
-  // head_dim 256, where one wave per SIMD issues every instruction itself).
-  // The addresses go through an empty asm so that the compiler keeps them
-  // whole: split into a base and a constant, the V tile's offsets of the
-  // second slot exceed the 16-bit immediate and cost an add per read.
-  constexpr bool UNR = !XT;
-  if constexpr (UNR) {
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(ar[kk]));
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(at[db][0]), "+v"(at[db][1]));
-  }
-  auto advance_slot = [&](int st) {
-    const int dq = st == NS - 1 ? -(NS - 1) * TILE : TILE;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) ar[kk] += dq;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) { at[db][0] += dq; at[db][1] += dq; }
-  };
 
   f32x16 oacc[QB][NDB];
   float mref[QB], lsum[QB];
@@ -291,11 +282,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
   // key tile n; the last one is a separate copy (LAST) that also loads the
   // next tile's first key tile and Q fragments, so that those loads sit
   // outside the loop and the compiler tracks no loop-carried load
-  // so: byte offset of the tile's ring slot from the addresses' slot (UNR;
-  // else 0, the addresses move instead)
+  // so: byte offset of the tile's ring slot from slot 0
   auto k_tile = [&](int j, auto last_c, int so) {
     constexpr bool LAST = decltype(last_c)::value;
-    const int st = (s0 + j) % NS;
     if constexpr (LAST) {
       prefetch_kv();
     } else {
@@ -459,23 +448,20 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams& p, const Tile& t, char
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) lsum[qb] += acc[qb][0] + acc[qb][1];
     }
-    if constexpr (!UNR) advance_slot(st);
     if constexpr (!LAST) wait_next(j + NS - 1 < nv);
   };
-  if constexpr (UNR) {
-    static_assert(NS == 2 || NS == 3, "one copy per ring slot");
-    for (int j = 0; j + 1 < nv; j += NS) {   // tiles j .. j + NS - 1 in slots 0 .. NS - 1
-      k_tile(j, std::false_type{}, 0);
-      if (j + 2 < nv) k_tile(j + 1, std::false_type{}, TILE);
-      if constexpr (NS == 3) {
-        if (j + 3 < nv) k_tile(j + 2, std::false_type{}, 2 * TILE);
-      }
+  static_assert(NS == 2 || NS == 3, "one copy per ring slot");
+  int j0 = 0;
+  // tiles before the ring wraps to slot 0 (the ring continues from the last tile)
+  for (; j0 + 1 < nv && (s0 + j0) % NS != 0; ++j0) k_tile(j0, std::false_type{}, (s0 + j0) % NS * TILE);
+  for (int j = j0; j + 1 < nv; j += NS) {   // tiles j .. j + NS - 1 in slots 0 .. NS - 1
+    k_tile(j, std::false_type{}, 0);
+    if (j + 2 < nv) k_tile(j + 1, std::false_type{}, TILE);
+    if constexpr (NS == 3) {
+      if (j + 3 < nv) k_tile(j + 2, std::false_type{}, 2 * TILE);
     }
-    if (nv > 0) k_tile(nv - 1, std::true_type{}, (nv - 1) % NS * TILE);
-  } else {
-    for (int j = 0; j + 1 < nv; ++j) k_tile(j, std::false_type{}, 0);
-    if (nv > 0) k_tile(nv - 1, std::true_type{}, 0);
   }
+  if (nv > 0) k_tile(nv - 1, std::true_type{}, (s0 + nv - 1) % NS * TILE);
   if (nv == 0) {
     prefetch_kv();
     if (nxt_ok) load_q(nqs, nlq, nh, nm0);
