@@ -377,12 +377,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, const Tile& t, int
   // UNR: the step loop holds one copy of the step per ring slot, whose reads
   // add the slot's offset (from slot 0) as an immediate, with no per-step
   // address updates (17 VALU adds fewer per step: dK/dV 2-3 % faster at
-  // head_dim 128); otherwise the addresses move by one slot per step (the
-  // copies would spill registers of the mask and fused-dQ variants inside
-  // the step loop; at head_dim 256 the dO tile's offsets in the third slot
-  // exceed the 16-bit immediate, and the copies measured 0.5-1 % slower).
-  // Slot offsets are multiples of TILE, above every bit the XORs touch.
-  constexpr bool UNR = D <= 128 && !MASK && !DQ;
+  // head_dim 128, with or without a block mask); otherwise the addresses
+  // move by one slot per step (the copies would spill registers of the
+  // fused-dQ variants inside the step loop; at head_dim 256 the dO tile's
+  // offsets in the third slot exceed the 16-bit immediate, and the copies
+  // measured 0.5-1 % slower). Slot offsets are multiples of TILE, above
+  // every bit the XORs touch.
+  constexpr bool UNR = D <= 128 && !DQ;
   uint32_t ar[KS], at[NDB][2];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) ar[kk] = lds_q + (a_rm ^ (32 * kk));
